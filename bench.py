@@ -1,0 +1,211 @@
+"""Benchmark of one GPU's share of the MoE layer, forward + backward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C1]
+
+A step is one forward + backward of the whole layer (router, permute,
+grouped FFN, combine and their backward) over one batch of seeded synthetic
+input already resident in HBM.  Prints ONE JSON line with tokens/s, the
+roofline position of the dominant kernel (timed with HIP events on its own
+stream inside the timed region) and the CPU oracle timed on a bounded
+sample of the same workload.
+
+This build runs on one GPU: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd tokens/sec on 1 MI355X; % bf16 MFMA peak, % HBM BW"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+# CPU-oracle sample sizes (tokens) that take roughly 10-30 s on ~8-16 cores
+CPU_SAMPLE_T = {"tiny_f32": 64, "c1_bf16": 4096, "c2_zipf": 2048, "c3_epshare": 1024,
+                "c4_large": 256}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description="MoE layer fwd+bwd benchmark (1 GPU)")
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C1",
+                    help="workload: C0..C4 or its name (default C1)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--kernel", default=None,
+                    help="kernel timed for the roofline (default: the up-projection GEMM)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def dev(a):
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(
+            torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def cpu_baseline(w, seed):
+    """The oracle, as it stands, on the first T' tokens of the workload."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    Ts = min(w.T, CPU_SAMPLE_T.get(w.name, 1024))
+    ws = w.replace(T=Ts)
+    inp = W.make_inputs(ws, seed=seed)
+    if w.kind == "ep_share":
+        # the generator draws the ragged batch for T' rows
+        pass
+    threads = None
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads") or 0) for i in info) if info else None
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    fw = O.layer_fwd(inp, ws)
+    O.layer_bwd(inp, ws, fw)
+    dt = time.perf_counter() - t0
+    unit = "rows/s" if w.kind == "ep_share" else "tokens/s"
+    return {"value": Ts / dt, "unit": unit, "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"oracle fwd+bwd of the same layer shape on the first {Ts} of "
+                      f"{w.T} tokens (seed {seed}), one run, {dt:.1f} s; host has "
+                      f"{os.cpu_count()} logical CPUs"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build is one GPU's share of the MoE layer; --gpus {a.gpus} "
+              "is not supported (multi-GPU sharding is a design note only).",
+              file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import expert_router_gemm_softmax_amd as M
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    w = W.get(a.config)
+    log(f"[bench] workload {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} {w.dtype} "
+        f"cf={w.cf}")
+    inp = W.make_inputs(w, seed=a.seed)
+    d = {k: dev(v) for k, v in inp.items()}
+    if w.cf is None:
+        cap = None
+    else:
+        cap = M.moe_capacity(w.T, w.k, w.E, w.cf)
+    cfg = M.make_cfg(w.T, w.d, w.E, w.k, w.f, w.dtype, capacity=cap)
+    sdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    if w.kind == "layer":
+        layer = M.MoeLayer(cfg, d["Wr"], d["b"], d["W1"], d["W2"])
+        out = torch.empty(w.T, w.d, dtype=sdt, device="cuda")
+        dX = torch.empty_like(out)
+        grads = layer.alloc_grads()
+
+        def step():
+            layer.forward(d["x"], out)
+            layer.backward(d["x"], d["dOut"], dX, grads)
+
+        offsets = layer.saved["offsets"]
+    else:
+        # one EP rank's share: the batch arrives already permuted
+        Rmax = M.moe_rows_max(cfg)
+        ws = torch.empty(M.moe_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+        e = lambda *s, dt=sdt: torch.empty(*s, dtype=dt, device="cuda")
+        A, H, Y = e(Rmax, w.f), e(Rmax, w.f), e(Rmax, w.d)
+        out, dYp, dXp = e(w.T, w.d), e(Rmax, w.d), e(Rmax, w.d)
+        dg = e(w.T, 1, dt=torch.float32)
+        dW1, dW2 = torch.empty_like(d["W1"]), torch.empty_like(d["W2"])
+        offsets = d["offsets"]
+
+        def step():
+            M.moe_grouped_ffn(cfg, d["x_perm"], offsets, d["W1"], d["W2"], A, H, Y, ws)
+            M.moe_combine(cfg, Y, d["row_of"], d["gate"], out)
+            M.moe_combine_bwd(cfg, d["dOut"], Y, d["row_of"], d["gate"], dYp, dg)
+            M.moe_grouped_ffn_bwd(cfg, d["x_perm"], offsets, d["W1"], d["W2"], A, H, dYp,
+                                  dXp, dW1, dW2, ws)
+
+    for i in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    R = int(offsets[-1].item())
+    log(f"[bench] warmup done, R={R} kept rows of {w.T * w.k}")
+
+    kernel = a.kernel or "GEMM_UP"
+    M.moe_prof_arm(kernel, a.steps)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(a.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    k_ms, k_n = M.moe_prof_read()
+    ms_per_step = wall * 1e3 / a.steps
+    log(f"[bench] {a.steps} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms; "
+        f"{kernel}: {k_n} launches, {k_ms / max(k_n, 1):.4f} ms avg")
+
+    # algorithmic work of the timed kernel per launch
+    flops = {"GEMM_UP": 2.0 * R * w.d * w.f, "GEMM_DOWN": 2.0 * R * w.d * w.f,
+             "GEMM_DH": 2.0 * R * w.d * w.f, "GEMM_DX": 2.0 * R * w.d * w.f,
+             "GEMM_DW1": 2.0 * R * w.d * w.f, "GEMM_DW2": 2.0 * R * w.d * w.f}
+    avg_s = (k_ms / 1e3) / max(k_n, 1)
+    if kernel in flops:
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        achieved = flops[kernel] / avg_s / 1e12 if avg_s > 0 else 0.0
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": kernel, "avg_ms": round(avg_s * 1e3, 5)}
+    else:
+        roof = {"bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": None, "traffic": None, "kernel": kernel,
+                "avg_ms": round(avg_s * 1e3, 5)}
+
+    unit = "rows/s" if w.kind == "ep_share" else "tokens/s"
+    value = w.T * a.steps / wall
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded; random-init weights)",
+        "config": {"workload": f"{w.name}: T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} "
+                               f"cf={w.cf} bias={w.bias}",
+                   "tokens": w.T, "d": w.d, "experts": w.E, "top_k": w.k, "ffn": w.f,
+                   "capacity": cap, "kept_rows": R, "parallelism": "single GPU"},
+        "roofline": roof,
+        "gpu_event_ms_per_step": round(gpu_ms / a.steps, 4),
+    }
+    if not a.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(w, a.seed)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

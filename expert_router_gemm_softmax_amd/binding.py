@@ -1,0 +1,242 @@
+"""ctypes binding of libmoe.so (include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+of libmoe.so.  Tensors are passed as device pointers (``data_ptr()``) and
+the stream is torch's current HIP stream unless one is given.  There is no
+fallback: if libmoe.so is missing or fails to load, importing this module
+raises ``MoeLibraryError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_char_p, c_double, c_float, c_int, c_int32, \
+    c_int64, c_size_t, c_uint32, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_ARG = -1
+MOE_ERR_DTYPE = -2
+MOE_ERR_SHAPE = -3
+MOE_ERR_ALIGN = -4
+MOE_ERR_WORKSPACE = -5
+MOE_ERR_LAUNCH = -6
+MOE_ERR_UNIMPLEMENTED = -7
+
+MOE_FP32 = 0
+MOE_BF16 = 1
+MOE_NO_CAPACITY = -1
+
+KERNELS = dict(ROUTE=0, PERMUTE_COUNT=1, PERMUTE_SCAN=2, PERMUTE_SCATTER=3,
+               GEMM_UP=4, GEMM_DOWN=5, COMBINE=6, COMBINE_BWD=7, GEMM_DH=8,
+               GEMM_DX=9, GEMM_DW2=10, GEMM_DW1=11, UNPERMUTE_BWD=12,
+               ROUTE_BWD_DZ=13, ROUTE_BWD_DX=14, ROUTE_BWD_DW=15, SCHEDULE=16,
+               ROUTE_PREP=17)
+
+
+class MoeLibraryError(ImportError):
+    pass
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({status_str(status)})")
+        self.status = status
+
+
+class MoeCfg(ctypes.Structure):
+    _fields_ = [("T", c_int64), ("d", c_int32), ("E", c_int32), ("k", c_int32),
+                ("f", c_int32), ("dtype", c_int32), ("capacity", c_int64),
+                ("route_margin", c_float), ("flags", c_uint32)]
+
+    def __repr__(self):
+        return (f"MoeCfg(T={self.T}, d={self.d}, E={self.E}, k={self.k}, f={self.f}, "
+                f"dtype={self.dtype}, capacity={self.capacity})")
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [("Wr", c_void_p), ("b", c_void_p), ("W1", c_void_p), ("W2", c_void_p)]
+
+
+class MoeCtx(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("probs", "idx", "gate", "counts", "offsets",
+                                         "row_of", "src_of", "x_perm", "A", "H", "Y")]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [("dWr", c_void_p), ("db", c_void_p), ("dW1", c_void_p), ("dW2", c_void_p)]
+
+
+_P = c_void_p
+_CFG = POINTER(MoeCfg)
+_SIGS = {
+    "moe_capacity": (c_int64, [c_int64, c_int32, c_int32, c_double]),
+    "moe_rows_max": (c_int64, [_CFG]),
+    "moe_workspace_bytes": (c_size_t, [_CFG]),
+    "moe_status_str": (c_char_p, [c_int]),
+    "moe_check_cfg": (c_int, [_CFG]),
+    "moe_route": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_permute": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_grouped_ffn": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_combine": (c_int, [_CFG, _P, _P, _P, _P, _P]),
+    "moe_combine_bwd": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_grouped_ffn_bwd": (c_int, [_CFG] + [_P] * 11 + [c_size_t, _P]),
+    "moe_unpermute_bwd": (c_int, [_CFG, _P, _P, _P, _P]),
+    "moe_route_bwd": (c_int, [_CFG] + [_P] * 11 + [c_size_t, _P]),
+    "moe_layer_fwd": (c_int, [_CFG, POINTER(MoeWeights), _P, _P, POINTER(MoeCtx), _P,
+                              c_size_t, _P]),
+    "moe_layer_bwd": (c_int, [_CFG, POINTER(MoeWeights), _P, _P, POINTER(MoeCtx), _P,
+                              POINTER(MoeGrads), _P, c_size_t, _P]),
+    "moe_prof_arm": (c_int, [c_int, c_int]),
+    "moe_prof_read": (c_int, [POINTER(c_float), POINTER(c_int)]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise MoeLibraryError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m expert_router_gemm_softmax_amd.build`")
+    try:
+        lib = ctypes.CDLL(LIB_PATH)
+    except OSError as e:
+        raise MoeLibraryError(f"cannot load {LIB_PATH}: {e}") from e
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+# ------------------------------------------------------------------ helpers
+def status_str(status: int) -> str:
+    return lib.moe_status_str(int(status)).decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != MOE_OK:
+        raise MoeError(fn, rc)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr() or None
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_cfg(T, d, E, k, f, dtype="bf16", capacity=None, route_margin=0.0) -> MoeCfg:
+    """capacity: None = no limit, else an int >= 0."""
+    dt = {"bf16": MOE_BF16, "f32": MOE_FP32, MOE_BF16: MOE_BF16, MOE_FP32: MOE_FP32}[dtype]
+    return MoeCfg(T=int(T), d=int(d), E=int(E), k=int(k), f=int(f), dtype=dt,
+                  capacity=MOE_NO_CAPACITY if capacity is None else int(capacity),
+                  route_margin=float(route_margin), flags=0)
+
+
+def moe_capacity(T, k, E, cf) -> int:
+    return int(lib.moe_capacity(int(T), int(k), int(E), float(cf)))
+
+
+def moe_rows_max(cfg: MoeCfg) -> int:
+    return int(lib.moe_rows_max(byref(cfg)))
+
+
+def moe_workspace_bytes(cfg: MoeCfg) -> int:
+    return int(lib.moe_workspace_bytes(byref(cfg)))
+
+
+def moe_check_cfg(cfg: MoeCfg) -> int:
+    return int(lib.moe_check_cfg(byref(cfg)))
+
+
+# ------------------------------------------------------------------ entry points
+def moe_route(cfg, x, Wr, b, probs, idx, gate, ws, stream=None):
+    _check("moe_route", lib.moe_route(
+        byref(cfg), _ptr(x), _ptr(Wr), _ptr(b), _ptr(probs), _ptr(idx), _ptr(gate),
+        _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_permute(cfg, x, idx, counts, offsets, row_of, src_of, x_perm, ws, stream=None):
+    _check("moe_permute", lib.moe_permute(
+        byref(cfg), _ptr(x), _ptr(idx), _ptr(counts), _ptr(offsets), _ptr(row_of),
+        _ptr(src_of), _ptr(x_perm), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_grouped_ffn(cfg, x_perm, offsets, W1, W2, A, H, Y, ws, stream=None):
+    _check("moe_grouped_ffn", lib.moe_grouped_ffn(
+        byref(cfg), _ptr(x_perm), _ptr(offsets), _ptr(W1), _ptr(W2), _ptr(A), _ptr(H),
+        _ptr(Y), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_combine(cfg, Y, row_of, gate, out, stream=None):
+    _check("moe_combine", lib.moe_combine(
+        byref(cfg), _ptr(Y), _ptr(row_of), _ptr(gate), _ptr(out), _stream(stream)))
+
+
+def moe_combine_bwd(cfg, dOut, Y, row_of, gate, dYp, dgate, stream=None):
+    _check("moe_combine_bwd", lib.moe_combine_bwd(
+        byref(cfg), _ptr(dOut), _ptr(Y), _ptr(row_of), _ptr(gate), _ptr(dYp),
+        _ptr(dgate), _stream(stream)))
+
+
+def moe_grouped_ffn_bwd(cfg, x_perm, offsets, W1, W2, A, H, dYp, dXp, dW1, dW2, ws,
+                        stream=None):
+    _check("moe_grouped_ffn_bwd", lib.moe_grouped_ffn_bwd(
+        byref(cfg), _ptr(x_perm), _ptr(offsets), _ptr(W1), _ptr(W2), _ptr(A), _ptr(H),
+        _ptr(dYp), _ptr(dXp), _ptr(dW1), _ptr(dW2), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def moe_unpermute_bwd(cfg, dXp, row_of, dXe, stream=None):
+    _check("moe_unpermute_bwd", lib.moe_unpermute_bwd(
+        byref(cfg), _ptr(dXp), _ptr(row_of), _ptr(dXe), _stream(stream)))
+
+
+def moe_route_bwd(cfg, x, Wr, probs, idx, row_of, dgate, dXp, dX, dWr, db, ws,
+                  stream=None):
+    _check("moe_route_bwd", lib.moe_route_bwd(
+        byref(cfg), _ptr(x), _ptr(Wr), _ptr(probs), _ptr(idx), _ptr(row_of), _ptr(dgate),
+        _ptr(dXp), _ptr(dX), _ptr(dWr), _ptr(db), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def moe_layer_fwd(cfg, weights: MoeWeights, x, out, ctx: MoeCtx, ws, stream=None):
+    _check("moe_layer_fwd", lib.moe_layer_fwd(
+        byref(cfg), byref(weights), _ptr(x), _ptr(out), byref(ctx), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def moe_layer_bwd(cfg, weights: MoeWeights, x, dOut, ctx: MoeCtx, dX, grads: MoeGrads, ws,
+                  stream=None):
+    _check("moe_layer_bwd", lib.moe_layer_bwd(
+        byref(cfg), byref(weights), _ptr(x), _ptr(dOut), byref(ctx), _ptr(dX),
+        byref(grads), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_prof_arm(kernel, max_launches):
+    kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    _check("moe_prof_arm", lib.moe_prof_arm(kid, int(max_launches)))
+
+
+def moe_prof_read():
+    ms, n = c_float(0.0), c_int(0)
+    _check("moe_prof_read", lib.moe_prof_read(byref(ms), byref(n)))
+    return float(ms.value), int(n.value)

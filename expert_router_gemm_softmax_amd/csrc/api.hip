@@ -1,0 +1,379 @@
+// C-ABI of the MoE layer library: argument validation, workspace layout,
+// the step sequence of the layer forward and backward, and opt-in kernel
+// timing.  Every entry point validates everything before it enqueues
+// anything; on an error nothing is enqueued and nothing is written.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "common.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ timing hook
+namespace {
+struct Prof {
+  int kid = -1;
+  int cap = 0;
+  int n = 0;
+  bool open = false;
+  std::vector<hipEvent_t> ev0, ev1;
+};
+Prof g_prof;
+}  // namespace
+
+void prof_begin(int kid, hipStream_t s) {
+  if (kid != g_prof.kid || g_prof.n >= g_prof.cap) return;
+  if (hipEventRecord(g_prof.ev0[g_prof.n], s) == hipSuccess) g_prof.open = true;
+}
+void prof_end(int kid, hipStream_t s) {
+  if (!g_prof.open || kid != g_prof.kid) return;
+  if (hipEventRecord(g_prof.ev1[g_prof.n], s) == hipSuccess) g_prof.n++;
+  g_prof.open = false;
+}
+
+// ------------------------------------------------------------------ validation
+namespace {
+
+int check_cfg(const moe_cfg* c) {
+  if (!c) return MOE_ERR_ARG;
+  if (c->dtype != MOE_FP32 && c->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (c->T < 0 || c->T > 0x7fffffffLL) return MOE_ERR_ARG;
+  if (c->k < 1 || c->k > 32 || c->E < c->k || c->E > 256) return MOE_ERR_ARG;
+  if (c->d < 1 || c->f < 1) return MOE_ERR_ARG;
+  if (c->capacity < MOE_NO_CAPACITY) return MOE_ERR_ARG;
+  if (c->flags != 0) return MOE_ERR_ARG;
+  if (c->T * c->k > 0x7fffffffLL) return MOE_ERR_SHAPE;
+  if (!(c->route_margin == c->route_margin)) return MOE_ERR_ARG;  // NaN
+  const size_t s = elem_bytes(*c);
+  if ((c->d * s) % 16 != 0 || (c->f * s) % 16 != 0) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+// a tensor of `bytes` bytes: NULL only if empty; `align`-byte aligned
+int need(const void* p, size_t bytes, size_t align) {
+  if (bytes == 0) return MOE_OK;
+  if (!p) return MOE_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(p) % align != 0) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+int need_ws(const moe_cfg& c, const void* ws, size_t ws_bytes) {
+  const size_t want = ws_layout(c).total;
+  if (ws_bytes < want) return MOE_ERR_WORKSPACE;
+  return need(ws, want, 256);
+}
+
+#define MOE_TRY(expr)            \
+  do {                           \
+    const int rc_ = (expr);      \
+    if (rc_ != MOE_OK) return rc_; \
+  } while (0)
+
+struct Sizes {
+  size_t s, Td, TE, Tk, E1, Rd, Rf, Edf, dE, Rmax;
+};
+Sizes sizes(const moe_cfg& c) {
+  Sizes z;
+  z.s = elem_bytes(c);
+  z.Rmax = (size_t)rows_max(c);
+  z.Td = (size_t)c.T * c.d * z.s;
+  z.TE = (size_t)c.T * c.E * 4;
+  z.Tk = (size_t)c.T * c.k * 4;
+  z.E1 = (size_t)(c.E + 1) * 4;
+  z.Rd = z.Rmax * c.d * z.s;
+  z.Rf = z.Rmax * c.f * z.s;
+  z.Edf = (size_t)c.E * c.d * c.f * z.s;
+  z.dE = (size_t)c.d * c.E * z.s;
+  return z;
+}
+
+inline hipStream_t S(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double cf) {
+  if (cf < 0.0 || E <= 0 || T < 0 || k < 0) return MOE_NO_CAPACITY;
+  const double v = cf * (double)T * (double)k / (double)E;
+  double fl = floor(v);
+  if (v - fl <= 1e-9 * (v > 1.0 ? v : 1.0)) return (int64_t)fl;  // integer up to rounding
+  return (int64_t)ceil(v);
+}
+
+int64_t moe_rows_max(const moe_cfg* cfg) {
+  if (check_cfg(cfg) != MOE_OK) return -1;
+  return rows_max(*cfg);
+}
+
+size_t moe_workspace_bytes(const moe_cfg* cfg) {
+  if (check_cfg(cfg) != MOE_OK) return 0;
+  return ws_layout(*cfg).total;
+}
+
+int moe_check_cfg(const moe_cfg* cfg) { return check_cfg(cfg); }
+
+const char* moe_status_str(int st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument (null pointer or out-of-range value)";
+    case MOE_ERR_DTYPE: return "unknown dtype";
+    case MOE_ERR_SHAPE: return "inconsistent or too large shape";
+    case MOE_ERR_ALIGN: return "row or pointer not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes(cfg)";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_UNIMPLEMENTED: return "not implemented";
+    default: return "unknown status";
+  }
+}
+
+int moe_route(const moe_cfg* cfg, const void* x, const void* Wr, const float* b,
+              float* probs, int32_t* idx, float* gate, void* ws, size_t ws_bytes,
+              moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_cfg& c = *cfg;
+  const Sizes z = sizes(c);
+  MOE_TRY(need(x, z.Td, 16));
+  MOE_TRY(need(Wr, z.dE, 4));
+  if (b) MOE_TRY(need(b, (size_t)c.E * 4, 4));
+  MOE_TRY(need(probs, z.TE, 4));
+  MOE_TRY(need(idx, z.Tk, 4));
+  MOE_TRY(need(gate, z.Tk, 4));
+  MOE_TRY(need_ws(c, ws, ws_bytes));
+  void* wrT = ws_ptr<void>(ws, ws_layout(c).wrT);
+  return launch_route(c, x, Wr, b, probs, idx, gate, wrT, S(stream));
+}
+
+int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx, int32_t* counts,
+                int32_t* offsets, int32_t* row_of, int32_t* src_of, void* x_perm, void* ws,
+                size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_cfg& c = *cfg;
+  const Sizes z = sizes(c);
+  MOE_TRY(need(x, z.Td, 16));
+  MOE_TRY(need(idx, z.Tk, 4));
+  MOE_TRY(need(counts, (size_t)c.E * 4, 4));
+  MOE_TRY(need(offsets, z.E1, 4));
+  MOE_TRY(need(row_of, z.Tk, 4));
+  MOE_TRY(need(src_of, z.Rmax * 4, 4));
+  MOE_TRY(need(x_perm, z.Rd, 16));
+  MOE_TRY(need_ws(c, ws, ws_bytes));
+  return launch_permute(c, x, idx, counts, offsets, row_of, src_of, x_perm, ws, S(stream));
+}
+
+int moe_grouped_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
+                    const void* W1, const void* W2, void* A, void* H, void* Y, void* ws,
+                    size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_cfg& c = *cfg;
+  const Sizes z = sizes(c);
+  MOE_TRY(need(x_perm, z.Rd, 16));
+  MOE_TRY(need(offsets, z.E1, 4));
+  MOE_TRY(need(W1, z.Edf, 16));
+  MOE_TRY(need(W2, z.Edf, 16));
+  MOE_TRY(need(A, z.Rf, 16));
+  MOE_TRY(need(H, z.Rf, 16));
+  MOE_TRY(need(Y, z.Rd, 16));
+  MOE_TRY(need_ws(c, ws, ws_bytes));
+  return launch_ffn_fwd(c, x_perm, offsets, W1, W2, A, H, Y, ws, S(stream));
+}
+
+int moe_combine(const moe_cfg* cfg, const void* Y, const int32_t* row_of, const float* gate,
+                void* out, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_cfg& c = *cfg;
+  const Sizes z = sizes(c);
+  MOE_TRY(need(Y, z.Rd, 16));
+  MOE_TRY(need(row_of, z.Tk, 4));
+  MOE_TRY(need(gate, z.Tk, 4));
+  MOE_TRY(need(out, z.Td, 16));
+  return launch_combine(c, Y, row_of, gate, out, S(stream));
+}
+
+int moe_combine_bwd(const moe_cfg* cfg, const void* dOut, const void* Y,
+                    const int32_t* row_of, const float* gate, void* dYp, float* dgate,
+                    moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_cfg& c = *cfg;
+  const Sizes z = sizes(c);
+  MOE_TRY(need(dOut, z.Td, 16));
+  MOE_TRY(need(Y, z.Rd, 16));
+  MOE_TRY(need(row_of, z.Tk, 4));
+  MOE_TRY(need(gate, z.Tk, 4));
+  MOE_TRY(need(dYp, z.Rd, 16));
+  MOE_TRY(need(dgate, z.Tk, 4));
+  return launch_combine_bwd(c, dOut, Y, row_of, gate, dYp, dgate, S(stream));
+}
+
+int moe_grouped_ffn_bwd(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
+                        const void* W1, const void* W2, const void* A, const void* H,
+                        const void* dYp, void* dXp, void* dW1, void* dW2, void* ws,
+                        size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_cfg& c = *cfg;
+  const Sizes z = sizes(c);
+  MOE_TRY(need(x_perm, z.Rd, 16));
+  MOE_TRY(need(offsets, z.E1, 4));
+  MOE_TRY(need(W1, z.Edf, 16));
+  MOE_TRY(need(W2, z.Edf, 16));
+  MOE_TRY(need(A, z.Rf, 16));
+  MOE_TRY(need(H, z.Rf, 16));
+  MOE_TRY(need(dYp, z.Rd, 16));
+  MOE_TRY(need(dXp, z.Rd, 16));
+  MOE_TRY(need(dW1, z.Edf, 16));
+  MOE_TRY(need(dW2, z.Edf, 16));
+  MOE_TRY(need_ws(c, ws, ws_bytes));
+  return launch_ffn_bwd(c, x_perm, offsets, W1, W2, A, H, dYp, dXp, dW1, dW2, ws,
+                        S(stream));
+}
+
+int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp, const int32_t* row_of,
+                      float* dXe, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_cfg& c = *cfg;
+  const Sizes z = sizes(c);
+  MOE_TRY(need(dXp, z.Rd, 16));
+  MOE_TRY(need(row_of, z.Tk, 4));
+  MOE_TRY(need(dXe, (size_t)c.T * c.d * 4, 16));
+  return launch_unpermute_bwd(c, dXp, row_of, dXe, S(stream));
+}
+
+int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr, const float* probs,
+                  const int32_t* idx, const int32_t* row_of, const float* dgate,
+                  const void* dXp, void* dX, void* dWr, float* db, void* ws, size_t ws_bytes,
+                  moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_cfg& c = *cfg;
+  const Sizes z = sizes(c);
+  MOE_TRY(need(x, z.Td, 16));
+  MOE_TRY(need(Wr, z.dE, 4));
+  MOE_TRY(need(probs, z.TE, 4));
+  MOE_TRY(need(idx, z.Tk, 4));
+  MOE_TRY(need(row_of, z.Tk, 4));
+  MOE_TRY(need(dgate, z.Tk, 4));
+  MOE_TRY(need(dXp, z.Rd, 16));
+  MOE_TRY(need(dX, z.Td, 16));
+  MOE_TRY(need(dWr, z.dE, 4));
+  if (db) MOE_TRY(need(db, (size_t)c.E * 4, 4));
+  MOE_TRY(need_ws(c, ws, ws_bytes));
+  return launch_route_bwd(c, x, Wr, probs, idx, row_of, dgate, dXp, dX, dWr, db, ws,
+                          S(stream));
+}
+
+static int check_ctx(const moe_cfg& c, const moe_ctx* x) {
+  if (!x) return MOE_ERR_ARG;
+  const Sizes z = sizes(c);
+  MOE_TRY(need(x->probs, z.TE, 4));
+  MOE_TRY(need(x->idx, z.Tk, 4));
+  MOE_TRY(need(x->gate, z.Tk, 4));
+  MOE_TRY(need(x->counts, (size_t)c.E * 4, 4));
+  MOE_TRY(need(x->offsets, z.E1, 4));
+  MOE_TRY(need(x->row_of, z.Tk, 4));
+  MOE_TRY(need(x->src_of, z.Rmax * 4, 4));
+  MOE_TRY(need(x->x_perm, z.Rd, 16));
+  MOE_TRY(need(x->A, z.Rf, 16));
+  MOE_TRY(need(x->H, z.Rf, 16));
+  MOE_TRY(need(x->Y, z.Rd, 16));
+  return MOE_OK;
+}
+
+static int check_weights(const moe_cfg& c, const moe_weights* w) {
+  if (!w) return MOE_ERR_ARG;
+  const Sizes z = sizes(c);
+  MOE_TRY(need(w->Wr, z.dE, 4));
+  if (w->b) MOE_TRY(need(w->b, (size_t)c.E * 4, 4));
+  MOE_TRY(need(w->W1, z.Edf, 16));
+  MOE_TRY(need(w->W2, z.Edf, 16));
+  return MOE_OK;
+}
+
+int moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const void* x, void* out,
+                  const moe_ctx* ctx, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_cfg& c = *cfg;
+  const Sizes z = sizes(c);
+  MOE_TRY(check_weights(c, w));
+  MOE_TRY(check_ctx(c, ctx));
+  MOE_TRY(need(x, z.Td, 16));
+  MOE_TRY(need(out, z.Td, 16));
+  MOE_TRY(need_ws(c, ws, ws_bytes));
+  const hipStream_t s = S(stream);
+  const WsLayout L = ws_layout(c);
+  MOE_TRY(launch_route(c, x, w->Wr, w->b, ctx->probs, ctx->idx, ctx->gate,
+                       ws_ptr<void>(ws, L.wrT), s));
+  MOE_TRY(launch_permute(c, x, ctx->idx, ctx->counts, ctx->offsets, ctx->row_of,
+                         ctx->src_of, ctx->x_perm, ws, s));
+  MOE_TRY(launch_ffn_fwd(c, ctx->x_perm, ctx->offsets, w->W1, w->W2, ctx->A, ctx->H, ctx->Y,
+                         ws, s));
+  return launch_combine(c, ctx->Y, ctx->row_of, ctx->gate, out, s);
+}
+
+int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* x, const void* dOut,
+                  const moe_ctx* ctx, void* dX, const moe_grads* g, void* ws,
+                  size_t ws_bytes, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_cfg& c = *cfg;
+  const Sizes z = sizes(c);
+  MOE_TRY(check_weights(c, w));
+  MOE_TRY(check_ctx(c, ctx));
+  if (!g) return MOE_ERR_ARG;
+  MOE_TRY(need(g->dWr, z.dE, 4));
+  if (g->db) MOE_TRY(need(g->db, (size_t)c.E * 4, 4));
+  MOE_TRY(need(g->dW1, z.Edf, 16));
+  MOE_TRY(need(g->dW2, z.Edf, 16));
+  MOE_TRY(need(x, z.Td, 16));
+  MOE_TRY(need(dOut, z.Td, 16));
+  MOE_TRY(need(dX, z.Td, 16));
+  MOE_TRY(need_ws(c, ws, ws_bytes));
+  const hipStream_t s = S(stream);
+  const WsLayout L = ws_layout(c);
+  float* dgate = ws_ptr<float>(ws, L.dgate);
+  void* dYp = ws_ptr<void>(ws, L.dYp);
+  void* dXp = ws_ptr<void>(ws, L.dXp);
+  MOE_TRY(launch_combine_bwd(c, dOut, ctx->Y, ctx->row_of, ctx->gate, dYp, dgate, s));
+  MOE_TRY(launch_ffn_bwd(c, ctx->x_perm, ctx->offsets, w->W1, w->W2, ctx->A, ctx->H, dYp,
+                         dXp, g->dW1, g->dW2, ws, s));
+  return launch_route_bwd(c, x, w->Wr, ctx->probs, ctx->idx, ctx->row_of, dgate, dXp, dX,
+                          g->dWr, g->db, ws, s);
+}
+
+int moe_prof_arm(int kernel_id, int max_launches) {
+  if (kernel_id < 0 || kernel_id >= MOE_KERNEL_COUNT_ || max_launches < 0)
+    return MOE_ERR_ARG;
+  while ((int)g_prof.ev0.size() < max_launches) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return MOE_ERR_LAUNCH;
+    if (hipEventCreate(&b) != hipSuccess) return MOE_ERR_LAUNCH;
+    g_prof.ev0.push_back(a);
+    g_prof.ev1.push_back(b);
+  }
+  g_prof.kid = kernel_id;
+  g_prof.cap = max_launches;
+  g_prof.n = 0;
+  g_prof.open = false;
+  return MOE_OK;
+}
+
+int moe_prof_read(float* total_ms, int* launches) {
+  if (!total_ms || !launches) return MOE_ERR_ARG;
+  float sum = 0.0f;
+  for (int i = 0; i < g_prof.n; ++i) {
+    if (hipEventSynchronize(g_prof.ev1[i]) != hipSuccess) return MOE_ERR_LAUNCH;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, g_prof.ev0[i], g_prof.ev1[i]) != hipSuccess)
+      return MOE_ERR_LAUNCH;
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = g_prof.n;
+  g_prof.kid = -1;
+  g_prof.n = 0;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,215 @@
+// Internal definitions shared by the MoE HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ------------------------------------------------------------------ bf16
+// bfloat16 is carried as its 16 bit pattern (uint16_t).
+__device__ __forceinline__ float bf2f(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// float -> bf16, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+// two floats -> packed bf16x2 (lo in bits 0..15)
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+}
+
+// ------------------------------------------------------------------ storage traits
+// St<float> / St<uint16_t>: element type of the activation/weight storage.
+template <typename T> struct St;
+template <> struct St<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  __device__ static __forceinline__ float to_f(float v) { return v; }
+  __device__ static __forceinline__ float from_f(float v) { return v; }
+  // unpack one 16-byte vector into kVec floats
+  __device__ static __forceinline__ void unpack(const u32x4& u, float* o) {
+    o[0] = __uint_as_float(u.x); o[1] = __uint_as_float(u.y);
+    o[2] = __uint_as_float(u.z); o[3] = __uint_as_float(u.w);
+  }
+  __device__ static __forceinline__ u32x4 pack(const float* o) {
+    return u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]),
+                 __float_as_uint(o[2]), __float_as_uint(o[3])};
+  }
+};
+template <> struct St<uint16_t> {
+  static constexpr int kVec = 8;
+  __device__ static __forceinline__ float to_f(uint16_t v) { return bf2f(v); }
+  __device__ static __forceinline__ uint16_t from_f(float v) { return f2bf(v); }
+  __device__ static __forceinline__ void unpack(const u32x4& u, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(u[i] << 16);
+      o[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static __forceinline__ u32x4 pack(const float* o) {
+    return u32x4{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]),
+                 pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7])};
+  }
+};
+
+// ------------------------------------------------------------------ GELU (tanh form)
+// gelu(a) = 0.5 a (1 + tanh(u)),  u = sqrt(2/pi) (a + 0.044715 a^3)
+__device__ __forceinline__ float gelu_tanh(float a) {
+  const float u = 0.7978845608028654f * (a + 0.044715f * a * a * a);
+  return 0.5f * a * (1.0f + tanhf(u));
+}
+// d gelu / da = 0.5 (1 + tanh u) + 0.5 a (1 - tanh^2 u) sqrt(2/pi) (1 + 3*0.044715 a^2)
+__device__ __forceinline__ float gelu_tanh_grad(float a) {
+  const float u = 0.7978845608028654f * (a + 0.044715f * a * a * a);
+  const float th = tanhf(u);
+  return 0.5f * (1.0f + th) +
+         0.5f * a * (1.0f - th * th) * 0.7978845608028654f *
+             (1.0f + 0.134145f * a * a);
+}
+
+// ------------------------------------------------------------------ wave helpers
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ------------------------------------------------------------------ workspace
+// One workspace buffer serves every entry point; each region is 256-byte
+// aligned.  Regions:
+//   wrT        [Epad, d] s           router weights transposed, zero rows >= E
+//   perm_blk   [nblk_perm, E] int32  per-block expert histograms / bases
+//   tiles      [E+1] int32           grouped-GEMM M-tile prefix per expert
+//   dz         [T, E] float          router logit gradient
+//   dwr_part   [nsplit, d, E] float  split-T partial sums of x^T dz
+//   db_part    [nsplit, E] float     split-T partial sums of dz
+//   dgate      [T, k] float          combine-backward gate gradient
+//   dYp        [Rmax, d] s           combine-backward row gradient
+//   dA         [Rmax, f] s           GELU-backward hidden gradient
+//   dXp        [Rmax, d] s           expert input gradient
+//   dw_part    [nsplitk, tile] float split-K partials of weight gradients
+struct WsLayout {
+  size_t wrT, perm_blk, tiles, dz, dwr_part, db_part, dgate, dYp, dA, dXp, total;
+  int nblk_perm;
+  int dwr_split;
+};
+
+constexpr int kPermTokens = 256;  // tokens per permute block
+constexpr int kDwrRows = 1024;    // tokens per split of the dWr reduction
+
+inline int64_t rows_max(const moe_cfg& c) {
+  const int64_t tk = c.T * c.k;
+  if (c.capacity < 0) return tk;
+  const int64_t ec = c.capacity * (int64_t)c.E;
+  return tk < ec ? tk : ec;
+}
+
+// experts padded to 32, 64, 128 or 256 (whole 32-wide MFMA tiles) in the router
+inline int route_epad(int E) {
+  const int nt = (E + 31) / 32;
+  return 32 * (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8);
+}
+
+inline size_t elem_bytes(const moe_cfg& c) { return c.dtype == MOE_BF16 ? 2 : 4; }
+
+inline WsLayout ws_layout(const moe_cfg& c) {
+  WsLayout L{};
+  const size_t s = elem_bytes(c);
+  const int64_t Rmax = rows_max(c);
+  L.nblk_perm = (int)ceil_div(c.T > 0 ? c.T : 1, kPermTokens);
+  L.dwr_split = (int)ceil_div(c.T > 0 ? c.T : 1, kDwrRows);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  L.wrT = take((size_t)route_epad(c.E) * c.d * s);
+  L.perm_blk = take((size_t)L.nblk_perm * c.E * 4);
+  L.tiles = take((size_t)(c.E + 1) * 4 * 4);
+  L.dz = take((size_t)c.T * c.E * 4);
+  L.dwr_part = take((size_t)L.dwr_split * c.d * c.E * 4);
+  L.db_part = take((size_t)L.dwr_split * c.E * 4);
+  L.dgate = take((size_t)c.T * c.k * 4);
+  L.dYp = take((size_t)Rmax * c.d * s);
+  L.dA = take((size_t)Rmax * c.f * s);
+  L.dXp = take((size_t)Rmax * c.d * s);
+  L.total = off;
+  return L;
+}
+
+template <typename P>
+inline P* ws_ptr(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+// ------------------------------------------------------------------ launch + timing
+void prof_begin(int kernel_id, hipStream_t s);
+void prof_end(int kernel_id, hipStream_t s);
+
+#define MOE_LAUNCH(kid, stream, ...)                                  \
+  do {                                                                \
+    ::moe::prof_begin((kid), (stream));                               \
+    __VA_ARGS__;                                                      \
+    hipError_t e_ = hipGetLastError();                                \
+    ::moe::prof_end((kid), (stream));                                 \
+    if (e_ != hipSuccess) return MOE_ERR_LAUNCH;                      \
+  } while (0)
+
+// ------------------------------------------------------------------ launchers
+// (each validates nothing: the C-ABI layer in api.hip has done that)
+int launch_route(const moe_cfg& c, const void* x, const void* Wr, const float* b,
+                 float* probs, int32_t* idx, float* gate, void* wrT, hipStream_t s);
+int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
+                   int32_t* counts, int32_t* offsets, int32_t* row_of,
+                   int32_t* src_of, void* x_perm, void* ws, hipStream_t s);
+int launch_ffn_fwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
+                   const void* W1, const void* W2, void* A, void* H, void* Y,
+                   void* ws, hipStream_t s);
+int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
+                   const void* W1, const void* W2, const void* A, const void* H,
+                   const void* dYp, void* dXp, void* dW1, void* dW2, void* ws,
+                   hipStream_t s);
+int launch_combine(const moe_cfg& c, const void* Y, const int32_t* row_of,
+                   const float* gate, void* out, hipStream_t s);
+int launch_combine_bwd(const moe_cfg& c, const void* dOut, const void* Y,
+                       const int32_t* row_of, const float* gate, void* dYp,
+                       float* dgate, hipStream_t s);
+int launch_unpermute_bwd(const moe_cfg& c, const void* dXp, const int32_t* row_of,
+                         float* dXe, hipStream_t s);
+int launch_route_bwd(const moe_cfg& c, const void* x, const void* Wr,
+                     const float* probs, const int32_t* idx, const int32_t* row_of,
+                     const float* dgate, const void* dXp, void* dX, void* dWr,
+                     float* db, void* ws, hipStream_t s);
+
+}  // namespace moe

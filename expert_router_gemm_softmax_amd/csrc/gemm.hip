@@ -1,0 +1,498 @@
+// Grouped expert GEMMs over ragged per-expert segments (F3, F4, B4, B3).
+// Every local expert runs on the rows routed to it as one grouped GEMM
+// rather than one small GEMM per expert ("GPU expert parallel", section
+// "The step timeline").  The per-expert segments are [offsets[e],
+// offsets[e+1]) and live on the device only; tile lists are derived on the
+// device.
+//
+// Two problem shapes:
+//   ROW  (forward and input-gradient GEMMs): C_e[m_e, N] = A_e[m_e, K] B_e
+//        with A_e the expert's rows (K contiguous) and B_e the expert's
+//        weight, stored either [K][N] (N contiguous: x W1, H W2) or [N][K]
+//        (K contiguous: dYp W2^T, dA W1^T).
+//   KRAG (weight gradients): C_e[M, N] = A_e^T B_e over the expert's m_e
+//        rows, A_e [m_e][M] and B_e [m_e][N] both row-major, i.e. the
+//        reduction runs over a ragged K = m_e (H^T dYp, x_perm^T dA).
+//        Experts with m_e = 0 get a zero matrix.
+//
+// bf16 kernel (gfx950): v_mfma_f32_32x32x16_bf16, block tile BM x BN x 64,
+// 4 waves in 2 x 2, LDS double buffer of K-contiguous tiles with an XOR
+// swizzle; operands stored MN-contiguous in HBM are transposed in
+// registers on their way into LDS.  Tiles are ordered so that the blocks
+// resident on one XCD (block id mod 8) work on a compact group of output
+// tiles, which keeps their operand panels in that XCD's L2.
+#include "common.h"
+
+namespace moe {
+
+enum { MODE_ROW = 0, MODE_KRAG = 1 };
+enum { EPI_STORE = 0, EPI_GELU = 1, EPI_DGELU = 2 };
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;
+  void* C2;            // EPI_GELU: H = gelu(A_out)
+  const void* Aux;     // EPI_DGELU: forward pre-activation, laid out like C
+  const int32_t* offsets;
+  const int32_t* tiles;  // ROW: prefix of M tiles per expert, [E+1]
+  int E, M, N, K;        // ROW uses N, K; KRAG uses M, N
+  int lda, ldb, ldc;     // leading dims (elements)
+  int64_t b_estride;     // ROW: elements between experts' B
+  int64_t c_estride;     // KRAG: elements between experts' C
+  int ntn, ntm;          // N tiles; KRAG: M tiles per expert
+};
+
+constexpr int kGroupM = 4;  // M tiles per traversal group
+
+namespace {
+
+// Block -> output tile.  Block ids are dealt round-robin to the 8 XCDs;
+// give each XCD a contiguous range of logical tiles, then walk that range
+// in groups of kGroupM M-tiles with M fastest (compact 2-D groups).
+__device__ __forceinline__ bool xcd_logical(int ntotal, int& lid) {
+  const int per = (ntotal + 7) >> 3;
+  const int bid = blockIdx.x;
+  const int local = bid >> 3, xcd = bid & 7;
+  if (local >= per) return false;
+  lid = xcd * per + local;
+  return lid < ntotal;
+}
+__device__ __forceinline__ void group_mn(int lid, int num_m, int ntn, int& mt, int& nt) {
+  const int per_group = kGroupM * ntn;
+  const int g = lid / per_group;
+  const int first = g * kGroupM;
+  const int gsz = min(num_m - first, kGroupM);
+  const int in = lid - g * per_group;
+  mt = first + in % gsz;
+  nt = in / gsz;
+}
+
+struct Tile {
+  int e, m0, n0, M, K;
+  int64_t row0;  // ROW: first row of the expert; KRAG: first K row
+};
+
+template <int MODE, int BM, int BN>
+__device__ __forceinline__ bool decode_tile(const GemmArgs& g, int* s_tiles, Tile& t) {
+  if constexpr (MODE == MODE_ROW) {
+    for (int i = threadIdx.x; i <= g.E; i += blockDim.x) s_tiles[i] = g.tiles[i];
+    __syncthreads();
+    const int num_m = s_tiles[g.E];
+    int lid;
+    if (!xcd_logical(num_m * g.ntn, lid)) return false;
+    int mt, nt;
+    group_mn(lid, num_m, g.ntn, mt, nt);
+    int lo = 0, hi = g.E - 1;  // last e with s_tiles[e] <= mt
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tiles[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    t.e = lo;
+    t.row0 = g.offsets[lo];
+    t.M = g.offsets[lo + 1] - (int)t.row0;
+    t.m0 = (mt - s_tiles[lo]) * BM;
+    t.n0 = nt * BN;
+    t.K = g.K;
+    return true;
+  } else {
+    const int per_e = g.ntm * g.ntn;
+    int lid;
+    if (!xcd_logical(g.E * per_e, lid)) return false;
+    t.e = lid / per_e;
+    int mt, nt;
+    group_mn(lid - t.e * per_e, g.ntm, g.ntn, mt, nt);
+    t.row0 = g.offsets[t.e];
+    t.K = g.offsets[t.e + 1] - (int)t.row0;
+    t.M = g.M;
+    t.m0 = mt * BM;
+    t.n0 = nt * BN;
+    return true;
+  }
+}
+
+// ------------------------------------------------------------------ bf16 MFMA kernel
+constexpr int BK = 64;
+
+// element offset of (row, 8-element chunk) in a K-contiguous [rows][64] tile
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * BK + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
+}
+
+// K-contiguous operand: R tile rows, element (row, k) at base + row*ld + k
+template <int R>
+__device__ __forceinline__ void load_kc(const uint16_t* base, int ld, int row0, int rlim,
+                                        int k0, int klim, u32x4 (&reg)[R / 32]) {
+#pragma unroll
+  for (int i = 0; i < R / 32; ++i) {
+    const int c = threadIdx.x + i * 256;
+    const int row = c >> 3, q = c & 7;
+    const int gr = row0 + row, gk = k0 + q * 8;
+    reg[i] = (gr < rlim && gk < klim) ? ld16(base + (int64_t)gr * ld + gk)
+                                      : u32x4{0, 0, 0, 0};
+  }
+}
+template <int R>
+__device__ __forceinline__ void store_kc(uint16_t* s, const u32x4 (&reg)[R / 32]) {
+#pragma unroll
+  for (int i = 0; i < R / 32; ++i) {
+    const int c = threadIdx.x + i * 256;
+    const int row = c >> 3, q = c & 7;
+    *reinterpret_cast<u32x4*>(s + swz(row, q)) = reg[i];
+  }
+}
+// MN-contiguous operand: element (k, mn) at base + k*ld + mn.  Unit = 4 K
+// rows x 8 MN columns, transposed into 8 LDS rows of 4 K values.
+template <int R>
+__device__ __forceinline__ void load_mnc(const uint16_t* base, int ld, int mn0, int mnlim,
+                                         int k0, int klim, u32x4 (&reg)[R / 128][4]) {
+#pragma unroll
+  for (int i = 0; i < R / 128; ++i) {
+    const int u = threadIdx.x + i * 256;
+    const int mc = u % (R / 8), kq = u / (R / 8);
+    const int gm = mn0 + mc * 8;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int gk = k0 + kq * 4 + r;
+      reg[i][r] = (gm < mnlim && gk < klim) ? ld16(base + (int64_t)gk * ld + gm)
+                                            : u32x4{0, 0, 0, 0};
+    }
+  }
+}
+template <int R>
+__device__ __forceinline__ void store_mnc(uint16_t* s, const u32x4 (&reg)[R / 128][4]) {
+#pragma unroll
+  for (int i = 0; i < R / 128; ++i) {
+    const int u = threadIdx.x + i * 256;
+    const int mc = u % (R / 8), kq = u / (R / 8);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int sh = (c & 1) * 16;
+      const uint32_t e0 = (reg[i][0][c >> 1] >> sh) & 0xFFFFu;
+      const uint32_t e1 = (reg[i][1][c >> 1] >> sh) & 0xFFFFu;
+      const uint32_t e2 = (reg[i][2][c >> 1] >> sh) & 0xFFFFu;
+      const uint32_t e3 = (reg[i][3][c >> 1] >> sh) & 0xFFFFu;
+      const int row = mc * 8 + c;
+      *reinterpret_cast<u32x2*>(s + swz(row, kq >> 1) + (kq & 1) * 4) =
+          u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+    }
+  }
+}
+
+template <int MODE, bool B_KC, int EPI, int BM, int BN>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr bool A_KC = (MODE == MODE_ROW);
+  __shared__ __align__(16) uint16_t sA[2][BM * BK];
+  __shared__ __align__(16) uint16_t sB[2][BN * BK];
+  __shared__ int s_tiles[MODE == MODE_ROW ? 257 : 1];
+
+  Tile t;
+  if (!decode_tile<MODE, BM, BN>(g, s_tiles, t)) return;
+  if constexpr (MODE == MODE_ROW) {
+    if (t.m0 >= t.M) return;
+  }
+
+  const uint16_t* A = static_cast<const uint16_t*>(g.A) + t.row0 * g.lda;
+  const uint16_t* B;
+  if constexpr (MODE == MODE_ROW)
+    B = static_cast<const uint16_t*>(g.B) + (int64_t)t.e * g.b_estride;
+  else
+    B = static_cast<const uint16_t*>(g.B) + t.row0 * g.ldb;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int h = lane >> 5, r = lane & 31;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+  // register staging of the next K tile
+  u32x4 ra_kc[A_KC ? BM / 32 : 1];
+  u32x4 ra_mn[A_KC ? 1 : BM / 128][4];
+  u32x4 rb_kc[B_KC ? BN / 32 : 1];
+  u32x4 rb_mn[B_KC ? 1 : BN / 128][4];
+
+  auto gload = [&](int k0) {
+    if constexpr (A_KC) load_kc<BM>(A, g.lda, t.m0, t.M, k0, t.K, ra_kc);
+    else load_mnc<BM>(A, g.lda, t.m0, t.M, k0, t.K, ra_mn);
+    if constexpr (MODE == MODE_ROW) {
+      if constexpr (B_KC) load_kc<BN>(B, g.ldb, t.n0, g.N, k0, t.K, rb_kc);
+      else load_mnc<BN>(B, g.ldb, t.n0, g.N, k0, t.K, rb_mn);
+    } else {
+      load_mnc<BN>(B, g.ldb, t.n0, g.N, k0, t.K, rb_mn);
+    }
+  };
+  auto lstore = [&](int buf) {
+    if constexpr (A_KC) store_kc<BM>(sA[buf], ra_kc);
+    else store_mnc<BM>(sA[buf], ra_mn);
+    if constexpr (B_KC) store_kc<BN>(sB[buf], rb_kc);
+    else store_mnc<BN>(sB[buf], rb_mn);
+  };
+
+  const int nk = (t.K + BK - 1) / BK;
+  if (nk > 0) {
+    gload(0);
+    lstore(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) gload((kt + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[TM], bfv[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(sA[buf] + swz(wm * WM + i * 32 + r, kk * 2 + h));
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfv[j] = *reinterpret_cast<const bf16x8*>(sB[buf] + swz(wn * WN + j * 32 + r, kk * 2 + h));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: D[i][j] at lane (j + 32*((i/4)%2)), register (i%4) + 4*(i/8)
+  uint16_t* C = static_cast<uint16_t*>(g.C);
+  uint16_t* C2 = static_cast<uint16_t*>(g.C2);
+  const uint16_t* Aux = static_cast<const uint16_t*>(g.Aux);
+  int64_t cbase;
+  if constexpr (MODE == MODE_ROW) cbase = t.row0 * g.ldc;
+  else cbase = (int64_t)t.e * g.c_estride;
+  const int mlim = t.M;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = t.n0 + wn * WN + j * 32 + r;
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = t.m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row >= mlim) continue;
+        const int64_t o = cbase + (int64_t)row * g.ldc + col;
+        const float a = acc[i][j][v];
+        if constexpr (EPI == EPI_STORE) {
+          C[o] = f2bf(a);
+        } else if constexpr (EPI == EPI_GELU) {
+          const uint16_t ab = f2bf(a);
+          C[o] = ab;
+          C2[o] = f2bf(gelu_tanh(bf2f(ab)));
+        } else {
+          C[o] = f2bf(a * gelu_tanh_grad(bf2f(Aux[o])));
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32 VALU kernel
+// Plain LDS-tiled fp32 GEMM with the same problem decode and epilogues,
+// used for float storage (64 x 64 tile, 4 x 4 outputs per thread).
+template <int MODE, bool B_KC, int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
+  constexpr int BM = 64, BN = 64, BKF = 16;
+  __shared__ float sA[BKF][BM + 1];
+  __shared__ float sB[BKF][BN + 1];
+  __shared__ int s_tiles[MODE == MODE_ROW ? 257 : 1];
+  Tile t;
+  if (!decode_tile<MODE, BM, BN>(g, s_tiles, t)) return;
+  if constexpr (MODE == MODE_ROW) {
+    if (t.m0 >= t.M) return;
+  }
+  const float* A = static_cast<const float*>(g.A) + t.row0 * g.lda;
+  const float* B;
+  if constexpr (MODE == MODE_ROW) B = static_cast<const float*>(g.B) + (int64_t)t.e * g.b_estride;
+  else B = static_cast<const float*>(g.B) + t.row0 * g.ldb;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < t.K; k0 += BKF) {
+    for (int i = threadIdx.x; i < BM * BKF; i += 256) {
+      const int kk = i % BKF, m = i / BKF;  // A element (m, k)
+      const int gm = t.m0 + m, gk = k0 + kk;
+      float v = 0.0f;
+      if (gm < t.M && gk < t.K) {
+        if constexpr (MODE == MODE_ROW) v = A[(int64_t)gm * g.lda + gk];
+        else v = A[(int64_t)gk * g.lda + gm];
+      }
+      sA[kk][m] = v;
+    }
+    for (int i = threadIdx.x; i < BN * BKF; i += 256) {
+      const int kk = i % BKF, n = i / BKF;
+      const int gn = t.n0 + n, gk = k0 + kk;
+      float v = 0.0f;
+      if (gn < g.N && gk < t.K) {
+        if constexpr (MODE == MODE_ROW && B_KC) v = B[(int64_t)gn * g.ldb + gk];
+        else v = B[(int64_t)gk * g.ldb + gn];
+      }
+      sB[kk][n] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BKF; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sA[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sB[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+    }
+    __syncthreads();
+  }
+  float* C = static_cast<float*>(g.C);
+  float* C2 = static_cast<float*>(g.C2);
+  const float* Aux = static_cast<const float*>(g.Aux);
+  int64_t cbase;
+  if constexpr (MODE == MODE_ROW) cbase = t.row0 * g.ldc;
+  else cbase = (int64_t)t.e * g.c_estride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = t.m0 + ty * 4 + i;
+    if (row >= t.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = t.n0 + tx * 4 + j;
+      if (col >= g.N) continue;
+      const int64_t o = cbase + (int64_t)row * g.ldc + col;
+      if constexpr (EPI == EPI_STORE) C[o] = acc[i][j];
+      else if constexpr (EPI == EPI_GELU) { C[o] = acc[i][j]; C2[o] = gelu_tanh(acc[i][j]); }
+      else C[o] = acc[i][j] * gelu_tanh_grad(Aux[o]);
+    }
+  }
+}
+
+// tiles[e] = sum_{e' < e} ceil(m_e' / BM); tiles[E] = number of M tiles
+__global__ void gemm_schedule_kernel(const int32_t* __restrict__ offsets,
+                                     int32_t* __restrict__ tiles, int E, int BM) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    int32_t acc = 0;
+    for (int e = 0; e < E; ++e) {
+      tiles[e] = acc;
+      const int m = offsets[e + 1] - offsets[e];
+      acc += (m + BM - 1) / BM;
+    }
+    tiles[E] = acc;
+  }
+}
+
+constexpr int kBM = 128, kBN = 128;  // bf16 block tile
+constexpr int kFM = 64, kFN = 64;    // fp32 block tile
+
+inline int grid8(int64_t n) { return (int)((n + 7) / 8 * 8); }
+
+// Upper bound of M tiles of a ROW problem: sum_e ceil(m_e/BM) <= Rmax/BM + E
+inline int64_t row_mtiles_bound(const moe_cfg& c, int BM) {
+  return ceil_div(rows_max(c), BM) + c.E;
+}
+
+template <int MODE, bool B_KC, int EPI>
+int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
+  const bool bf = c.dtype == MOE_BF16;
+  const int BM = bf ? kBM : kFM, BN = bf ? kBN : kFN;
+  g.ntn = (int)ceil_div(g.N, BN);
+  int64_t nblk;
+  if constexpr (MODE == MODE_ROW) {
+    nblk = row_mtiles_bound(c, BM) * g.ntn;
+  } else {
+    g.ntm = (int)ceil_div(g.M, BM);
+    nblk = (int64_t)c.E * g.ntm * g.ntn;
+  }
+  if (nblk == 0) return MOE_OK;
+  const int grid = grid8(nblk);
+  if (bf)
+    MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, kBM, kBN><<<grid, 256, 0, s>>>(g));
+  else
+    MOE_LAUNCH(kid, s, gemm_f32_kernel<MODE, B_KC, EPI><<<grid, 256, 0, s>>>(g));
+  return MOE_OK;
+}
+
+int schedule(const moe_cfg& c, const int32_t* offsets, int32_t* tiles, hipStream_t s) {
+  const int BM = c.dtype == MOE_BF16 ? kBM : kFM;
+  MOE_LAUNCH(MOE_KERNEL_SCHEDULE, s,
+             gemm_schedule_kernel<<<1, 64, 0, s>>>(offsets, tiles, c.E, BM));
+  return MOE_OK;
+}
+
+}  // namespace
+
+int launch_ffn_fwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
+                   const void* W1, const void* W2, void* A, void* H, void* Y, void* ws,
+                   hipStream_t s) {
+  if (rows_max(c) == 0) return MOE_OK;
+  const WsLayout L = ws_layout(c);
+  int32_t* tiles = ws_ptr<int32_t>(ws, L.tiles);
+  int rc = schedule(c, offsets, tiles, s);
+  if (rc != MOE_OK) return rc;
+  GemmArgs g{};
+  g.offsets = offsets;
+  g.tiles = tiles;
+  g.E = c.E;
+  // A = x_perm W1 ; H = gelu(A)
+  g.A = x_perm; g.B = W1; g.C = A; g.C2 = H;
+  g.N = c.f; g.K = c.d; g.lda = c.d; g.ldb = c.f; g.ldc = c.f;
+  g.b_estride = (int64_t)c.d * c.f;
+  rc = run_gemm<MODE_ROW, false, EPI_GELU>(MOE_KERNEL_GEMM_UP, c, g, s);
+  if (rc != MOE_OK) return rc;
+  // Y = H W2
+  g.A = H; g.B = W2; g.C = Y; g.C2 = nullptr;
+  g.N = c.d; g.K = c.f; g.lda = c.f; g.ldb = c.d; g.ldc = c.d;
+  g.b_estride = (int64_t)c.f * c.d;
+  return run_gemm<MODE_ROW, false, EPI_STORE>(MOE_KERNEL_GEMM_DOWN, c, g, s);
+}
+
+int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
+                   const void* W1, const void* W2, const void* A, const void* H,
+                   const void* dYp, void* dXp, void* dW1, void* dW2, void* ws,
+                   hipStream_t s) {
+  const WsLayout L = ws_layout(c);
+  int32_t* tiles = ws_ptr<int32_t>(ws, L.tiles);
+  void* dA = ws_ptr<void>(ws, L.dA);
+  int rc;
+  GemmArgs g{};
+  g.offsets = offsets;
+  g.tiles = tiles;
+  g.E = c.E;
+  if (rows_max(c) > 0) {
+    rc = schedule(c, offsets, tiles, s);
+    if (rc != MOE_OK) return rc;
+    // dA = (dYp W2^T) * gelu'(A): B = W2[e] as [N=f][K=d]
+    g.A = dYp; g.B = W2; g.C = dA; g.Aux = A;
+    g.N = c.f; g.K = c.d; g.lda = c.d; g.ldb = c.d; g.ldc = c.f;
+    g.b_estride = (int64_t)c.f * c.d;
+    rc = run_gemm<MODE_ROW, true, EPI_DGELU>(MOE_KERNEL_GEMM_DH, c, g, s);
+    if (rc != MOE_OK) return rc;
+    // dXp = dA W1^T: B = W1[e] as [N=d][K=f]
+    g.A = dA; g.B = W1; g.C = dXp; g.Aux = nullptr;
+    g.N = c.d; g.K = c.f; g.lda = c.f; g.ldb = c.f; g.ldc = c.d;
+    g.b_estride = (int64_t)c.d * c.f;
+    rc = run_gemm<MODE_ROW, true, EPI_STORE>(MOE_KERNEL_GEMM_DX, c, g, s);
+    if (rc != MOE_OK) return rc;
+  }
+  // dW2[e] = H_e^T dYp_e : M = f, N = d
+  g.A = H; g.B = dYp; g.C = dW2; g.Aux = nullptr;
+  g.M = c.f; g.N = c.d; g.lda = c.f; g.ldb = c.d; g.ldc = c.d;
+  g.c_estride = (int64_t)c.f * c.d;
+  rc = run_gemm<MODE_KRAG, false, EPI_STORE>(MOE_KERNEL_GEMM_DW2, c, g, s);
+  if (rc != MOE_OK) return rc;
+  // dW1[e] = x_perm_e^T dA_e : M = d, N = f
+  g.A = x_perm; g.B = dA; g.C = dW1;
+  g.M = c.d; g.N = c.f; g.lda = c.d; g.ldb = c.f; g.ldc = c.f;
+  g.c_estride = (int64_t)c.d * c.f;
+  return run_gemm<MODE_KRAG, false, EPI_STORE>(MOE_KERNEL_GEMM_DW1, c, g, s);
+}
+
+}  // namespace moe

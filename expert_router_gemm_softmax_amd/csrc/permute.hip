@@ -1,0 +1,167 @@
+// Permute with capacity drop (F2): per-expert histogram, exclusive scan of
+// the kept counts, stable scatter in token order, and the row copy
+// x -> x_perm.  Routed tokens are laid out contiguously per expert ("GPU
+// expert parallel", section "The step timeline"); assignments beyond the
+// capacity are dropped (distributed-training tutorial, "The Capacity
+// Factor"), the later tokens first.
+//
+// Determinism: atomics are used only to count (order-independent) and to
+// OR lane bits into 64-bit LDS masks; every position comes from scans and
+// popcounts in token order.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kPW = kPermTokens / kWave;  // waves per permute block
+
+// per-block expert histogram: blk[b][e] = #assignments of block b to e
+__global__ __launch_bounds__(kPermTokens) void permute_count_kernel(
+    const int32_t* __restrict__ idx, int32_t* __restrict__ blk, int64_t T_, int E, int k) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * kPermTokens + threadIdx.x;
+  if (t < T_)
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+    }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    blk[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Column scan over blocks (blk becomes each block's starting position per
+// expert), counts, and offsets = exclusive scan of min(count, C).
+__global__ __launch_bounds__(256) void permute_scan_kernel(
+    int32_t* __restrict__ blk, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int nblk, int E, int64_t cap) {
+  __shared__ int32_t kept[256];
+  const int e = threadIdx.x;
+  if (e < E) {
+    int32_t run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int32_t v = blk[(int64_t)b * E + e];
+      blk[(int64_t)b * E + e] = run;
+      run += v;
+    }
+    counts[e] = run;
+    kept[e] = (cap >= 0 && run > cap) ? (int32_t)cap : run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t o = 0;
+    for (int i = 0; i < E; ++i) {
+      offsets[i] = o;
+      o += kept[i];
+    }
+    offsets[E] = o;
+  }
+}
+
+// Rank every assignment among the assignments to the same expert in token
+// order, drop beyond capacity, write the maps, then copy rows.
+template <typename T>
+__global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
+    const T* __restrict__ x, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ blk, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ src_of, T* __restrict__ x_perm,
+    int64_t T_, int d, int E, int k, int64_t cap) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);  // [kPW][E]
+  int32_t* wbase = reinterpret_cast<int32_t*>(mask + kPW * E);            // [kPW][E]
+  int32_t* srow = wbase + kPW * E;                                         // [256][k]
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t0 = (int64_t)blockIdx.x * kPermTokens;
+  const int64_t t = t0 + threadIdx.x;
+  const bool valid = t < T_;
+
+  for (int i = threadIdx.x; i < kPW * E; i += blockDim.x) mask[i] = 0ull;
+  __syncthreads();
+  if (valid)
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if ((unsigned)e < (unsigned)E) atomicOr(&mask[w * E + e], 1ull << lane);
+    }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int32_t run = 0;
+    for (int ww = 0; ww < kPW; ++ww) {
+      wbase[ww * E + e] = run;
+      run += __popcll(mask[ww * E + e]);
+    }
+  }
+  __syncthreads();
+  if (valid) {
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if ((unsigned)e >= (unsigned)E) {  // outside the contract: treat as dropped
+        row_of[t * k + j] = -1;
+        srow[threadIdx.x * k + j] = -1;
+        continue;
+      }
+      const int64_t pos = (int64_t)blk[(int64_t)blockIdx.x * E + e] + wbase[w * E + e] +
+                          __popcll(mask[w * E + e] & lt);
+      int32_t row = -1;
+      if (cap < 0 || pos < cap) {
+        row = (int32_t)(offsets[e] + pos);
+        src_of[row] = (int32_t)(t * k + j);
+      }
+      row_of[t * k + j] = row;
+      srow[threadIdx.x * k + j] = row;
+    }
+  }
+  __syncthreads();
+  // row copy: each wave copies its 64 tokens, one 16-byte vector per lane
+  constexpr int V = St<T>::kVec;
+  const int nch = d / V;
+  for (int tt = 0; tt < kWave; ++tt) {
+    const int ti = w * kWave + tt;
+    const int64_t tok = t0 + ti;
+    if (tok >= T_) break;
+    const T* src = x + tok * (int64_t)d;
+    for (int c = lane; c < nch; c += kWave) {
+      const u32x4 v = ld16(src + c * V);
+      for (int j = 0; j < k; ++j) {
+        const int32_t row = srow[ti * k + j];
+        if (row >= 0) st16(x_perm + (int64_t)row * d + c * V, v);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
+                   int32_t* counts, int32_t* offsets, int32_t* row_of,
+                   int32_t* src_of, void* x_perm, void* ws, hipStream_t s) {
+  const WsLayout L = ws_layout(c);
+  int32_t* blk = ws_ptr<int32_t>(ws, L.perm_blk);
+  const int nblk = c.T > 0 ? (int)ceil_div(c.T, kPermTokens) : 0;
+  if (nblk > 0)
+    MOE_LAUNCH(MOE_KERNEL_PERMUTE_COUNT, s,
+               permute_count_kernel<<<nblk, kPermTokens, c.E * 4, s>>>(idx, blk, c.T,
+                                                                      c.E, c.k));
+  MOE_LAUNCH(MOE_KERNEL_PERMUTE_SCAN, s,
+             permute_scan_kernel<<<1, 256, 0, s>>>(blk, counts, offsets, nblk, c.E,
+                                                  c.capacity));
+  if (nblk > 0) {
+    const size_t sm = (size_t)kPW * c.E * 8 + (size_t)kPW * c.E * 4 +
+                      (size_t)kPermTokens * c.k * 4;
+    if (c.dtype == MOE_BF16)
+      MOE_LAUNCH(MOE_KERNEL_PERMUTE_SCATTER, s,
+                 permute_scatter_kernel<uint16_t><<<nblk, kPermTokens, sm, s>>>(
+                     static_cast<const uint16_t*>(x), idx, blk, offsets, row_of, src_of,
+                     static_cast<uint16_t*>(x_perm), c.T, c.d, c.E, c.k, c.capacity));
+    else
+      MOE_LAUNCH(MOE_KERNEL_PERMUTE_SCATTER, s,
+                 permute_scatter_kernel<float><<<nblk, kPermTokens, sm, s>>>(
+                     static_cast<const float*>(x), idx, blk, offsets, row_of, src_of,
+                     static_cast<float*>(x_perm), c.T, c.d, c.E, c.k, c.capacity));
+  }
+  return MOE_OK;
+}
+
+}  // namespace moe

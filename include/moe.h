@@ -1,0 +1,289 @@
+/*
+ * moe.h -- one GPU's share of an expert-parallel mixture-of-experts layer,
+ * forward and backward, as hand-written HIP kernels for MI355X (gfx950).
+ *
+ * The operation is the per-device step sequence of an MoE layer described
+ * in "GPU expert parallel" (aicassindra.com), section "The step timeline":
+ * the router scores every token, tokens are permuted into contiguous
+ * per-expert buffers, each expert's FFN runs over its rows as one grouped
+ * GEMM, and the inverse permutation restores token order; backward walks
+ * the same path in reverse.  Top-k and the capacity factor (tokens beyond
+ * an expert's capacity are dropped) follow the distributed-training
+ * tutorial (deepseekmodel.com), section "The Capacity Factor" and its EP
+ * configuration block.  The all-to-all exchanges and gradient reductions of
+ * those pages span several GPUs and are not part of this library.
+ *
+ * Conventions for every entry point
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or synchronises; each call only
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = default stream).
+ *  - Row-major, densely packed.  "s" is the activation/weight type given by
+ *    cfg->dtype: float (MOE_FP32) or bfloat16 bits (MOE_BF16, uint16).
+ *    Router probabilities, gates, gate gradients, dXe and db are float.
+ *  - Arguments are validated before anything is enqueued.  On an error the
+ *    call returns a negative moe_status, enqueues nothing and writes
+ *    nothing.  Device-side faults surface at the caller's next sync.
+ *  - Shapes: T >= 0, 1 <= k <= 32, k <= E <= 256, d >= 1, f >= 1, and
+ *    d * sizeof(s) and f * sizeof(s) multiples of 16 bytes
+ *    (MOE_ERR_ALIGN otherwise); every pointer 16-byte aligned.
+ *  - R = number of kept (token, expert) assignments, known only on the
+ *    device (offsets[E]).  Buffers with R rows are sized Rmax =
+ *    moe_rows_max(cfg); rows in [R, Rmax) are left untouched.
+ *  - Results are deterministic: identical inputs give bitwise identical
+ *    outputs (no result depends on the order of atomic operations).
+ *  - Non-finite inputs are outside the contract.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,            /* null pointer or out-of-range scalar */
+  MOE_ERR_DTYPE = -2,          /* unknown cfg->dtype */
+  MOE_ERR_SHAPE = -3,          /* inconsistent sizes */
+  MOE_ERR_ALIGN = -4,          /* row or pointer not 16-byte aligned */
+  MOE_ERR_WORKSPACE = -5,      /* ws_bytes < moe_workspace_bytes(cfg) */
+  MOE_ERR_LAUNCH = -6,         /* a kernel launch failed */
+  MOE_ERR_UNIMPLEMENTED = -7
+} moe_status;
+
+typedef enum { MOE_FP32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+#define MOE_NO_CAPACITY (-1)
+
+/* hipStream_t, passed opaquely so that this header needs no HIP headers. */
+typedef void* moe_stream_t;
+
+typedef struct moe_cfg {
+  int64_t T;          /* tokens; for the expert-share use (a ragged batch
+                         that arrives already permuted) the number of rows */
+  int32_t d;          /* model dim */
+  int32_t E;          /* experts held by this GPU */
+  int32_t k;          /* experts per token (top-k) */
+  int32_t f;          /* expert FFN hidden dim */
+  int32_t dtype;      /* moe_dtype of x, Wr, W1, W2 and every s tensor */
+  int64_t capacity;   /* per-expert capacity C >= 0, or MOE_NO_CAPACITY */
+  float route_margin; /* router certification margin (logit units); <= 0
+                         selects the default 1e-3.  See moe_route. */
+  uint32_t flags;     /* must be 0 */
+} moe_cfg;
+
+/* Capacity of the capacity-factor rule: C = ceil(cf * T * k / E).  A value
+ * of cf*T*k/E within 1e-9 (relative) above an integer counts as that
+ * integer, so decimal factors such as 1.1 are not pushed up by binary
+ * rounding.  cf < 0 returns MOE_NO_CAPACITY.
+ * Distributed-training tutorial, section "The Capacity Factor". */
+int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double cf);
+
+/* Rmax = min(T*k, E*C) (T*k without a capacity); -1 on invalid cfg. */
+int64_t moe_rows_max(const moe_cfg* cfg);
+
+/* Bytes of device workspace that any entry point taking `ws` needs for
+ * this cfg (the layer entry points need the most; one buffer of this size
+ * serves all of them).  0 on invalid cfg. */
+size_t moe_workspace_bytes(const moe_cfg* cfg);
+
+/* Human-readable text of a moe_status (static storage). */
+const char* moe_status_str(int status);
+
+/* Validates cfg alone (the checks every entry point starts with). */
+int moe_check_cfg(const moe_cfg* cfg);
+
+/* ---------------------------------------------------------------- forward */
+
+/* F1 router: every token gets a score per expert ("The step timeline");
+ * the router is a small replicated parameter whose decisions must agree on
+ * every rank ("Sharded by expert, replicated everywhere else").
+ *   x [T,d] s, Wr [d,E] s, b [E] float (NULL = zero bias)
+ *   probs [T,E] float  softmax over all E of z = x Wr + b
+ *   idx   [T,k] int32  the k experts in order (z descending, expert index
+ *                      ascending on equal z)
+ *   gate  [T,k] float  probs[t, idx[t,j]] (not renormalised)
+ * Decisions are made on the canonical logit RN_fp32(sum in fp64 + b): the
+ * fast fp32 logits are used where the top-(k+1) gaps exceed
+ * cfg->route_margin, and every logit that can change the decision is
+ * recomputed in fp64 otherwise.  Workspace: ws of ws_bytes >=
+ * moe_workspace_bytes(cfg) (holds a transposed copy of Wr). */
+int moe_route(const moe_cfg* cfg, const void* x, const void* Wr,
+              const float* b, float* probs, int32_t* idx, float* gate,
+              void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* F2 permute with capacity drop: the routed tokens are laid out in one
+ * contiguous buffer per expert ("The step timeline"); assignments beyond an
+ * expert's capacity are dropped ("The Capacity Factor").  Assignments are kept in
+ * token order: (t,j) is kept iff fewer than C earlier tokens chose expert
+ * idx[t,j].
+ *   idx [T,k] int32 (each row k distinct experts in [0,E))
+ *   counts  [E]   int32  routed assignments per expert, before the drop
+ *   offsets [E+1] int32  exclusive scan of min(counts, C); offsets[E] = R
+ *   row_of  [T,k] int32  row of (t,j) in x_perm, -1 if dropped
+ *   src_of  [Rmax] int32 t*k + j of the assignment in each row
+ *   x_perm  [Rmax,d] s   x_perm[r] = x[src_of[r] / k] (bitwise copy)
+ * Workspace: ws of ws_bytes >= moe_workspace_bytes(cfg). */
+int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx,
+                int32_t* counts, int32_t* offsets, int32_t* row_of,
+                int32_t* src_of, void* x_perm, void* ws, size_t ws_bytes,
+                moe_stream_t stream);
+
+/* F3+F4 grouped expert FFN over the ragged per-expert segments
+ * [offsets[e], offsets[e+1]) of x_perm: every local expert runs on the rows
+ * routed to it, as one grouped GEMM rather than one small GEMM per expert
+ * ("The step timeline").  fp32 accumulation; storage rounding RNE:
+ *   A = x_perm W1[e]      [Rmax,f] s   (saved for backward)
+ *   H = gelu_tanh(A)      [Rmax,f] s   (from the stored A)
+ *   Y = H W2[e]           [Rmax,d] s
+ * W1 [E,d,f] s, W2 [E,f,d] s.  offsets lives on the device and is never
+ * read back by the host.  Workspace as above. */
+int moe_grouped_ffn(const moe_cfg* cfg, const void* x_perm,
+                    const int32_t* offsets, const void* W1, const void* W2,
+                    void* A, void* H, void* Y, void* ws, size_t ws_bytes,
+                    moe_stream_t stream);
+
+/* F5 combine: the inverse of the permutation puts expert outputs back in
+ * token order ("The step timeline"), weighted by the gates:
+ *   out[t] = sum over kept j (ascending) of gate[t,j] * Y[row_of[t,j]],
+ * fp32 accumulation, one rounding to s; 0 for a token with every
+ * assignment dropped.  out [T,d] s. */
+int moe_combine(const moe_cfg* cfg, const void* Y, const int32_t* row_of,
+                const float* gate, void* out, moe_stream_t stream);
+
+/* --------------------------------------------------------------- backward
+ * The backward pass retraces the forward steps in reverse order ("The step
+ * timeline").  The
+ * upstream gradient is dOut [T,d] s, i.e. L = <out, dOut>. */
+
+/* B5 combine backward:
+ *   dYp[row_of[t,j]] = RN_s(gate[t,j] * dOut[t])  [Rmax,d] s
+ *   dgate[t,j]       = <dOut[t], Y[row_of[t,j]]>  [T,k] float (0 if dropped)
+ */
+int moe_combine_bwd(const moe_cfg* cfg, const void* dOut, const void* Y,
+                    const int32_t* row_of, const float* gate, void* dYp,
+                    float* dgate, moe_stream_t stream);
+
+/* B4+B3 grouped expert FFN backward; per expert e over its rows:
+ *   dH  = dYp W2[e]^T               (fp32, not stored)
+ *   dA  = RN_s(dH * gelu_tanh'(A))  (stored in the workspace)
+ *   dXp = dA W1[e]^T                [Rmax,d] s
+ *   dW2[e] = H^T dYp                [E,f,d] s
+ *   dW1[e] = x_perm^T dA            [E,d,f] s
+ * Experts with no rows get dW1[e] = dW2[e] = 0.  Expert weights live only
+ * on their owning rank and their gradients are reduced over the expert
+ * data-parallel group ("Two gradient reductions over two different
+ * groups"); that reduction spans GPUs and is the caller's.  Workspace as
+ * above. */
+int moe_grouped_ffn_bwd(const moe_cfg* cfg, const void* x_perm,
+                        const int32_t* offsets, const void* W1,
+                        const void* W2, const void* A, const void* H,
+                        const void* dYp, void* dXp, void* dW1, void* dW2,
+                        void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* B2 inverse of the permute for gradients:
+ *   dXe[t] = sum over kept j of dXp[row_of[t,j]]   [T,d] float */
+int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp,
+                      const int32_t* row_of, float* dXe, moe_stream_t stream);
+
+/* B1 router backward (the router is a shared parameter with an ordinary
+ * gradient -- "Sharded by expert, replicated everywhere else"):
+ *   dp[t, idx[t,j]] = dgate[t,j] for kept j, else 0
+ *   dz  = probs * (dp - sum_e probs * dp)
+ *   db  = sum_t dz                       [E] float
+ *   dWr = x^T dz                         [d,E] s
+ *   dX  = sum_{kept j} dXp[row_of[t,j]] + dz Wr^T   [T,d] s
+ * (the unpermute-sum of B2 is fused in).  Workspace as above. */
+int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr,
+                  const float* probs, const int32_t* idx,
+                  const int32_t* row_of, const float* dgate, const void* dXp,
+                  void* dX, void* dWr, float* db, void* ws, size_t ws_bytes,
+                  moe_stream_t stream);
+
+/* ------------------------------------------------------------ whole layer */
+
+typedef struct moe_weights {
+  const void* Wr;   /* [d,E] s */
+  const float* b;   /* [E] float, NULL = zero */
+  const void* W1;   /* [E,d,f] s */
+  const void* W2;   /* [E,f,d] s */
+} moe_weights;
+
+/* Saved forward state, all caller-owned device buffers.  The small integer
+ * routing map is kept and reused by backward instead of routing again
+ * (section "Recomputation re-runs the dispatch unless you save the
+ * permutation"). */
+typedef struct moe_ctx {
+  float* probs;     /* [T,E] float */
+  int32_t* idx;     /* [T,k] */
+  float* gate;      /* [T,k] float */
+  int32_t* counts;  /* [E] */
+  int32_t* offsets; /* [E+1] */
+  int32_t* row_of;  /* [T,k] */
+  int32_t* src_of;  /* [Rmax] */
+  void* x_perm;     /* [Rmax,d] s */
+  void* A;          /* [Rmax,f] s */
+  void* H;          /* [Rmax,f] s */
+  void* Y;          /* [Rmax,d] s */
+} moe_ctx;
+
+typedef struct moe_grads {
+  void* dWr;        /* [d,E] s */
+  float* db;        /* [E] float (may be NULL) */
+  void* dW1;        /* [E,d,f] s */
+  void* dW2;        /* [E,f,d] s */
+} moe_grads;
+
+/* Forward of the layer: moe_route, moe_permute, moe_grouped_ffn and
+ * moe_combine in sequence on `stream`; out [T,d] s. */
+int moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const void* x,
+                  void* out, const moe_ctx* ctx, void* ws, size_t ws_bytes,
+                  moe_stream_t stream);
+
+/* Backward of the layer from the saved ctx: moe_combine_bwd,
+ * moe_grouped_ffn_bwd and moe_route_bwd (dYp, dA, dXp and dgate live in
+ * the workspace); dX [T,d] s. */
+int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* x,
+                  const void* dOut, const moe_ctx* ctx, void* dX,
+                  const moe_grads* g, void* ws, size_t ws_bytes,
+                  moe_stream_t stream);
+
+/* ----------------------------------------------------------- measurement
+ * Kernel timing for benchmarks: after moe_prof_arm(kernel, n), the next n
+ * launches of that kernel are bracketed by HIP events on their stream;
+ * moe_prof_read waits for them and returns the summed milliseconds and
+ * the number of launches recorded.  Process-wide state: not for use from
+ * several threads at once.  Kernel ids: */
+typedef enum {
+  MOE_KERNEL_ROUTE = 0,
+  MOE_KERNEL_PERMUTE_COUNT = 1,
+  MOE_KERNEL_PERMUTE_SCAN = 2,
+  MOE_KERNEL_PERMUTE_SCATTER = 3,
+  MOE_KERNEL_GEMM_UP = 4,        /* A = x_perm W1, H = gelu(A) */
+  MOE_KERNEL_GEMM_DOWN = 5,      /* Y = H W2 */
+  MOE_KERNEL_COMBINE = 6,
+  MOE_KERNEL_COMBINE_BWD = 7,
+  MOE_KERNEL_GEMM_DH = 8,        /* dA = (dYp W2^T) * gelu'(A) */
+  MOE_KERNEL_GEMM_DX = 9,        /* dXp = dA W1^T */
+  MOE_KERNEL_GEMM_DW2 = 10,      /* dW2 = H^T dYp */
+  MOE_KERNEL_GEMM_DW1 = 11,      /* dW1 = x_perm^T dA */
+  MOE_KERNEL_UNPERMUTE_BWD = 12,
+  MOE_KERNEL_ROUTE_BWD_DZ = 13,
+  MOE_KERNEL_ROUTE_BWD_DX = 14,
+  MOE_KERNEL_ROUTE_BWD_DW = 15,
+  MOE_KERNEL_SCHEDULE = 16,
+  MOE_KERNEL_ROUTE_PREP = 17,    /* router weight transpose */
+  MOE_KERNEL_COUNT_ = 18
+} moe_kernel_id;
+
+int moe_prof_arm(int kernel_id, int max_launches);
+int moe_prof_read(float* total_ms, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -7,13 +7,13 @@ it, and this module imports nothing from the product package.
 
 What is computed, and where the pages say so:
 
-* Step order of the layer forward -- the router scores every token, tokens
-  are permuted into contiguous per-destination buffers, the local experts
-  run over what arrived, and the inverse permutation restores token order:
+* Step order of the layer forward -- score each token against every expert,
+  lay the routed tokens out contiguously per expert, run every local expert
+  on its rows, then undo the permutation back to token order:
   "GPU expert parallel" (aicassindra.com), section "The step timeline".
   The all-to-all exchanges of that section need several GPUs and are not
   part of one GPU's share.
-* Backward walks the same path in reverse: same section.
+* The backward pass retraces those steps in reverse: same section.
 * The router is replicated, must give identical decisions everywhere, and
   its gradient is an ordinary parameter gradient: section "Sharded by
   expert, replicated everywhere else".
@@ -106,7 +106,7 @@ def bf16_bits(a64: np.ndarray) -> np.ndarray:
 # ------------------------------------------------------------ F1: router
 def router_logits(x, Wr, b, round32: bool = True) -> np.ndarray:
     """z[t,e] = sum_i x[t,i] Wr[i,e] + b[e], summed in fp64, then rounded
-    once to fp32 (reading R3).  "The router scores every token"."""
+    once to fp32 (reading R3): every token is scored against every expert."""
     z = np.asarray(x, np.float64) @ np.asarray(Wr, np.float64)
     z = z + np.asarray(b, np.float64)[None, :]
     return fp32_rne(z) if round32 else z

@@ -1,0 +1,184 @@
+"""GPU parity of the HIP path (through the C-ABI) against the CPU oracle.
+
+Integer routing outputs (idx, counts, offsets, row_of, src_of) must be
+bit-exact and x_perm bitwise; float outputs within the stated tolerances:
+bf16 configs rtol 2e-2 / atol 1e-2, fp32 configs 1e-5 / 1e-5, router
+probabilities and gates 1e-5 / 1e-6 in every config.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_parity_helpers import (TOL, assert_close, cfg_of, check_layer_full,
+                                check_routing_exact, logit_error, make_case,
+                                run_layer, say, to_dev, to_f64, to_int)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import expert_router_gemm_softmax_amd as M
+    return M
+
+
+SMALL_CASES = [
+    # T, d, E, k, f, dtype, cf, bias
+    (64, 32, 4, 1, 64, "f32", 1.25, "zero"),        # the tiny fp32 workload
+    (300, 36, 5, 2, 52, "f32", 0.9, "normal"),      # fp32, ragged, drops
+    (1000, 264, 6, 2, 200, "bf16", 1.1, "zero"),    # ragged K and N tails, drops
+    (777, 128, 16, 4, 96, "bf16", None, "normal"),  # dropless, ragged T
+    (513, 64, 40, 3, 136, "bf16", 0.75, "zipf"),    # 2 router N tiles, skew + drops
+    (1, 64, 8, 2, 64, "bf16", 1.0, "zero"),         # a single token
+    (200, 64, 4, 4, 64, "bf16", None, "normal"),    # k == E
+    (260, 48, 130, 8, 40, "bf16", None, "normal"),  # E > 128: 8 router tiles, k = 8
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: "T{}d{}E{}k{}f{}{}".format(*c))
+def test_layer_matches_oracle_small(M, case):
+    T, d, E, k, f, dt, cf, bias = case
+    w, inp = make_case(T, d, E, k, f, dt, cf, bias, seed=T)
+    say("case", case)
+    res = run_layer(M, w, inp)
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    R = check_layer_full(res, fw, bw, w)
+    say("  R =", R, "of", T * k, "logit err", logit_error(res, fw))
+
+
+def test_tiny_workload_named(M):
+    w = W.get("C0")
+    inp = W.make_inputs(w, seed=0)
+    res = run_layer(M, w, inp)
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    check_layer_full(res, fw, bw, w)
+    assert fw["C"] == 20
+
+
+def test_zero_capacity_drops_everything(M):
+    w, inp = make_case(100, 64, 4, 2, 64, "bf16", 0.0, seed=3)
+    res = run_layer(M, w, inp)
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    check_layer_full(res, fw, bw, w)
+    assert int(to_int(res["offsets"])[-1]) == 0
+    assert np.all(to_f64(res["out"]) == 0) and np.all(to_f64(res["dX"]) == 0)
+    assert np.all(to_f64(res["dW1"]) == 0) and np.all(to_f64(res["dWr"]) == 0)
+
+
+def test_one_hot_expert_overflows_capacity(M):
+    # a large bias sends every token's first choice to expert 2
+    w, inp = make_case(600, 64, 8, 2, 64, "bf16", 1.0, seed=4)
+    inp["b"] = np.zeros(8, np.float32)
+    inp["b"][2] = 20.0
+    res = run_layer(M, w, inp)
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    check_layer_full(res, fw, bw, w)
+    assert fw["counts"][2] == 600 and np.diff(fw["offsets"])[2] == fw["C"]
+
+
+def test_exact_ties_go_to_the_lower_expert(M):
+    # duplicated router columns make logits of experts 1, 4 and 6 bitwise equal
+    w, inp = make_case(400, 64, 8, 2, 64, "bf16", None, seed=5)
+    inp["Wr"][:, 4] = inp["Wr"][:, 1]
+    inp["Wr"][:, 6] = inp["Wr"][:, 1]
+    res = run_layer(M, w, inp)
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    check_layer_full(res, fw, bw, w)
+    ties = np.isin(fw["idx"], [1, 4, 6]).any(axis=1)
+    assert ties.sum() > 50
+
+
+def test_zero_tokens(M):
+    import torch
+    w = W.custom(0, 64, 4, 2, 64, dtype="bf16", cf=None)
+    cfg = cfg_of(M, w)
+    e = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt, device="cuda")
+    layer = M.MoeLayer(cfg, e(64, 4), None, e(4, 64, 64), e(4, 64, 64))
+    x = e(0, 64)
+    out = layer.forward(x)
+    dX, g = layer.backward(x, e(0, 64))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+    assert to_int(layer.saved["counts"]).tolist() == [0] * 4
+    assert to_int(layer.saved["offsets"]).tolist() == [0] * 5
+    assert np.all(to_f64(g["dW1"]) == 0) and np.all(to_f64(g["dWr"]) == 0)
+
+
+def test_step_entry_points_equal_the_layer_entry_points(M):
+    """moe_route .. moe_route_bwd called one by one give bitwise the layer's
+    results (same kernels, same order)."""
+    import torch
+    w, inp = make_case(700, 128, 8, 2, 160, "bf16", 1.0, "normal", seed=7)
+    res = run_layer(M, w, inp)
+    cfg, d, L = res["_cfg"], res["_dev"], res["_layer"]
+    T, E, k = w.T, w.E, w.k
+    Rmax = M.moe_rows_max(cfg)
+    z = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt, device="cuda")
+    probs, idx, gate = z(T, E, dt=torch.float32), z(T, k, dt=torch.int32), z(T, k, dt=torch.float32)
+    ws = torch.zeros(M.moe_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    M.moe_route(cfg, d["x"], d["Wr"], d["b"], probs, idx, gate, ws)
+    counts, offsets = z(E, dt=torch.int32), z(E + 1, dt=torch.int32)
+    row_of, src_of, xp = z(T, k, dt=torch.int32), z(Rmax, dt=torch.int32), z(Rmax, w.d)
+    M.moe_permute(cfg, d["x"], idx, counts, offsets, row_of, src_of, xp, ws)
+    A, H, Y = z(Rmax, w.f), z(Rmax, w.f), z(Rmax, w.d)
+    M.moe_grouped_ffn(cfg, xp, offsets, d["W1"], d["W2"], A, H, Y, ws)
+    out = z(T, w.d)
+    M.moe_combine(cfg, Y, row_of, gate, out)
+    dYp, dg = z(Rmax, w.d), z(T, k, dt=torch.float32)
+    M.moe_combine_bwd(cfg, d["dOut"], Y, row_of, gate, dYp, dg)
+    dXp, dW1, dW2 = z(Rmax, w.d), torch.zeros_like(d["W1"]), torch.zeros_like(d["W2"])
+    M.moe_grouped_ffn_bwd(cfg, xp, offsets, d["W1"], d["W2"], A, H, dYp, dXp, dW1, dW2, ws)
+    dXe = z(T, w.d, dt=torch.float32)
+    M.moe_unpermute_bwd(cfg, dXp, row_of, dXe)
+    dX, dWr, db = z(T, w.d), torch.zeros_like(d["Wr"]), z(E, dt=torch.float32)
+    M.moe_route_bwd(cfg, d["x"], d["Wr"], probs, idx, row_of, dg, dXp, dX, dWr, db, ws)
+    torch.cuda.synchronize()
+    R = int(to_int(offsets)[-1])
+    for name, a, b in [("probs", probs, res["probs"]), ("idx", idx, res["idx"]),
+                       ("gate", gate, res["gate"]), ("offsets", offsets, res["offsets"]),
+                       ("row_of", row_of, res["row_of"]), ("out", out, res["out"]),
+                       ("dX", dX, res["dX"]), ("dWr", dWr, res["dWr"]), ("db", db, res["db"]),
+                       ("dW1", dW1, res["dW1"]), ("dW2", dW2, res["dW2"])]:
+        assert torch.equal(a, b), name
+    for name, a, b in [("x_perm", xp, res["x_perm"]), ("A", A, res["A"]),
+                       ("Y", Y, res["Y"]), ("src_of", src_of, res["src_of"])]:
+        assert torch.equal(a[:R], b[:R]), name
+    # unpermute-sum against the oracle definition on the GPU's own dXp
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    assert_close("dXe", to_f64(dXe), bw["dXe"], "bf16")
+    assert_close("dgate", to_f64(dg), bw["dgate"], "bf16")
+
+
+def test_runs_are_bitwise_deterministic(M):
+    import torch
+    w, inp = make_case(1500, 256, 16, 2, 384, "bf16", 1.0, "normal", seed=8)
+    a = run_layer(M, w, inp)
+    b = run_layer(M, w, inp)
+    for key in ("probs", "idx", "gate", "counts", "offsets", "row_of", "out", "dX",
+                "dWr", "db", "dW1", "dW2"):
+        assert torch.equal(a[key], b[key]), key
+    R = int(to_int(a["offsets"])[-1])
+    for key in ("src_of", "x_perm", "A", "H", "Y"):
+        assert torch.equal(a[key][:R], b[key][:R]), key
+
+
+def test_c1_full_layer_matches_oracle(M):
+    w = W.get("C1")
+    inp = W.make_inputs(w, seed=0)
+    res = run_layer(M, w, inp)
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    R = check_layer_full(res, fw, bw, w)
+    err = logit_error(res, fw)
+    say("C1 R", R, "logit err", err)
+    assert err <= 1e-3 / 2

@@ -1,0 +1,151 @@
+"""Host-side tests of the C-ABI library (no GPU needed, nothing is launched).
+
+The library must load, export every function include/moe.h declares, and
+reject invalid arguments before enqueueing anything.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+import workloads as W
+
+M = pytest.importorskip("expert_router_gemm_softmax_amd")
+B = M.binding
+
+
+def _declared_functions(repo_root):
+    text = open(os.path.join(repo_root, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function(repo_root):
+    names = _declared_functions(repo_root)
+    assert len(names) >= 15, names
+    lib = ctypes.CDLL(M.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding declares a signature for each one
+    assert set(names) <= set(B._SIGS), set(names) - set(B._SIGS)
+
+
+def test_library_is_in_tree_and_for_gfx950(repo_root):
+    assert os.path.dirname(M.LIB_PATH) == os.path.join(repo_root,
+                                                        "expert_router_gemm_softmax_amd")
+    blob = open(M.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+@pytest.mark.parametrize("T,k,E,cf", [(64, 1, 4, 1.25), (4096, 2, 8, 1.25),
+                                      (32768, 8, 128, 1.0), (80, 1, 8, 1.1),
+                                      (81, 1, 8, 1.1), (1000, 3, 7, 0.3),
+                                      (10, 2, 4, 0.0), (12345, 4, 96, 2.5)])
+def test_capacity_helper_matches_oracle(T, k, E, cf):
+    assert M.moe_capacity(T, k, E, cf) == O.capacity(T, k, E, cf)
+
+
+def test_capacity_negative_factor_means_no_limit():
+    assert M.moe_capacity(100, 2, 4, -1.0) == M.MOE_NO_CAPACITY
+
+
+def test_rows_max_and_workspace():
+    c = M.make_cfg(4096, 1024, 8, 2, 4096, "bf16", capacity=1280)
+    assert M.moe_rows_max(c) == 8192
+    c = M.make_cfg(32768, 4096, 128, 8, 1536, "bf16", capacity=2048)
+    assert M.moe_rows_max(c) == 128 * 2048
+    c = M.make_cfg(100, 32, 4, 2, 64, "f32", capacity=None)
+    assert M.moe_rows_max(c) == 200
+    assert M.moe_workspace_bytes(c) > 0
+    c0 = M.make_cfg(0, 32, 4, 2, 64, "bf16", capacity=None)
+    assert M.moe_rows_max(c0) == 0 and M.moe_workspace_bytes(c0) > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), B.MOE_ERR_ARG), (dict(k=33, E=64), B.MOE_ERR_ARG),
+    (dict(E=1, k=2), B.MOE_ERR_ARG), (dict(E=257), B.MOE_ERR_ARG),
+    (dict(d=0), B.MOE_ERR_ARG), (dict(f=0), B.MOE_ERR_ARG),
+    (dict(T=-1), B.MOE_ERR_ARG), (dict(capacity=-5), B.MOE_ERR_ARG),
+    (dict(d=12), B.MOE_ERR_ALIGN), (dict(f=20), B.MOE_ERR_ALIGN),
+])
+def test_invalid_cfg_is_rejected(kw, status):
+    base = dict(T=16, d=64, E=8, k=2, f=64, dtype="bf16", capacity=None)
+    base.update(kw)
+    cap = base.pop("capacity")
+    c = M.make_cfg(**base, capacity=None)
+    if cap is not None:
+        c.capacity = cap
+    assert M.moe_check_cfg(c) == status
+    assert M.moe_rows_max(c) == -1 and M.moe_workspace_bytes(c) == 0
+
+
+def test_bad_dtype_and_flags():
+    c = M.make_cfg(16, 64, 8, 2, 64, "bf16")
+    c.dtype = 7
+    assert M.moe_check_cfg(c) == B.MOE_ERR_DTYPE
+    c = M.make_cfg(16, 64, 8, 2, 64, "bf16")
+    c.flags = 1
+    assert M.moe_check_cfg(c) == B.MOE_ERR_ARG
+    c = M.make_cfg(16, 12, 8, 2, 64, "f32")   # 48-byte rows: aligned for fp32
+    assert M.moe_check_cfg(c) == B.MOE_OK
+
+
+# Fake device addresses: validation only inspects them, never dereferences.
+_A = 1 << 20
+
+
+def _call_route(cfg, **over):
+    args = dict(x=_A, Wr=_A, b=None, probs=_A, idx=_A, gate=_A, ws=_A,
+                ws_bytes=M.moe_workspace_bytes(cfg))
+    args.update(over)
+    return B.lib.moe_route(ctypes.byref(cfg), args["x"], args["Wr"], args["b"],
+                           args["probs"], args["idx"], args["gate"], args["ws"],
+                           args["ws_bytes"], None)
+
+
+def test_entry_points_reject_bad_arguments_before_launch():
+    c = M.make_cfg(16, 64, 8, 2, 64, "bf16")
+    assert _call_route(c, x=None) == B.MOE_ERR_ARG
+    assert _call_route(c, probs=None) == B.MOE_ERR_ARG
+    assert _call_route(c, x=_A + 2) == B.MOE_ERR_ALIGN
+    assert _call_route(c, ws_bytes=10) == B.MOE_ERR_WORKSPACE
+    assert _call_route(c, ws=None) == B.MOE_ERR_ARG
+    bad = M.make_cfg(16, 64, 8, 2, 64, "bf16")
+    bad.k = 9
+    assert _call_route(bad) == B.MOE_ERR_ARG
+    assert B.lib.moe_combine(ctypes.byref(c), None, _A, _A, _A, None) == B.MOE_ERR_ARG
+    assert B.lib.moe_permute(ctypes.byref(c), _A, _A, _A, _A, _A, _A, _A, _A, 0,
+                             None) == B.MOE_ERR_WORKSPACE
+    assert B.lib.moe_layer_fwd(ctypes.byref(c), None, _A, _A, None, _A, 1 << 30,
+                               None) == B.MOE_ERR_ARG
+    assert B.lib.moe_prof_arm(99, 1) == B.MOE_ERR_ARG
+
+
+def test_status_strings():
+    for st in range(-7, 1):
+        assert M.status_str(st) and M.status_str(st) != "unknown status"
+    assert M.status_str(-99) == "unknown status"
+
+
+def test_cfg_struct_layout_matches_header():
+    # int64 T; 5 x int32; int64 capacity (8-aligned); float; uint32 -> 48 bytes
+    assert ctypes.sizeof(B.MoeCfg) == 48
+    assert B.MoeCfg.capacity.offset == 32 and B.MoeCfg.flags.offset == 44
+
+
+def test_binding_has_no_oracle_dependency(repo_root):
+    pkg = os.path.join(repo_root, "expert_router_gemm_softmax_amd")
+    for root, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(root, fn)).read()
+                assert "import oracle" not in src and "from oracle" not in src, fn
+
+
+def test_workload_shapes_are_the_named_configs():
+    assert (W.get("C1").T, W.get("C1").d, W.get("C1").E, W.get("C1").k, W.get("C1").f) == \
+        (4096, 1024, 8, 2, 4096)
+    assert W.get("C4").cf == 1.0 and W.get("C2").cf is None
