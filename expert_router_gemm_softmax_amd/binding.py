@@ -32,7 +32,7 @@ KERNELS = dict(ROUTE=0, PERMUTE_COUNT=1, PERMUTE_SCAN=2, PERMUTE_SCATTER=3,
                GEMM_UP=4, GEMM_DOWN=5, COMBINE=6, COMBINE_BWD=7, GEMM_DH=8,
                GEMM_DX=9, GEMM_DW2=10, GEMM_DW1=11, UNPERMUTE_BWD=12,
                ROUTE_BWD_DZ=13, ROUTE_BWD_DX=14, ROUTE_BWD_DW=15, SCHEDULE=16,
-               ROUTE_PREP=17)
+               ROUTE_PREP=17, PERMUTE_COPY=18)
 
 
 class MoeLibraryError(ImportError):
@@ -41,7 +41,8 @@ class MoeLibraryError(ImportError):
 
 class MoeError(RuntimeError):
     def __init__(self, fn: str, status: int):
-        super().__init__(f"{fn} failed: {status} ({status_str(status)})")
+        detail = lib.moe_last_error().decode() if status == MOE_ERR_LAUNCH else ""
+        super().__init__(f"{fn} failed: {status} ({status_str(status)}) {detail}".rstrip())
         self.status = status
 
 
@@ -76,6 +77,7 @@ _SIGS = {
     "moe_workspace_bytes": (c_size_t, [_CFG]),
     "moe_status_str": (c_char_p, [c_int]),
     "moe_check_cfg": (c_int, [_CFG]),
+    "moe_last_error": (c_char_p, []),
     "moe_route": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_permute": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_grouped_ffn": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
@@ -93,11 +95,27 @@ _SIGS = {
 }
 
 
+def _hip_runtimes():
+    """Paths of the HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
 def _load():
+    # Device pointers and streams come from torch's HIP runtime; load it
+    # first so that libmoe.so's libamdhip64.so.7 resolves to that same
+    # runtime (by soname) instead of mapping a second one.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise MoeLibraryError(
             f"{LIB_PATH} is missing: build it with "
-            "`python -m expert_router_gemm_softmax_amd.build`")
+            "`python expert_router_gemm_softmax_amd/build.py`")
     try:
         lib = ctypes.CDLL(LIB_PATH)
     except OSError as e:
@@ -106,6 +124,11 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    rts = _hip_runtimes()
+    if len(rts) > 1:
+        raise MoeLibraryError(
+            "two HIP runtimes are mapped into this process (" + ", ".join(rts) + "); "
+            "import torch before anything that loads libamdhip64")
     return lib
 
 

@@ -1,6 +1,9 @@
 """Build libmoe.so (the HIP kernels and the C-ABI) in-tree for gfx950.
 
-    python -m expert_router_gemm_softmax_amd.build [--jobs N] [--verbose]
+    python expert_router_gemm_softmax_amd/build.py [--jobs N] [--verbose]
+
+(run by file path: importing the package loads libmoe.so, which may not
+exist yet)
 
 Each csrc/*.hip is compiled by hipcc for --offload-arch=gfx950 into
 _build/ at the repository root, then linked into

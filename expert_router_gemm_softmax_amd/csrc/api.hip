@@ -3,6 +3,7 @@
 // timing.  Every entry point validates everything before it enqueues
 // anything; on an error nothing is enqueued and nothing is written.
 #include <math.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <vector>
@@ -33,8 +34,24 @@ void prof_end(int kid, hipStream_t s) {
   g_prof.open = false;
 }
 
+namespace {
+thread_local char g_last_error[160] = "";
+}  // namespace
+
+void note_launch_error(int kid, hipError_t e) {
+  snprintf(g_last_error, sizeof g_last_error, "kernel %d: %s (%s)", kid, hipGetErrorName(e),
+           hipGetErrorString(e));
+}
+
 // ------------------------------------------------------------------ validation
 namespace {
+
+// Drop error state left by earlier HIP calls that are not this library's,
+// so that the checks after our launches see only our launches.
+inline void clear_stale_error() {
+  (void)hipGetLastError();
+  g_last_error[0] = '\0';
+}
 
 int check_cfg(const moe_cfg* c) {
   if (!c) return MOE_ERR_ARG;
@@ -146,6 +163,7 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* Wr, const float* b,
   MOE_TRY(need(gate, z.Tk, 4));
   MOE_TRY(need_ws(c, ws, ws_bytes));
   void* wrT = ws_ptr<void>(ws, ws_layout(c).wrT);
+  clear_stale_error();
   return launch_route(c, x, Wr, b, probs, idx, gate, wrT, S(stream));
 }
 
@@ -163,6 +181,7 @@ int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx, int32_t* 
   MOE_TRY(need(src_of, z.Rmax * 4, 4));
   MOE_TRY(need(x_perm, z.Rd, 16));
   MOE_TRY(need_ws(c, ws, ws_bytes));
+  clear_stale_error();
   return launch_permute(c, x, idx, counts, offsets, row_of, src_of, x_perm, ws, S(stream));
 }
 
@@ -180,6 +199,7 @@ int moe_grouped_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offse
   MOE_TRY(need(H, z.Rf, 16));
   MOE_TRY(need(Y, z.Rd, 16));
   MOE_TRY(need_ws(c, ws, ws_bytes));
+  clear_stale_error();
   return launch_ffn_fwd(c, x_perm, offsets, W1, W2, A, H, Y, ws, S(stream));
 }
 
@@ -192,6 +212,7 @@ int moe_combine(const moe_cfg* cfg, const void* Y, const int32_t* row_of, const 
   MOE_TRY(need(row_of, z.Tk, 4));
   MOE_TRY(need(gate, z.Tk, 4));
   MOE_TRY(need(out, z.Td, 16));
+  clear_stale_error();
   return launch_combine(c, Y, row_of, gate, out, S(stream));
 }
 
@@ -207,6 +228,7 @@ int moe_combine_bwd(const moe_cfg* cfg, const void* dOut, const void* Y,
   MOE_TRY(need(gate, z.Tk, 4));
   MOE_TRY(need(dYp, z.Rd, 16));
   MOE_TRY(need(dgate, z.Tk, 4));
+  clear_stale_error();
   return launch_combine_bwd(c, dOut, Y, row_of, gate, dYp, dgate, S(stream));
 }
 
@@ -228,6 +250,7 @@ int moe_grouped_ffn_bwd(const moe_cfg* cfg, const void* x_perm, const int32_t* o
   MOE_TRY(need(dW1, z.Edf, 16));
   MOE_TRY(need(dW2, z.Edf, 16));
   MOE_TRY(need_ws(c, ws, ws_bytes));
+  clear_stale_error();
   return launch_ffn_bwd(c, x_perm, offsets, W1, W2, A, H, dYp, dXp, dW1, dW2, ws,
                         S(stream));
 }
@@ -240,6 +263,7 @@ int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp, const int32_t* row_of
   MOE_TRY(need(dXp, z.Rd, 16));
   MOE_TRY(need(row_of, z.Tk, 4));
   MOE_TRY(need(dXe, (size_t)c.T * c.d * 4, 16));
+  clear_stale_error();
   return launch_unpermute_bwd(c, dXp, row_of, dXe, S(stream));
 }
 
@@ -261,6 +285,7 @@ int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr, const float
   MOE_TRY(need(dWr, z.dE, 4));
   if (db) MOE_TRY(need(db, (size_t)c.E * 4, 4));
   MOE_TRY(need_ws(c, ws, ws_bytes));
+  clear_stale_error();
   return launch_route_bwd(c, x, Wr, probs, idx, row_of, dgate, dXp, dX, dWr, db, ws,
                           S(stream));
 }
@@ -304,6 +329,7 @@ int moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const void* x, void*
   MOE_TRY(need_ws(c, ws, ws_bytes));
   const hipStream_t s = S(stream);
   const WsLayout L = ws_layout(c);
+  clear_stale_error();
   MOE_TRY(launch_route(c, x, w->Wr, w->b, ctx->probs, ctx->idx, ctx->gate,
                        ws_ptr<void>(ws, L.wrT), s));
   MOE_TRY(launch_permute(c, x, ctx->idx, ctx->counts, ctx->offsets, ctx->row_of,
@@ -335,12 +361,15 @@ int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* x, const
   float* dgate = ws_ptr<float>(ws, L.dgate);
   void* dYp = ws_ptr<void>(ws, L.dYp);
   void* dXp = ws_ptr<void>(ws, L.dXp);
+  clear_stale_error();
   MOE_TRY(launch_combine_bwd(c, dOut, ctx->Y, ctx->row_of, ctx->gate, dYp, dgate, s));
   MOE_TRY(launch_ffn_bwd(c, ctx->x_perm, ctx->offsets, w->W1, w->W2, ctx->A, ctx->H, dYp,
                          dXp, g->dW1, g->dW2, ws, s));
   return launch_route_bwd(c, x, w->Wr, ctx->probs, ctx->idx, ctx->row_of, dgate, dXp, dX,
                           g->dWr, g->db, ws, s);
 }
+
+const char* moe_last_error(void) { return g_last_error; }
 
 int moe_prof_arm(int kernel_id, int max_launches) {
   if (kernel_id < 0 || kernel_id >= MOE_KERNEL_COUNT_ || max_launches < 0)

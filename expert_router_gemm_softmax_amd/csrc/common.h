@@ -107,25 +107,25 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // ------------------------------------------------------------------ workspace
 // One workspace buffer serves every entry point; each region is 256-byte
 // aligned.  Regions:
-//   wrT        [Epad, d] s           router weights transposed, zero rows >= E
-//   perm_blk   [nblk_perm, E] int32  per-block expert histograms / bases
-//   tiles      [E+1] int32           grouped-GEMM M-tile prefix per expert
-//   dz         [T, E] float          router logit gradient
-//   dwr_part   [nsplit, d, E] float  split-T partial sums of x^T dz
-//   db_part    [nsplit, E] float     split-T partial sums of dz
-//   dgate      [T, k] float          combine-backward gate gradient
-//   dYp        [Rmax, d] s           combine-backward row gradient
-//   dA         [Rmax, f] s           GELU-backward hidden gradient
-//   dXp        [Rmax, d] s           expert input gradient
-//   dw_part    [nsplitk, tile] float split-K partials of weight gradients
+//   wrT      [Epad, d] s        router weights transposed, zero rows >= E
+//   perm_blk [nblk_perm, E] i32 per-block expert histograms / bases
+//   tiles    [E+1] i32          grouped-GEMM M-tile prefix per expert
+//   dz       [T, E] f32         router logit gradient (float storage)
+//   dzb      [T, 2*Ep] bf16     dz split into bf16 high and low parts
+//   wrp      [d, 2*Ep] bf16     Wr twice side by side, zero padded (bf16)
+//   dwr_part [nchunk, d, Nw] f32 per-token-chunk partial sums of x^T dz
+//   db_part  [nblk_dz, E] f32   per-block partial sums of dz
+//   dgate    [T, k] f32         combine-backward gate gradient
+//   dYp, dA, dXp                backward row gradients (Rmax rows, s)
 struct WsLayout {
-  size_t wrT, perm_blk, tiles, dz, dwr_part, db_part, dgate, dYp, dA, dXp, total;
+  size_t wrT, perm_blk, tiles, dz, dzb, wrp, dwr_part, db_part, dgate, dYp, dA, dXp, total;
   int nblk_perm;
-  int dwr_split;
+  int nblk_dz;
+  int dwr_chunks, dwr_chunk, dwr_n;
 };
 
 constexpr int kPermTokens = 256;  // tokens per permute block
-constexpr int kDwrRows = 1024;    // tokens per split of the dWr reduction
+constexpr int kDzTokens = 64;     // tokens per router-backward dz block
 
 inline int64_t rows_max(const moe_cfg& c) {
   const int64_t tk = c.T * c.k;
@@ -139,6 +139,8 @@ inline int route_epad(int E) {
   const int nt = (E + 31) / 32;
   return 32 * (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8);
 }
+// experts padded to a multiple of 8 (16-byte bf16 rows) in the router backward
+inline int bwd_ep(int E) { return (E + 7) / 8 * 8; }
 
 inline size_t elem_bytes(const moe_cfg& c) { return c.dtype == MOE_BF16 ? 2 : 4; }
 
@@ -146,8 +148,20 @@ inline WsLayout ws_layout(const moe_cfg& c) {
   WsLayout L{};
   const size_t s = elem_bytes(c);
   const int64_t Rmax = rows_max(c);
-  L.nblk_perm = (int)ceil_div(c.T > 0 ? c.T : 1, kPermTokens);
-  L.dwr_split = (int)ceil_div(c.T > 0 ? c.T : 1, kDwrRows);
+  const int64_t T1 = c.T > 0 ? c.T : 1;
+  L.nblk_perm = (int)ceil_div(T1, kPermTokens);
+  L.nblk_dz = (int)ceil_div(T1, kDzTokens);
+  // dWr = x^T dz as a k-ragged GEMM over uniform token chunks: enough chunks
+  // for ~1024 blocks of 128 x 128 output tiles, at least 256 tokens each
+  const bool bf = c.dtype == MOE_BF16;
+  L.dwr_n = bf ? 2 * bwd_ep(c.E) : c.E;
+  const int64_t tiles = ceil_div(c.d, bf ? 128 : 64) * ceil_div(L.dwr_n, bf ? 128 : 64);
+  int64_t nch = ceil_div(1024, tiles);
+  const int64_t cap = ceil_div(T1, 256);
+  if (nch > cap) nch = cap;
+  if (nch < 1) nch = 1;
+  L.dwr_chunk = (int)(ceil_div(ceil_div(T1, nch), 64) * 64);
+  L.dwr_chunks = (int)ceil_div(T1, L.dwr_chunk);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -157,9 +171,11 @@ inline WsLayout ws_layout(const moe_cfg& c) {
   L.wrT = take((size_t)route_epad(c.E) * c.d * s);
   L.perm_blk = take((size_t)L.nblk_perm * c.E * 4);
   L.tiles = take((size_t)(c.E + 1) * 4 * 4);
-  L.dz = take((size_t)c.T * c.E * 4);
-  L.dwr_part = take((size_t)L.dwr_split * c.d * c.E * 4);
-  L.db_part = take((size_t)L.dwr_split * c.E * 4);
+  L.dz = take(bf ? 0 : (size_t)c.T * c.E * 4);
+  L.dzb = take(bf ? (size_t)c.T * 2 * bwd_ep(c.E) * 2 : 0);
+  L.wrp = take(bf ? (size_t)c.d * 2 * bwd_ep(c.E) * 2 : 0);
+  L.dwr_part = take((size_t)L.dwr_chunks * c.d * L.dwr_n * 4);
+  L.db_part = take((size_t)L.nblk_dz * c.E * 4);
   L.dgate = take((size_t)c.T * c.k * 4);
   L.dYp = take((size_t)Rmax * c.d * s);
   L.dA = take((size_t)Rmax * c.f * s);
@@ -176,14 +192,20 @@ inline P* ws_ptr(void* ws, size_t off) {
 // ------------------------------------------------------------------ launch + timing
 void prof_begin(int kernel_id, hipStream_t s);
 void prof_end(int kernel_id, hipStream_t s);
+void note_launch_error(int kernel_id, hipError_t e);
 
+// Launch, then check that launch.  Entry points clear any error state left
+// by earlier, unrelated HIP calls of the process before their first launch.
 #define MOE_LAUNCH(kid, stream, ...)                                  \
   do {                                                                \
     ::moe::prof_begin((kid), (stream));                               \
     __VA_ARGS__;                                                      \
     hipError_t e_ = hipGetLastError();                                \
     ::moe::prof_end((kid), (stream));                                 \
-    if (e_ != hipSuccess) return MOE_ERR_LAUNCH;                      \
+    if (e_ != hipSuccess) {                                           \
+      ::moe::note_launch_error((kid), e_);                            \
+      return MOE_ERR_LAUNCH;                                          \
+    }                                                                 \
   } while (0)
 
 // ------------------------------------------------------------------ launchers

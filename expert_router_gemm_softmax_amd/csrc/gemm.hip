@@ -21,27 +21,9 @@
 // registers on their way into LDS.  Tiles are ordered so that the blocks
 // resident on one XCD (block id mod 8) work on a compact group of output
 // tiles, which keeps their operand panels in that XCD's L2.
-#include "common.h"
+#include "gemm.h"
 
 namespace moe {
-
-enum { MODE_ROW = 0, MODE_KRAG = 1 };
-enum { EPI_STORE = 0, EPI_GELU = 1, EPI_DGELU = 2 };
-
-struct GemmArgs {
-  const void* A;
-  const void* B;
-  void* C;
-  void* C2;            // EPI_GELU: H = gelu(A_out)
-  const void* Aux;     // EPI_DGELU: forward pre-activation, laid out like C
-  const int32_t* offsets;
-  const int32_t* tiles;  // ROW: prefix of M tiles per expert, [E+1]
-  int E, M, N, K;        // ROW uses N, K; KRAG uses M, N
-  int lda, ldb, ldc;     // leading dims (elements)
-  int64_t b_estride;     // ROW: elements between experts' B
-  int64_t c_estride;     // KRAG: elements between experts' C
-  int ntn, ntm;          // N tiles; KRAG: M tiles per expert
-};
 
 constexpr int kGroupM = 4;  // M tiles per traversal group
 
@@ -76,6 +58,20 @@ struct Tile {
 template <int MODE, int BM, int BN>
 __device__ __forceinline__ bool decode_tile(const GemmArgs& g, int* s_tiles, Tile& t) {
   if constexpr (MODE == MODE_ROW) {
+    if (!g.offsets) {  // one group of g.M rows
+      const int num_m = (g.M + BM - 1) / BM;
+      int lid;
+      if (!xcd_logical(num_m * g.ntn, lid)) return false;
+      int mt, nt;
+      group_mn(lid, num_m, g.ntn, mt, nt);
+      t.e = 0;
+      t.row0 = 0;
+      t.M = g.M;
+      t.m0 = mt * BM;
+      t.n0 = nt * BN;
+      t.K = g.K;
+      return true;
+    }
     for (int i = threadIdx.x; i <= g.E; i += blockDim.x) s_tiles[i] = g.tiles[i];
     __syncthreads();
     const int num_m = s_tiles[g.E];
@@ -102,8 +98,13 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, int* s_tiles, Til
     t.e = lid / per_e;
     int mt, nt;
     group_mn(lid - t.e * per_e, g.ntm, g.ntn, mt, nt);
-    t.row0 = g.offsets[t.e];
-    t.K = g.offsets[t.e + 1] - (int)t.row0;
+    if (g.offsets) {
+      t.row0 = g.offsets[t.e];
+      t.K = g.offsets[t.e + 1] - (int)t.row0;
+    } else {  // uniform groups of g.chunk rows out of g.K
+      t.row0 = (int64_t)t.e * g.chunk;
+      t.K = min(g.chunk, g.K - (int)t.row0);
+    }
     t.M = g.M;
     t.m0 = mt * BM;
     t.n0 = nt * BN;
@@ -184,9 +185,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr bool A_KC = (MODE == MODE_ROW);
-  __shared__ __align__(16) uint16_t sA[2][BM * BK];
-  __shared__ __align__(16) uint16_t sB[2][BN * BK];
+  // operand tiles, double buffered; reused as the epilogue staging area
+  __shared__ __align__(16) uint16_t smem[2 * BM * BK + 2 * BN * BK];
   __shared__ int s_tiles[MODE == MODE_ROW ? 257 : 1];
+  uint16_t (*sA)[BM * BK] = reinterpret_cast<uint16_t (*)[BM * BK]>(smem);
+  uint16_t (*sB)[BN * BK] = reinterpret_cast<uint16_t (*)[BN * BK]>(smem + 2 * BM * BK);
 
   Tile t;
   if (!decode_tile<MODE, BM, BN>(g, s_tiles, t)) return;
@@ -263,37 +266,73 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // epilogue: D[i][j] at lane (j + 32*((i/4)%2)), register (i%4) + 4*(i/8)
-  uint16_t* C = static_cast<uint16_t*>(g.C);
-  uint16_t* C2 = static_cast<uint16_t*>(g.C2);
-  const uint16_t* Aux = static_cast<const uint16_t*>(g.Aux);
+  // Epilogue through LDS: each wave stages 32 rows x WN columns of its
+  // accumulators (D[i][j] sits in lane j + 32*((i/4)%2), register
+  // (i%4) + 4*(i/8)), then every lane handles 8 consecutive columns of a row
+  // with 16-byte loads and stores.
+  constexpr int SP = WN + 4;        // staging row stride (floats)
+  constexpr int LPR = WN / 8;       // lanes per staged row
+  constexpr int RPP = kWave / LPR;  // rows per pass
+  static_assert(4 * 32 * SP * 4 <= (int)sizeof(smem), "staging does not fit");
+  float* stage = reinterpret_cast<float*>(smem) + w * 32 * SP;
   int64_t cbase;
   if constexpr (MODE == MODE_ROW) cbase = t.row0 * g.ldc;
   else cbase = (int64_t)t.e * g.c_estride;
-  const int mlim = t.M;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = t.n0 + wn * WN + j * 32 + r;
-      if (col >= g.N) continue;
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = t.m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (row >= mlim) continue;
+      for (int v = 0; v < 16; ++v)
+        stage[(8 * (v >> 2) + 4 * h + (v & 3)) * SP + j * 32 + r] = acc[i][j][v];
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 32 / RPP; ++p) {
+      const int rl = p * RPP + lane / LPR, cl = (lane % LPR) * 8;
+      const int row = t.m0 + wm * WM + i * 32 + rl;
+      const int col = t.n0 + wn * WN + cl;
+      if (row < t.M && col < g.N) {
+        float v8[8];
+        *reinterpret_cast<f32x4*>(v8) = *reinterpret_cast<const f32x4*>(stage + rl * SP + cl);
+        *reinterpret_cast<f32x4*>(v8 + 4) =
+            *reinterpret_cast<const f32x4*>(stage + rl * SP + cl + 4);
         const int64_t o = cbase + (int64_t)row * g.ldc + col;
-        const float a = acc[i][j][v];
-        if constexpr (EPI == EPI_STORE) {
-          C[o] = f2bf(a);
+        if constexpr (EPI == EPI_F32) {
+          float* C = static_cast<float*>(g.C) + o;
+          *reinterpret_cast<f32x4*>(C) = *reinterpret_cast<const f32x4*>(v8);
+          *reinterpret_cast<f32x4*>(C + 4) = *reinterpret_cast<const f32x4*>(v8 + 4);
+        } else if constexpr (EPI == EPI_STORE) {
+          st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
         } else if constexpr (EPI == EPI_GELU) {
-          const uint16_t ab = f2bf(a);
-          C[o] = ab;
-          C2[o] = f2bf(gelu_tanh(bf2f(ab)));
+          const u32x4 ab = St<uint16_t>::pack(v8);
+          st16(static_cast<uint16_t*>(g.C) + o, ab);
+          float a8[8];
+          St<uint16_t>::unpack(ab, a8);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) a8[q] = gelu_tanh(a8[q]);
+          st16(static_cast<uint16_t*>(g.C2) + o, St<uint16_t>::pack(a8));
+        } else if constexpr (EPI == EPI_UNPERM) {
+          const int32_t* ro = g.aux_idx + (t.row0 + row) * (int64_t)g.aux_k;
+          for (int jj = 0; jj < g.aux_k; ++jj) {
+            const int32_t rr = ro[jj];
+            if (rr < 0) continue;
+            float x8[8];
+            St<uint16_t>::unpack(
+                ld16(static_cast<const uint16_t*>(g.Aux) + (int64_t)rr * g.ldc + col), x8);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v8[q] += x8[q];
+          }
+          st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
         } else {
-          C[o] = f2bf(a * gelu_tanh_grad(bf2f(Aux[o])));
+          float x8[8];
+          St<uint16_t>::unpack(ld16(static_cast<const uint16_t*>(g.Aux) + o), x8);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v8[q] *= gelu_tanh_grad(x8[q]);
+          st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
         }
       }
     }
+    __syncthreads();
   }
 }
 
@@ -368,7 +407,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       const int col = t.n0 + tx * 4 + j;
       if (col >= g.N) continue;
       const int64_t o = cbase + (int64_t)row * g.ldc + col;
-      if constexpr (EPI == EPI_STORE) C[o] = acc[i][j];
+      if constexpr (EPI == EPI_STORE || EPI == EPI_F32) C[o] = acc[i][j];
+      else if constexpr (EPI == EPI_UNPERM) {
+        float sum = acc[i][j];
+        const int32_t* ro = g.aux_idx + (t.row0 + row) * (int64_t)g.aux_k;
+        for (int jj = 0; jj < g.aux_k; ++jj)
+          if (ro[jj] >= 0) sum += Aux[(int64_t)ro[jj] * g.ldc + col];
+        C[o] = sum;
+      }
       else if constexpr (EPI == EPI_GELU) { C[o] = acc[i][j]; C2[o] = gelu_tanh(acc[i][j]); }
       else C[o] = acc[i][j] * gelu_tanh_grad(Aux[o]);
     }
@@ -406,10 +452,10 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
   g.ntn = (int)ceil_div(g.N, BN);
   int64_t nblk;
   if constexpr (MODE == MODE_ROW) {
-    nblk = row_mtiles_bound(c, BM) * g.ntn;
+    nblk = g.offsets ? row_mtiles_bound(c, BM) * g.ntn : ceil_div(g.M, BM) * g.ntn;
   } else {
     g.ntm = (int)ceil_div(g.M, BM);
-    nblk = (int64_t)c.E * g.ntm * g.ntn;
+    nblk = (int64_t)g.E * g.ntm * g.ntn;
   }
   if (nblk == 0) return MOE_OK;
   const int grid = grid8(nblk);
@@ -428,6 +474,30 @@ int schedule(const moe_cfg& c, const int32_t* offsets, int32_t* tiles, hipStream
 }
 
 }  // namespace
+
+int launch_gemm_schedule(const moe_cfg& c, const int32_t* offsets, int32_t* tiles,
+                         hipStream_t s) {
+  return schedule(c, offsets, tiles, s);
+}
+
+int launch_gemm(int kid, int mode, bool b_kc, int epi, const moe_cfg& c, GemmArgs g,
+                hipStream_t s) {
+  if (mode == MODE_ROW && !b_kc && epi == EPI_GELU)
+    return run_gemm<MODE_ROW, false, EPI_GELU>(kid, c, g, s);
+  if (mode == MODE_ROW && !b_kc && epi == EPI_STORE)
+    return run_gemm<MODE_ROW, false, EPI_STORE>(kid, c, g, s);
+  if (mode == MODE_ROW && b_kc && epi == EPI_DGELU)
+    return run_gemm<MODE_ROW, true, EPI_DGELU>(kid, c, g, s);
+  if (mode == MODE_ROW && b_kc && epi == EPI_STORE)
+    return run_gemm<MODE_ROW, true, EPI_STORE>(kid, c, g, s);
+  if (mode == MODE_KRAG && !b_kc && epi == EPI_STORE)
+    return run_gemm<MODE_KRAG, false, EPI_STORE>(kid, c, g, s);
+  if (mode == MODE_KRAG && !b_kc && epi == EPI_F32)
+    return run_gemm<MODE_KRAG, false, EPI_F32>(kid, c, g, s);
+  if (mode == MODE_ROW && b_kc && epi == EPI_UNPERM)
+    return run_gemm<MODE_ROW, true, EPI_UNPERM>(kid, c, g, s);
+  return MOE_ERR_UNIMPLEMENTED;
+}
 
 int launch_ffn_fwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
                    const void* W1, const void* W2, void* A, void* H, void* Y, void* ws,

@@ -61,17 +61,14 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
 }
 
 // Rank every assignment among the assignments to the same expert in token
-// order, drop beyond capacity, write the maps, then copy rows.
-template <typename T>
+// order, drop beyond capacity, and write the maps.
 __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
-    const T* __restrict__ x, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ blk, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ row_of, int32_t* __restrict__ src_of, T* __restrict__ x_perm,
-    int64_t T_, int d, int E, int k, int64_t cap) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ blk,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ src_of, int64_t T_, int E, int k, int64_t cap) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);  // [kPW][E]
   int32_t* wbase = reinterpret_cast<int32_t*>(mask + kPW * E);            // [kPW][E]
-  int32_t* srow = wbase + kPW * E;                                         // [256][k]
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t0 = (int64_t)blockIdx.x * kPermTokens;
   const int64_t t = t0 + threadIdx.x;
@@ -99,7 +96,6 @@ __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
       const int e = idx[t * k + j];
       if ((unsigned)e >= (unsigned)E) {  // outside the contract: treat as dropped
         row_of[t * k + j] = -1;
-        srow[threadIdx.x * k + j] = -1;
         continue;
       }
       const int64_t pos = (int64_t)blk[(int64_t)blockIdx.x * E + e] + wbase[w * E + e] +
@@ -110,23 +106,39 @@ __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
         src_of[row] = (int32_t)(t * k + j);
       }
       row_of[t * k + j] = row;
-      srow[threadIdx.x * k + j] = row;
     }
   }
-  __syncthreads();
-  // row copy: each wave copies its 64 tokens, one 16-byte vector per lane
+}
+
+// x_perm[row_of[t,j]] = x[t]: one wave per token reads the row once (up to
+// kCopyVec 16-byte vectors per lane in flight) and writes every kept copy.
+constexpr int kCopyVec = 4;
+template <typename T>
+__global__ __launch_bounds__(256) void permute_copy_kernel(
+    const T* __restrict__ x, const int32_t* __restrict__ row_of, T* __restrict__ x_perm,
+    int64_t T_, int d, int k) {
   constexpr int V = St<T>::kVec;
+  const int lane = threadIdx.x & 63;
   const int nch = d / V;
-  for (int tt = 0; tt < kWave; ++tt) {
-    const int ti = w * kWave + tt;
-    const int64_t tok = t0 + ti;
-    if (tok >= T_) break;
-    const T* src = x + tok * (int64_t)d;
-    for (int c = lane; c < nch; c += kWave) {
-      const u32x4 v = ld16(src + c * V);
+  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T_;
+       t += (int64_t)gridDim.x * 4) {
+    const T* src = x + t * (int64_t)d;
+    for (int c0 = 0; c0 < nch; c0 += kWave * kCopyVec) {
+      u32x4 v[kCopyVec];
+#pragma unroll
+      for (int q = 0; q < kCopyVec; ++q) {
+        const int c = c0 + q * kWave + lane;
+        if (c < nch) v[q] = ld16(src + c * V);
+      }
       for (int j = 0; j < k; ++j) {
-        const int32_t row = srow[ti * k + j];
-        if (row >= 0) st16(x_perm + (int64_t)row * d + c * V, v);
+        const int32_t row = row_of[t * k + j];
+        if (row < 0) continue;
+        T* dst = x_perm + (int64_t)row * d;
+#pragma unroll
+        for (int q = 0; q < kCopyVec; ++q) {
+          const int c = c0 + q * kWave + lane;
+          if (c < nch) st16(dst + c * V, v[q]);
+        }
       }
     }
   }
@@ -148,18 +160,21 @@ int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
              permute_scan_kernel<<<1, 256, 0, s>>>(blk, counts, offsets, nblk, c.E,
                                                   c.capacity));
   if (nblk > 0) {
-    const size_t sm = (size_t)kPW * c.E * 8 + (size_t)kPW * c.E * 4 +
-                      (size_t)kPermTokens * c.k * 4;
+    const size_t sm = (size_t)kPW * c.E * 8 + (size_t)kPW * c.E * 4;
+    MOE_LAUNCH(MOE_KERNEL_PERMUTE_SCATTER, s,
+               permute_scatter_kernel<<<nblk, kPermTokens, sm, s>>>(
+                   idx, blk, offsets, row_of, src_of, c.T, c.E, c.k, c.capacity));
+    const int g = (int)std::min<int64_t>(ceil_div(c.T, 4), 65536);
     if (c.dtype == MOE_BF16)
-      MOE_LAUNCH(MOE_KERNEL_PERMUTE_SCATTER, s,
-                 permute_scatter_kernel<uint16_t><<<nblk, kPermTokens, sm, s>>>(
-                     static_cast<const uint16_t*>(x), idx, blk, offsets, row_of, src_of,
-                     static_cast<uint16_t*>(x_perm), c.T, c.d, c.E, c.k, c.capacity));
+      MOE_LAUNCH(MOE_KERNEL_PERMUTE_COPY, s,
+                 permute_copy_kernel<uint16_t><<<g, 256, 0, s>>>(
+                     static_cast<const uint16_t*>(x), row_of,
+                     static_cast<uint16_t*>(x_perm), c.T, c.d, c.k));
     else
-      MOE_LAUNCH(MOE_KERNEL_PERMUTE_SCATTER, s,
-                 permute_scatter_kernel<float><<<nblk, kPermTokens, sm, s>>>(
-                     static_cast<const float*>(x), idx, blk, offsets, row_of, src_of,
-                     static_cast<float*>(x_perm), c.T, c.d, c.E, c.k, c.capacity));
+      MOE_LAUNCH(MOE_KERNEL_PERMUTE_COPY, s,
+                 permute_copy_kernel<float><<<g, 256, 0, s>>>(
+                     static_cast<const float*>(x), row_of, static_cast<float*>(x_perm),
+                     c.T, c.d, c.k));
   }
   return MOE_OK;
 }

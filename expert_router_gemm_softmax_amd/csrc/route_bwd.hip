@@ -6,27 +6,33 @@
 //   dp[t, idx[t,j]] = dgate[t,j] for kept j;  dz = p * (dp - sum_e p dp)
 //   dX  = sum_{kept j} dXp[row_of[t,j]] + dz Wr^T
 //   dWr = x^T dz,  db = sum_t dz
-// dWr and db are reduced in fixed order (split over token chunks, then a
-// sequential sum over the chunks): bitwise deterministic.
-#include "common.h"
+// Both products run on the grouped GEMM kernels.  For bf16 storage dz is
+// split into bf16 high and low parts (dz = hi + lo to ~2^-16 relative), and
+// the products use [hi | lo] against Wr stacked twice, so the router
+// gradient keeps ~fp32 accuracy on bf16 MFMA.  dX is one row-GEMM whose
+// epilogue adds the unpermute-sum; dWr is a k-ragged GEMM over uniform
+// token chunks writing fp32 partials, summed in fixed order with db.
+#include "gemm.h"
 
 namespace moe {
-
-int launch_transpose_wr(const moe_cfg& c, const void* Wr, void* wrT, hipStream_t s);
-
 namespace {
 
-constexpr int kDxTok = 16;   // tokens per block in the dX kernel
-constexpr int kDwE = 64;     // experts per block in the dWr kernel
-constexpr int kDwChunk = 64; // tokens staged per LDS chunk in the dWr kernel
-
+// dz for kDzTokens tokens per block (one wave per token); writes dz (fp32
+// storage) or its bf16 hi/lo split (bf16 storage), and the block's partial
+// sums of dz for db.
+template <bool BF>
 __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
     const float* __restrict__ probs, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ row_of, const float* __restrict__ dgate,
-    float* __restrict__ dz, int64_t T_, int E, int k) {
-  const int lane = threadIdx.x & 63;
-  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T_;
-       t += (int64_t)gridDim.x * 4) {
+    float* __restrict__ dz, uint16_t* __restrict__ dzb, float* __restrict__ db_part,
+    int64_t T_, int E, int Ep, int k) {
+  __shared__ float sdb[4][256];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float dbacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int64_t t0 = (int64_t)blockIdx.x * kDzTokens;
+  for (int tt = w; tt < kDzTokens; tt += 4) {
+    const int64_t t = t0 + tt;
+    if (t >= T_) break;
     float p[4], dp[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -49,146 +55,130 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      if (e < E) dz[t * E + e] = p[i] * (dp[i] - sp);
+      const float v = p[i] * (dp[i] - sp);  // 0 for padded experts
+      if (e < E) dbacc[i] += v;
+      if constexpr (BF) {
+        if (e < Ep) {
+          const uint16_t hi = f2bf(v);
+          dzb[t * 2 * Ep + e] = hi;
+          dzb[t * 2 * Ep + Ep + e] = f2bf(v - bf2f(hi));
+        }
+      } else {
+        if (e < E) dz[t * E + e] = v;
+      }
     }
   }
-}
-
-// dX[t][i] = sum_j dXp[row][i] + sum_e dz[t][e] wrT[e][i]
-template <typename T>
-__global__ __launch_bounds__(256) void route_bwd_dx_kernel(
-    const float* __restrict__ dz, const T* __restrict__ wrT, const T* __restrict__ dXp,
-    const int32_t* __restrict__ row_of, T* __restrict__ dX, int64_t T_, int d, int E,
-    int k) {
-  extern __shared__ float sdz[];  // [kDxTok][E]
-  int32_t* srow = reinterpret_cast<int32_t*>(sdz + kDxTok * E);  // [kDxTok][k]
-  const int64_t t0 = (int64_t)blockIdx.x * kDxTok;
-  for (int o = threadIdx.x; o < kDxTok * E; o += 256) {
-    const int tt = o / E;
-    sdz[o] = t0 + tt < T_ ? dz[t0 * E + o] : 0.0f;
-  }
-  for (int o = threadIdx.x; o < kDxTok * k; o += 256) {
-    const int tt = o / k;
-    srow[o] = t0 + tt < T_ ? row_of[t0 * k + o] : -1;
-  }
+  // fixed-order block reduction of the per-wave partial sums
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sdb[w][lane + 64 * i] = dbacc[i];
   __syncthreads();
-  for (int i = threadIdx.x; i < d; i += 256) {
-    float acc[kDxTok];
-#pragma unroll
-    for (int tt = 0; tt < kDxTok; ++tt) acc[tt] = 0.0f;
-    for (int e = 0; e < E; ++e) {
-      const float w = St<T>::to_f(wrT[(int64_t)e * d + i]);
-#pragma unroll
-      for (int tt = 0; tt < kDxTok; ++tt) acc[tt] += sdz[tt * E + e] * w;
-    }
-#pragma unroll
-    for (int tt = 0; tt < kDxTok; ++tt) {
-      const int64_t t = t0 + tt;
-      if (t >= T_) break;
-      float sum = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        const int32_t r = srow[tt * k + j];
-        if (r >= 0) sum += St<T>::to_f(dXp[(int64_t)r * d + i]);
-      }
-      dX[t * d + i] = St<T>::from_f(sum + acc[tt]);
-    }
+  for (int e = threadIdx.x; e < E; e += 256)
+    db_part[(int64_t)blockIdx.x * E + e] = (sdb[0][e] + sdb[1][e]) + (sdb[2][e] + sdb[3][e]);
+}
+
+// wrp[i][e] = wrp[i][Ep + e] = Wr[i][e] (zero for E <= e < Ep)
+__global__ void stack_wr_kernel(const uint16_t* __restrict__ Wr, uint16_t* __restrict__ wrp,
+                                int d, int E, int Ep) {
+  const int64_t n = (int64_t)d * 2 * Ep;
+  for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < n;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(o / (2 * Ep));
+    int e = (int)(o - (int64_t)i * 2 * Ep);
+    if (e >= Ep) e -= Ep;
+    wrp[o] = e < E ? Wr[(int64_t)i * E + e] : (uint16_t)0;
   }
 }
 
-// partial[sp][i][e] = sum_{t in split sp} x[t][i] dz[t][e];
-// dbp[sp][e] = sum_{t in split sp} dz[t][e]
-template <typename T>
-__global__ __launch_bounds__(256) void route_bwd_dw_kernel(
-    const T* __restrict__ x, const float* __restrict__ dz, float* __restrict__ part,
-    float* __restrict__ dbp, int64_t T_, int d, int E) {
-  __shared__ float sdz[kDwChunk][kDwE];
-  const int sp = blockIdx.x;
-  const int i = blockIdx.y * 256 + threadIdx.x;
-  const int e0 = blockIdx.z * kDwE;
-  const int ne = min(kDwE, E - e0);
-  const int64_t tbeg = (int64_t)sp * kDwrRows;
-  const int64_t tend = min<int64_t>(tbeg + kDwrRows, T_);
-  float acc[kDwE];
-#pragma unroll
-  for (int q = 0; q < kDwE; ++q) acc[q] = 0.0f;
-  float dbacc = 0.0f;
-  for (int64_t tc = tbeg; tc < tend; tc += kDwChunk) {
-    const int nt = (int)min<int64_t>(kDwChunk, tend - tc);
-    for (int o = threadIdx.x; o < kDwChunk * kDwE; o += 256) {
-      const int tt = o / kDwE, q = o % kDwE;
-      sdz[tt][q] = (tt < nt && q < ne) ? dz[(tc + tt) * E + e0 + q] : 0.0f;
-    }
-    __syncthreads();
-    if (i < d) {
-      for (int tt = 0; tt < nt; ++tt) {
-        const float xv = St<T>::to_f(x[(tc + tt) * d + i]);
-#pragma unroll
-        for (int q = 0; q < kDwE; ++q) acc[q] += xv * sdz[tt][q];
-      }
-    }
-    if (blockIdx.y == 0 && threadIdx.x < ne)
-      for (int tt = 0; tt < nt; ++tt) dbacc += sdz[tt][threadIdx.x];
-    __syncthreads();
-  }
-  if (i < d) {
-    float* o = part + ((int64_t)sp * d + i) * E + e0;
-#pragma unroll
-    for (int q = 0; q < kDwE; ++q)
-      if (q < ne) o[q] = acc[q];
-  }
-  if (blockIdx.y == 0 && threadIdx.x < ne) dbp[(int64_t)sp * E + e0 + threadIdx.x] = dbacc;
-}
-
+// dWr[i][e] = sum over chunks (fixed order) of part[c][i][e] (+ the low half)
+// and db[e] = sum over blocks of db_part[b][e]
 template <typename T>
 __global__ __launch_bounds__(256) void route_bwd_reduce_kernel(
-    const float* __restrict__ part, const float* __restrict__ dbp, T* __restrict__ dWr,
-    float* __restrict__ db, int nsplit, int d, int E) {
+    const float* __restrict__ part, const float* __restrict__ db_part, T* __restrict__ dWr,
+    float* __restrict__ db, int nchunks, int nblk_dz, int d, int E, int Nw, int Ep) {
   const int64_t n = (int64_t)d * E;
   for (int64_t o = blockIdx.x * 256 + threadIdx.x; o < n; o += (int64_t)gridDim.x * 256) {
+    const int64_t i = o / E;
+    const int e = (int)(o - i * E);
     float s = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) s += part[(int64_t)sp * n + o];
+    for (int c = 0; c < nchunks; ++c) {
+      const float* pc = part + ((int64_t)c * d + i) * Nw;
+      s += pc[e];
+      if (Nw != E) s += pc[Ep + e];
+    }
     dWr[o] = St<T>::from_f(s);
   }
   if (blockIdx.x == 0 && db != nullptr)
     for (int e = threadIdx.x; e < E; e += 256) {
       float s = 0.0f;
-      for (int sp = 0; sp < nsplit; ++sp) s += dbp[(int64_t)sp * E + e];
+      for (int b = 0; b < nblk_dz; ++b) s += db_part[(int64_t)b * E + e];
       db[e] = s;
     }
 }
 
 template <typename T>
 int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
-                const int32_t* idx, const int32_t* row_of, const float* dgate,
-                const T* dXp, T* dX, T* dWr, float* db, void* ws, hipStream_t s) {
+                const int32_t* idx, const int32_t* row_of, const float* dgate, const T* dXp,
+                T* dX, T* dWr, float* db, void* ws, hipStream_t s) {
+  constexpr bool BF = sizeof(T) == 2;
   const WsLayout L = ws_layout(c);
+  const int Ep = bwd_ep(c.E);
   float* dz = ws_ptr<float>(ws, L.dz);
-  T* wrT = ws_ptr<T>(ws, L.wrT);
+  uint16_t* dzb = ws_ptr<uint16_t>(ws, L.dzb);
+  uint16_t* wrp = ws_ptr<uint16_t>(ws, L.wrp);
   float* part = ws_ptr<float>(ws, L.dwr_part);
   float* dbp = ws_ptr<float>(ws, L.db_part);
-  int rc = launch_transpose_wr(c, Wr, wrT, s);
-  if (rc != MOE_OK) return rc;
-  if (c.T > 0) {
-    const int g1 = (int)std::min<int64_t>(ceil_div(c.T, 4), 65536);
+  const int nblk = c.T > 0 ? (int)ceil_div(c.T, kDzTokens) : 0;
+  if (nblk > 0)
     MOE_LAUNCH(MOE_KERNEL_ROUTE_BWD_DZ, s,
-               route_bwd_dz_kernel<<<g1, 256, 0, s>>>(probs, idx, row_of, dgate, dz, c.T,
-                                                      c.E, c.k));
-    const int g2 = (int)ceil_div(c.T, kDxTok);
-    const size_t sm2 = (size_t)kDxTok * c.E * 4 + (size_t)kDxTok * c.k * 4;
-    MOE_LAUNCH(MOE_KERNEL_ROUTE_BWD_DX, s,
-               route_bwd_dx_kernel<T><<<g2, 256, sm2, s>>>(dz, wrT, dXp, row_of, dX, c.T,
-                                                          c.d, c.E, c.k));
+               route_bwd_dz_kernel<BF><<<nblk, 256, 0, s>>>(probs, idx, row_of, dgate, dz,
+                                                           dzb, dbp, c.T, c.E, Ep, c.k));
+  if constexpr (BF) {
+    const int64_t n = (int64_t)c.d * 2 * Ep;
+    MOE_LAUNCH(MOE_KERNEL_ROUTE_PREP, s,
+               stack_wr_kernel<<<(int)std::min<int64_t>(ceil_div(n, 256), 4096), 256, 0, s>>>(
+                   reinterpret_cast<const uint16_t*>(Wr), wrp, c.d, c.E, Ep));
   }
-  const int nsplit = c.T > 0 ? (int)ceil_div(c.T, kDwrRows) : 0;
-  if (nsplit > 0) {
-    dim3 g3(nsplit, (unsigned)ceil_div(c.d, 256), (unsigned)ceil_div(c.E, kDwE));
-    MOE_LAUNCH(MOE_KERNEL_ROUTE_BWD_DW, s,
-               route_bwd_dw_kernel<T><<<g3, 256, 0, s>>>(x, dz, part, dbp, c.T, c.d, c.E));
+  int rc;
+  if (c.T > 0) {
+    // dX = [dz_hi | dz_lo] [Wr | Wr]^T + unpermute-sum of dXp
+    GemmArgs g{};
+    g.E = 1;
+    g.M = (int)c.T;
+    g.N = c.d;
+    g.K = BF ? 2 * Ep : c.E;
+    g.A = BF ? static_cast<const void*>(dzb) : static_cast<const void*>(dz);
+    g.lda = g.K;
+    g.B = BF ? static_cast<const void*>(wrp) : static_cast<const void*>(Wr);
+    g.ldb = g.K;
+    g.C = dX;
+    g.ldc = c.d;
+    g.Aux = dXp;
+    g.aux_idx = row_of;
+    g.aux_k = c.k;
+    rc = launch_gemm(MOE_KERNEL_ROUTE_BWD_DX, MODE_ROW, true, EPI_UNPERM, c, g, s);
+    if (rc != MOE_OK) return rc;
+    // dWr partials = x^T [dz_hi | dz_lo] over uniform token chunks
+    GemmArgs h{};
+    h.E = L.dwr_chunks;
+    h.chunk = L.dwr_chunk;
+    h.K = (int)c.T;
+    h.M = c.d;
+    h.N = L.dwr_n;
+    h.A = x;
+    h.lda = c.d;
+    h.B = BF ? static_cast<const void*>(dzb) : static_cast<const void*>(dz);
+    h.ldb = L.dwr_n;
+    h.C = part;
+    h.ldc = L.dwr_n;
+    h.c_estride = (int64_t)c.d * L.dwr_n;
+    rc = launch_gemm(MOE_KERNEL_ROUTE_BWD_DW, MODE_KRAG, false, EPI_F32, c, h, s);
+    if (rc != MOE_OK) return rc;
   }
+  const int nch = c.T > 0 ? L.dwr_chunks : 0;
   const int g4 = (int)std::min<int64_t>(ceil_div((int64_t)c.d * c.E, 256), 4096);
   MOE_LAUNCH(MOE_KERNEL_ROUTE_BWD_DW, s,
-             route_bwd_reduce_kernel<T><<<g4, 256, 0, s>>>(part, dbp, dWr, db, nsplit, c.d,
-                                                          c.E));
+             route_bwd_reduce_kernel<T><<<g4, 256, 0, s>>>(part, dbp, dWr, db, nch, nblk,
+                                                          c.d, c.E, L.dwr_n, Ep));
   return MOE_OK;
 }
 

@@ -96,6 +96,10 @@ const char* moe_status_str(int status);
 /* Validates cfg alone (the checks every entry point starts with). */
 int moe_check_cfg(const moe_cfg* cfg);
 
+/* Text naming the kernel and HIP error of this thread's last
+ * MOE_ERR_LAUNCH ("" if none since the last entry-point call). */
+const char* moe_last_error(void);
+
 /* ---------------------------------------------------------------- forward */
 
 /* F1 router: every token gets a score per expert ("The step timeline");
@@ -275,8 +279,9 @@ typedef enum {
   MOE_KERNEL_ROUTE_BWD_DX = 14,
   MOE_KERNEL_ROUTE_BWD_DW = 15,
   MOE_KERNEL_SCHEDULE = 16,
-  MOE_KERNEL_ROUTE_PREP = 17,    /* router weight transpose */
-  MOE_KERNEL_COUNT_ = 18
+  MOE_KERNEL_ROUTE_PREP = 17,    /* router weight transpose / stacking */
+  MOE_KERNEL_PERMUTE_COPY = 18,  /* x -> x_perm row copy */
+  MOE_KERNEL_COUNT_ = 19
 } moe_kernel_id;
 
 int moe_prof_arm(int kernel_id, int max_launches);

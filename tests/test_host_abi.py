@@ -149,3 +149,18 @@ def test_workload_shapes_are_the_named_configs():
     assert (W.get("C1").T, W.get("C1").d, W.get("C1").E, W.get("C1").k, W.get("C1").f) == \
         (4096, 1024, 8, 2, 4096)
     assert W.get("C4").cf == 1.0 and W.get("C2").cf is None
+
+
+def test_one_hip_runtime_in_the_process(repo_root):
+    """libmoe.so must share torch's HIP runtime (pointers and streams come
+    from it), whatever the import order."""
+    import subprocess
+    import sys
+    for order in ("import expert_router_gemm_softmax_amd, torch",
+                  "import torch, expert_router_gemm_softmax_amd"):
+        code = order + ("; print(len({l.split()[-1] for l in open('/proc/self/maps') "
+                        "if 'libamdhip64' in l}))")
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                           cwd=repo_root, timeout=300)
+        assert r.returncode == 0, r.stderr[-500:]
+        assert r.stdout.strip() == "1", (order, r.stdout)
