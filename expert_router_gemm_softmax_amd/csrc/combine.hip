@@ -8,39 +8,85 @@
 namespace moe {
 namespace {
 
-constexpr int kCW = 4;  // waves per block
+constexpr int kCW = 4;   // waves per block
+constexpr int kCPL = 8;  // 16-byte chunks per lane in one pass over a row
 
-// out[t] = sum over kept j (ascending) of gate[t,j] * Y[row_of[t,j]]
+// Loads the chunks of one pass (chunk c = g0 + s*64 + lane) of row r of src
+// into v; chunks past the row end, and every chunk of a dropped row
+// (r < 0), are not loaded.
 template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(
-    const T* __restrict__ Y, const int32_t* __restrict__ row_of,
-    const float* __restrict__ gate, T* __restrict__ out, int64_t T_, int d, int k) {
+__device__ __forceinline__ void load_pass(const T* __restrict__ src, int64_t r, int d, int g0,
+                                          int nch, int lane, u32x4 (&v)[kCPL]) {
+  constexpr int V = St<T>::kVec;
+  if (r < 0) return;
+#pragma unroll
+  for (int s = 0; s < kCPL; ++s) {
+    const int c = g0 + s * kWave + lane;
+    if (c < nch) v[s] = ld16(src + r * d + c * V);
+  }
+}
+
+// out[t] = sum over kept j (ascending) of g_j * src[row_of[t,j]], with
+// g_j = gate[t,j] (combine) or 1 (gradient unpermute-sum, fp32 output).
+// One wave per token; two assignments' rows are in flight at once.
+template <typename T, typename OutT, bool GATED>
+__global__ __launch_bounds__(256) void gather_sum_kernel(
+    const T* __restrict__ src, const int32_t* __restrict__ row_of,
+    const float* __restrict__ gate, OutT* __restrict__ out, int64_t T_, int d, int k) {
   constexpr int V = St<T>::kVec;
   const int lane = threadIdx.x & 63;
   const int nch = d / V;
   for (int64_t t = (int64_t)blockIdx.x * kCW + (threadIdx.x >> 6); t < T_;
        t += (int64_t)gridDim.x * kCW) {
     const int32_t* rows = row_of + t * k;
-    const float* gt = gate + t * k;
-    for (int c = lane; c < nch; c += kWave) {
-      float acc[V];
+    for (int g0 = 0; g0 < nch; g0 += kWave * kCPL) {
+      float acc[kCPL][V];
 #pragma unroll
-      for (int q = 0; q < V; ++q) acc[q] = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        const int32_t r = rows[j];
-        if (r < 0) continue;
-        const float gj = gt[j];
-        float y[V];
-        St<T>::unpack(ld16(Y + (int64_t)r * d + c * V), y);
+      for (int s = 0; s < kCPL; ++s)
 #pragma unroll
-        for (int q = 0; q < V; ++q) acc[q] += gj * y[q];
+        for (int q = 0; q < V; ++q) acc[s][q] = 0.0f;
+      for (int j = 0; j < k; j += 2) {
+        const int32_t r0 = rows[j];
+        const int32_t r1 = j + 1 < k ? rows[j + 1] : -1;
+        u32x4 y0[kCPL], y1[kCPL];
+        load_pass(src, r0, d, g0, nch, lane, y0);
+        load_pass(src, r1, d, g0, nch, lane, y1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int32_t r = h ? r1 : r0;
+          if (r < 0) continue;
+          const float g = GATED ? gate[t * k + j + h] : 1.0f;
+#pragma unroll
+          for (int s = 0; s < kCPL; ++s) {
+            if (g0 + s * kWave + lane >= nch) continue;
+            float y[V];
+            St<T>::unpack(h ? y1[s] : y0[s], y);
+#pragma unroll
+            for (int q = 0; q < V; ++q) acc[s][q] += g * y[q];
+          }
+        }
       }
-      st16(out + t * d + c * V, St<T>::pack(acc));
+#pragma unroll
+      for (int s = 0; s < kCPL; ++s) {
+        const int c = g0 + s * kWave + lane;
+        if (c >= nch) continue;
+        if constexpr (sizeof(OutT) == sizeof(T)) {
+          st16(out + t * d + c * V, St<T>::pack(acc[s]));
+        } else {
+          float* o = reinterpret_cast<float*>(out) + t * d + c * V;
+#pragma unroll
+          for (int q = 0; q < V; q += 4)
+            st16(o + q, u32x4{__float_as_uint(acc[s][q]), __float_as_uint(acc[s][q + 1]),
+                              __float_as_uint(acc[s][q + 2]), __float_as_uint(acc[s][q + 3])});
+        }
+      }
     }
   }
 }
 
-// dYp[row] = gate * dOut[t];  dgate[t,j] = <dOut[t], Y[row]> (0 if dropped)
+// dYp[row] = gate * dOut[t];  dgate[t,j] = <dOut[t], Y[row]> (0 if dropped).
+// One wave per token: each pass holds dOut's chunks in registers while the
+// k rows of Y stream past, two at a time; lane j keeps dgate[t,j].
 template <typename T>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const T* __restrict__ dOut, const T* __restrict__ Y, const int32_t* __restrict__ row_of,
@@ -51,59 +97,43 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   const int nch = d / V;
   for (int64_t t = (int64_t)blockIdx.x * kCW + (threadIdx.x >> 6); t < T_;
        t += (int64_t)gridDim.x * kCW) {
-    for (int j = 0; j < k; ++j) {
-      const int32_t r = row_of[t * k + j];
-      if (r < 0) {
-        if (lane == 0) dgate[t * k + j] = 0.0f;
-        continue;
-      }
-      const float gj = gate[t * k + j];
-      float part = 0.0f;
-      for (int c = lane; c < nch; c += kWave) {
-        float g[V], y[V], o[V];
-        St<T>::unpack(ld16(dOut + t * d + c * V), g);
-        St<T>::unpack(ld16(Y + (int64_t)r * d + c * V), y);
+    const int32_t* rows = row_of + t * k;
+    float mine = 0.0f;  // lane j < k: dgate[t, j]
+    for (int g0 = 0; g0 < nch; g0 += kWave * kCPL) {
+      u32x4 gv[kCPL];
+      load_pass(dOut, t, d, g0, nch, lane, gv);
+      for (int j = 0; j < k; j += 2) {
+        const int32_t r0 = rows[j];
+        const int32_t r1 = j + 1 < k ? rows[j + 1] : -1;
+        u32x4 y0[kCPL], y1[kCPL];
+        load_pass(Y, r0, d, g0, nch, lane, y0);
+        load_pass(Y, r1, d, g0, nch, lane, y1);
 #pragma unroll
-        for (int q = 0; q < V; ++q) {
-          part += g[q] * y[q];
-          o[q] = gj * g[q];
+        for (int h = 0; h < 2; ++h) {
+          const int32_t r = h ? r1 : r0;
+          if (r < 0) continue;  // uniform over the wave
+          const float gj = gate[t * k + j + h];
+          float pp = 0.0f;
+#pragma unroll
+          for (int s = 0; s < kCPL; ++s) {
+            const int c = g0 + s * kWave + lane;
+            if (c >= nch) continue;
+            float g[V], y[V], o[V];
+            St<T>::unpack(gv[s], g);
+            St<T>::unpack(h ? y1[s] : y0[s], y);
+#pragma unroll
+            for (int q = 0; q < V; ++q) {
+              pp += g[q] * y[q];
+              o[q] = gj * g[q];
+            }
+            st16(dYp + (int64_t)r * d + c * V, St<T>::pack(o));
+          }
+          pp = wave_sum(pp);
+          if (lane == j + h) mine += pp;
         }
-        st16(dYp + (int64_t)r * d + c * V, St<T>::pack(o));
       }
-      part = wave_sum(part);
-      if (lane == 0) dgate[t * k + j] = part;
     }
-  }
-}
-
-// dXe[t] = sum over kept j of dXp[row_of[t,j]]  (float output)
-template <typename T>
-__global__ __launch_bounds__(256) void unpermute_bwd_kernel(
-    const T* __restrict__ dXp, const int32_t* __restrict__ row_of, float* __restrict__ dXe,
-    int64_t T_, int d, int k) {
-  constexpr int V = St<T>::kVec;
-  const int lane = threadIdx.x & 63;
-  const int nch = d / V;
-  for (int64_t t = (int64_t)blockIdx.x * kCW + (threadIdx.x >> 6); t < T_;
-       t += (int64_t)gridDim.x * kCW) {
-    for (int c = lane; c < nch; c += kWave) {
-      float acc[V];
-#pragma unroll
-      for (int q = 0; q < V; ++q) acc[q] = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        const int32_t r = row_of[t * k + j];
-        if (r < 0) continue;
-        float v[V];
-        St<T>::unpack(ld16(dXp + (int64_t)r * d + c * V), v);
-#pragma unroll
-        for (int q = 0; q < V; ++q) acc[q] += v[q];
-      }
-      float* o = dXe + t * d + c * V;
-#pragma unroll
-      for (int q = 0; q < V; q += 4)
-        st16(o + q, u32x4{__float_as_uint(acc[q]), __float_as_uint(acc[q + 1]),
-                          __float_as_uint(acc[q + 2]), __float_as_uint(acc[q + 3])});
-    }
+    if (lane < k) dgate[t * k + lane] = rows[lane] >= 0 ? mine : 0.0f;
   }
 }
 
@@ -120,12 +150,12 @@ int launch_combine(const moe_cfg& c, const void* Y, const int32_t* row_of,
   const int grid = token_grid(c.T);
   if (c.dtype == MOE_BF16)
     MOE_LAUNCH(MOE_KERNEL_COMBINE, s,
-               combine_kernel<uint16_t><<<grid, 256, 0, s>>>(
+               gather_sum_kernel<uint16_t, uint16_t, true><<<grid, 256, 0, s>>>(
                    static_cast<const uint16_t*>(Y), row_of, gate,
                    static_cast<uint16_t*>(out), c.T, c.d, c.k));
   else
     MOE_LAUNCH(MOE_KERNEL_COMBINE, s,
-               combine_kernel<float><<<grid, 256, 0, s>>>(
+               gather_sum_kernel<float, float, true><<<grid, 256, 0, s>>>(
                    static_cast<const float*>(Y), row_of, gate, static_cast<float*>(out),
                    c.T, c.d, c.k));
   return MOE_OK;
@@ -150,17 +180,17 @@ int launch_combine_bwd(const moe_cfg& c, const void* dOut, const void* Y,
 }
 
 int launch_unpermute_bwd(const moe_cfg& c, const void* dXp, const int32_t* row_of,
-                         float* dXe, hipStream_t s) {
+                         float* dXe, hipStream_t s, int kernel_id) {
   if (c.T == 0) return MOE_OK;
   const int grid = token_grid(c.T);
   if (c.dtype == MOE_BF16)
-    MOE_LAUNCH(MOE_KERNEL_UNPERMUTE_BWD, s,
-               unpermute_bwd_kernel<uint16_t><<<grid, 256, 0, s>>>(
-                   static_cast<const uint16_t*>(dXp), row_of, dXe, c.T, c.d, c.k));
+    MOE_LAUNCH(kernel_id, s,
+               gather_sum_kernel<uint16_t, float, false><<<grid, 256, 0, s>>>(
+                   static_cast<const uint16_t*>(dXp), row_of, nullptr, dXe, c.T, c.d, c.k));
   else
-    MOE_LAUNCH(MOE_KERNEL_UNPERMUTE_BWD, s,
-               unpermute_bwd_kernel<float><<<grid, 256, 0, s>>>(
-                   static_cast<const float*>(dXp), row_of, dXe, c.T, c.d, c.k));
+    MOE_LAUNCH(kernel_id, s,
+               gather_sum_kernel<float, float, false><<<grid, 256, 0, s>>>(
+                   static_cast<const float*>(dXp), row_of, nullptr, dXe, c.T, c.d, c.k));
   return MOE_OK;
 }
 

@@ -117,8 +117,9 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 //   db_part  [nblk_dz, E] f32   per-block partial sums of dz
 //   dgate    [T, k] f32         combine-backward gate gradient
 //   dYp, dA, dXp                backward row gradients (Rmax rows, s)
+//   dxe      [T, d] f32         unpermute-sum of dXp (router backward)
 struct WsLayout {
-  size_t wrT, perm_blk, tiles, dz, dzb, wrp, dwr_part, db_part, dgate, dYp, dA, dXp, total;
+  size_t wrT, perm_blk, tiles, dz, dzb, wrp, dwr_part, db_part, dgate, dYp, dA, dXp, dxe, total;
   int nblk_perm;
   int nblk_dz;
   int dwr_chunks, dwr_chunk, dwr_n;
@@ -180,6 +181,7 @@ inline WsLayout ws_layout(const moe_cfg& c) {
   L.dYp = take((size_t)Rmax * c.d * s);
   L.dA = take((size_t)Rmax * c.f * s);
   L.dXp = take((size_t)Rmax * c.d * s);
+  L.dxe = take((size_t)c.T * c.d * 4);
   L.total = off;
   return L;
 }
@@ -228,7 +230,7 @@ int launch_combine_bwd(const moe_cfg& c, const void* dOut, const void* Y,
                        const int32_t* row_of, const float* gate, void* dYp,
                        float* dgate, hipStream_t s);
 int launch_unpermute_bwd(const moe_cfg& c, const void* dXp, const int32_t* row_of,
-                         float* dXe, hipStream_t s);
+                         float* dXe, hipStream_t s, int kernel_id = MOE_KERNEL_UNPERMUTE_BWD);
 int launch_route_bwd(const moe_cfg& c, const void* x, const void* Wr,
                      const float* probs, const int32_t* idx, const int32_t* row_of,
                      const float* dgate, const void* dXp, void* dX, void* dWr,

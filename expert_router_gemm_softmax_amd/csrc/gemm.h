@@ -10,20 +10,19 @@ namespace moe {
 //   KRAG C_g[M, N]  = A_g^T B_g over the rows of group g (ragged K)
 enum { MODE_ROW = 0, MODE_KRAG = 1 };
 // Epilogues: store s; A and H = gelu(A); dA = acc * gelu'(Aux); store fp32;
-// C[t] = acc + sum over kept j of Aux[aux_idx[t*aux_k + j]] (unpermute-sum)
-enum { EPI_STORE = 0, EPI_GELU = 1, EPI_DGELU = 2, EPI_F32 = 3, EPI_UNPERM = 4 };
+// C = RN_s(acc + Aux) with Aux fp32 laid out like C
+enum { EPI_STORE = 0, EPI_GELU = 1, EPI_DGELU = 2, EPI_F32 = 3, EPI_ADDF32 = 4 };
 
 struct GemmArgs {
   const void* A;
   const void* B;
   void* C;
   void* C2;              // EPI_GELU: H = gelu(A_out)
-  const void* Aux;       // EPI_DGELU: forward pre-activation, laid out like C
+  const void* Aux;       // EPI_DGELU: forward pre-activation (s); EPI_ADDF32:
+                         // fp32 addend; both laid out like C
   const int32_t* offsets;  // group g = rows [offsets[g], offsets[g+1]); nullptr:
                            // KRAG uniform groups of `chunk` rows, ROW one group
                            // of M rows
-  const int32_t* aux_idx;  // EPI_UNPERM: row_of [rows][aux_k]
-  int aux_k;
   const int32_t* tiles;    // ROW: prefix of M tiles per expert, [E+1]
   int E;                 // number of groups
   int M, N, K;           // ROW: N, K (and M for one group); KRAG: M, N, and

@@ -311,16 +311,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
           for (int q = 0; q < 8; ++q) a8[q] = gelu_tanh(a8[q]);
           st16(static_cast<uint16_t*>(g.C2) + o, St<uint16_t>::pack(a8));
-        } else if constexpr (EPI == EPI_UNPERM) {
-          const int32_t* ro = g.aux_idx + (t.row0 + row) * (int64_t)g.aux_k;
-          for (int jj = 0; jj < g.aux_k; ++jj) {
-            const int32_t rr = ro[jj];
-            if (rr < 0) continue;
-            float x8[8];
-            St<uint16_t>::unpack(
-                ld16(static_cast<const uint16_t*>(g.Aux) + (int64_t)rr * g.ldc + col), x8);
+        } else if constexpr (EPI == EPI_ADDF32) {
+          const float* ad = static_cast<const float*>(g.Aux) + o;
+          const f32x4 a0 = *reinterpret_cast<const f32x4*>(ad);
+          const f32x4 a1 = *reinterpret_cast<const f32x4*>(ad + 4);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v8[q] += x8[q];
+          for (int q = 0; q < 4; ++q) {
+            v8[q] += a0[q];
+            v8[q + 4] += a1[q];
           }
           st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
         } else {
@@ -408,13 +406,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       if (col >= g.N) continue;
       const int64_t o = cbase + (int64_t)row * g.ldc + col;
       if constexpr (EPI == EPI_STORE || EPI == EPI_F32) C[o] = acc[i][j];
-      else if constexpr (EPI == EPI_UNPERM) {
-        float sum = acc[i][j];
-        const int32_t* ro = g.aux_idx + (t.row0 + row) * (int64_t)g.aux_k;
-        for (int jj = 0; jj < g.aux_k; ++jj)
-          if (ro[jj] >= 0) sum += Aux[(int64_t)ro[jj] * g.ldc + col];
-        C[o] = sum;
-      }
+      else if constexpr (EPI == EPI_ADDF32) C[o] = acc[i][j] + Aux[o];
       else if constexpr (EPI == EPI_GELU) { C[o] = acc[i][j]; C2[o] = gelu_tanh(acc[i][j]); }
       else C[o] = acc[i][j] * gelu_tanh_grad(Aux[o]);
     }
@@ -435,8 +427,23 @@ __global__ void gemm_schedule_kernel(const int32_t* __restrict__ offsets,
   }
 }
 
-constexpr int kBM = 128, kBN = 128;  // bf16 block tile
 constexpr int kFM = 64, kFN = 64;    // fp32 block tile
+
+// bf16 block tile: 256 x 256 (4 waves of 128 x 128) when the problem has at
+// least one full round of such tiles for the chip, else 128 x 128.
+inline bool use_big_tile(const moe_cfg& c, int mode, int M, int N, int E) {
+  if (c.dtype != MOE_BF16) return false;
+  int64_t tiles;
+  if (mode == MODE_ROW) tiles = (ceil_div(rows_max(c), 256) + E) * ceil_div(N, 256);
+  else tiles = (int64_t)E * ceil_div(M, 256) * ceil_div(N, 256);
+  return tiles >= 256;
+}
+// M tile of the ROW GEMMs of a layer (the schedule is built for it)
+inline int row_bm(const moe_cfg& c) {
+  if (c.dtype != MOE_BF16) return kFM;
+  const int nmin = c.d < c.f ? c.d : c.f;
+  return use_big_tile(c, MODE_ROW, 0, nmin, c.E) ? 256 : 128;
+}
 
 inline int grid8(int64_t n) { return (int)((n + 7) / 8 * 8); }
 
@@ -448,7 +455,17 @@ inline int64_t row_mtiles_bound(const moe_cfg& c, int BM) {
 template <int MODE, bool B_KC, int EPI>
 int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
   const bool bf = c.dtype == MOE_BF16;
-  const int BM = bf ? kBM : kFM, BN = bf ? kBN : kFN;
+  int BM, BN;
+  if (!bf) {
+    BM = kFM;
+    BN = kFN;
+  } else if constexpr (MODE == MODE_ROW) {
+    // one-group problems choose freely; grouped ones follow the schedule
+    BM = g.offsets ? row_bm(c) : (use_big_tile(c, MODE_KRAG, g.M, g.N, 1) ? 256 : 128);
+    BN = BM;
+  } else {
+    BM = BN = use_big_tile(c, MODE_KRAG, g.M, g.N, g.E) ? 256 : 128;
+  }
   g.ntn = (int)ceil_div(g.N, BN);
   int64_t nblk;
   if constexpr (MODE == MODE_ROW) {
@@ -459,17 +476,18 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
   }
   if (nblk == 0) return MOE_OK;
   const int grid = grid8(nblk);
-  if (bf)
-    MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, kBM, kBN><<<grid, 256, 0, s>>>(g));
-  else
+  if (!bf)
     MOE_LAUNCH(kid, s, gemm_f32_kernel<MODE, B_KC, EPI><<<grid, 256, 0, s>>>(g));
+  else if (BM == 256)
+    MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 256, 256><<<grid, 256, 0, s>>>(g));
+  else
+    MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 128, 128><<<grid, 256, 0, s>>>(g));
   return MOE_OK;
 }
 
 int schedule(const moe_cfg& c, const int32_t* offsets, int32_t* tiles, hipStream_t s) {
-  const int BM = c.dtype == MOE_BF16 ? kBM : kFM;
   MOE_LAUNCH(MOE_KERNEL_SCHEDULE, s,
-             gemm_schedule_kernel<<<1, 64, 0, s>>>(offsets, tiles, c.E, BM));
+             gemm_schedule_kernel<<<1, 64, 0, s>>>(offsets, tiles, c.E, row_bm(c)));
   return MOE_OK;
 }
 
@@ -494,8 +512,8 @@ int launch_gemm(int kid, int mode, bool b_kc, int epi, const moe_cfg& c, GemmArg
     return run_gemm<MODE_KRAG, false, EPI_STORE>(kid, c, g, s);
   if (mode == MODE_KRAG && !b_kc && epi == EPI_F32)
     return run_gemm<MODE_KRAG, false, EPI_F32>(kid, c, g, s);
-  if (mode == MODE_ROW && b_kc && epi == EPI_UNPERM)
-    return run_gemm<MODE_ROW, true, EPI_UNPERM>(kid, c, g, s);
+  if (mode == MODE_ROW && b_kc && epi == EPI_ADDF32)
+    return run_gemm<MODE_ROW, true, EPI_ADDF32>(kid, c, g, s);
   return MOE_ERR_UNIMPLEMENTED;
 }
 

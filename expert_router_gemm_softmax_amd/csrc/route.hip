@@ -112,20 +112,19 @@ __device__ __forceinline__ void logits_mfma(const uint16_t* __restrict__ x,
     }
   };
 
-  load_a(0, a_cur);
-  load_b(0, b_nxt);
-  store_b(0, b_nxt);
-  __syncthreads();
-  for (int kc = 0; kc < nkc; ++kc) {
+  // Token rows stream two K chunks ahead of the MFMAs: three register sets
+  // with fixed roles (a rotating copy would wait on the loads in flight);
+  // the router weights go through the LDS double buffer one chunk ahead.
+  u32x4 a_2[4];
+  auto step = [&](int kc, u32x4 (&acur)[4], u32x4 (&afar)[4]) {
+    if (kc >= nkc) return;
     const int buf = kc & 1;
     const bool more = kc + 1 < nkc;
-    if (more) {
-      load_a(kc + 1, a_nxt);
-      load_b(kc + 1, b_nxt);
-    }
+    if (kc + 2 < nkc) load_a(kc + 2, afar);
+    if (more) load_b(kc + 1, b_nxt);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, a_cur[kk]);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, acur[kk]);
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const u32x4 bv = *reinterpret_cast<const u32x4*>(
@@ -136,8 +135,16 @@ __device__ __forceinline__ void logits_mfma(const uint16_t* __restrict__ x,
     }
     if (more) store_b(buf ^ 1, b_nxt);
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) a_cur[q] = a_nxt[q];
+  };
+  load_a(0, a_cur);
+  if (nkc > 1) load_a(1, a_nxt);
+  load_b(0, b_nxt);
+  store_b(0, b_nxt);
+  __syncthreads();
+  for (int kc = 0; kc < nkc; kc += 3) {
+    step(kc, a_cur, a_2);
+    step(kc + 1, a_nxt, a_cur);
+    step(kc + 2, a_2, a_nxt);
   }
   // D[i][j]: token i = 8*(v/4) + 4*h + v%4, expert j = n*32 + r
 #pragma unroll
@@ -256,11 +263,33 @@ __global__ __launch_bounds__(256) void route_kernel(
       while (um) {
         const int ee = base + __builtin_ctzll(um);
         um &= um - 1;
-        double acc = 0.0;
+        // fp64 dot product of the token row with the expert's weights:
+        // 16-byte vectors, every lane's loads issued before their use
+        constexpr int V = St<T>::kVec;
         const T* xr = x + t * (int64_t)d;
         const T* wr = wrT + (int64_t)ee * d;
-        for (int i = lane; i < d; i += 64)
-          acc += (double)St<T>::to_f(xr[i]) * (double)St<T>::to_f(wr[i]);
+        const int nch = d / V;
+        double acc = 0.0;
+        for (int c0 = lane; c0 < nch; c0 += 4 * 64) {
+          u32x4 xv[4], wv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = c0 + q * 64;
+            if (c < nch) {
+              xv[q] = ld16(xr + c * V);
+              wv[q] = ld16(wr + c * V);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (c0 + q * 64 >= nch) continue;
+            float xf[V], wf[V];
+            St<T>::unpack(xv[q], xf);
+            St<T>::unpack(wv[q], wf);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc += (double)xf[i] * (double)wf[i];
+          }
+        }
         acc = wave_sum_d(acc);
         if (lane == 0) {
           s_uz[nU] = (float)(acc + (double)(bias ? bias[ee] : 0.0f));

@@ -10,7 +10,8 @@
 // split into bf16 high and low parts (dz = hi + lo to ~2^-16 relative), and
 // the products use [hi | lo] against Wr stacked twice, so the router
 // gradient keeps ~fp32 accuracy on bf16 MFMA.  dX is one row-GEMM whose
-// epilogue adds the unpermute-sum; dWr is a k-ragged GEMM over uniform
+// epilogue adds the unpermute-sum (gathered beforehand into an fp32 row
+// buffer by a bandwidth-bound kernel); dWr is a k-ragged GEMM over uniform
 // token chunks writing fp32 partials, summed in fixed order with db.
 #include "gemm.h"
 
@@ -99,18 +100,35 @@ __global__ __launch_bounds__(256) void route_bwd_reduce_kernel(
   for (int64_t o = blockIdx.x * 256 + threadIdx.x; o < n; o += (int64_t)gridDim.x * 256) {
     const int64_t i = o / E;
     const int e = (int)(o - i * E);
+    // chunks in ascending order; 8 chunks' loads in flight per step
+    const float* p0 = part + i * Nw + e;
+    const int64_t cs = (int64_t)d * Nw;
+    const bool two = Nw != E;
     float s = 0.0f;
-    for (int c = 0; c < nchunks; ++c) {
-      const float* pc = part + ((int64_t)c * d + i) * Nw;
-      s += pc[e];
-      if (Nw != E) s += pc[Ep + e];
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      float hi8[8], lo8[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool ok = c0 + q < nchunks;
+        hi8[q] = ok ? p0[(c0 + q) * cs] : 0.0f;
+        lo8[q] = ok && two ? p0[(c0 + q) * cs + Ep] : 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += hi8[q] + lo8[q];
     }
     dWr[o] = St<T>::from_f(s);
   }
   if (blockIdx.x == 0 && db != nullptr)
     for (int e = threadIdx.x; e < E; e += 256) {
       float s = 0.0f;
-      for (int b = 0; b < nblk_dz; ++b) s += db_part[(int64_t)b * E + e];
+      for (int b0 = 0; b0 < nblk_dz; b0 += 8) {
+        float v8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          v8[q] = b0 + q < nblk_dz ? db_part[(int64_t)(b0 + q) * E + e] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s += v8[q];
+      }
       db[e] = s;
     }
 }
@@ -140,7 +158,10 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
   }
   int rc;
   if (c.T > 0) {
-    // dX = [dz_hi | dz_lo] [Wr | Wr]^T + unpermute-sum of dXp
+    // dX = [dz_hi | dz_lo] [Wr | Wr]^T + unpermute-sum of dXp (fp32)
+    float* dxe = ws_ptr<float>(ws, L.dxe);
+    rc = launch_unpermute_bwd(c, dXp, row_of, dxe, s, MOE_KERNEL_ROUTE_BWD_DX);
+    if (rc != MOE_OK) return rc;
     GemmArgs g{};
     g.E = 1;
     g.M = (int)c.T;
@@ -152,10 +173,8 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
     g.ldb = g.K;
     g.C = dX;
     g.ldc = c.d;
-    g.Aux = dXp;
-    g.aux_idx = row_of;
-    g.aux_k = c.k;
-    rc = launch_gemm(MOE_KERNEL_ROUTE_BWD_DX, MODE_ROW, true, EPI_UNPERM, c, g, s);
+    g.Aux = dxe;
+    rc = launch_gemm(MOE_KERNEL_ROUTE_BWD_DX, MODE_ROW, true, EPI_ADDF32, c, g, s);
     if (rc != MOE_OK) return rc;
     // dWr partials = x^T [dz_hi | dz_lo] over uniform token chunks
     GemmArgs h{};

@@ -14,16 +14,36 @@ TOL = {  # (rtol, atol), numpy allclose semantics |g - o| <= atol + rtol |o|
     "f32": (1e-5, 1e-5),
     "prob": (1e-5, 1e-6),      # probs / gates: fp32 quantities from near-equal logits
 }
-# Outputs that are sums over the token (row) axis -- dW1, dW2, dWr, db --
-# of products whose inputs were rounded to the storage type upstream: two
-# correct implementations that round at the same points still flip single
-# upstream roundings (fp32 vs fp64 accumulation before the rounding), and a
-# flipped input moves one summand by one unit of the storage type.  With n
-# summands of rms size a, the sum has rms ~ sqrt(n) a, while the flips move
-# it by ~ u sqrt(rho n) a <= u * rms(sum), u = 2^-8 (bf16) or 2^-23 (fp32),
-# rho = fraction of flipped summands.  So the absolute tolerance of these
-# outputs is max(atol, u * rms(oracle output)); rtol is unchanged.
-RED_UNIT = {"bf16": 2.0 ** -8, "f32": 2.0 ** -23}
+# Outputs that are sums over the token (row) axis -- dW1, dW2, dWr, db,
+# dgate -- of products whose operands were rounded to the storage type
+# upstream: two correct implementations that round at the same points still
+# flip single upstream roundings (fp32 vs fp64 accumulation before the
+# rounding), and a flipped operand moves its summand a_i b_i by at most one
+# unit in the last place, u |a_i b_i| (u = 2^-7 for bf16's 8 significant
+# bits, 2^-23 for fp32).  Independent flips of a fraction rho of the n
+# summands move the sum by ~u sqrt(rho) ||(a_i b_i)_i||_2, and a single flip
+# by at most u max_i |a_i b_i| <= u ||(a_i b_i)_i||_2.  The absolute
+# tolerance of such an output element is therefore
+#     max(atol, 2 u ||(a_i b_i)_i||_2),
+# with ||(a_i b_i)_i||_2 = sqrt((a*a)^T (b*b)) computed from the oracle's own
+# operands (factor 2: several flips).  When the summands are not at hand
+# the rms of the sum stands in for their norm (random-sign sums:
+# rms(sum) ~ ||(a_i b_i)||_2 for a typical element).
+RED_UNIT = {"bf16": 2.0 ** -7, "f32": 2.0 ** -23}
+
+
+def term_norm(a, b):
+    """sqrt((a*a)^T (b*b)): per output element, the 2-norm of the summands
+    of a^T b (a [n, M], b [n, N])."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.sqrt((a * a).T @ (b * b))
+
+
+def terms_tol(norm, dtype):
+    """(rtol, atol array) for a sum whose summand norms are `norm`."""
+    rtol, atol = TOL[dtype]
+    return rtol, np.maximum(atol, 2.0 * RED_UNIT[dtype] * np.asarray(norm, np.float64))
 
 
 def say(*a):
@@ -57,11 +77,29 @@ def cfg_of(M, w, route_margin=0.0):
 
 
 def red_tol(ref, dtype):
-    """(rtol, atol) for a sum over the token axis (see RED_UNIT)."""
+    """(rtol, atol) for a sum over the token axis whose summands are not at
+    hand: the rms of the oracle output stands in for the summand norm."""
     rtol, atol = TOL[dtype]
     ref = np.asarray(ref, np.float64)
-    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-    return rtol, max(atol, RED_UNIT[dtype] * rms)
+    if ref.size == 0:
+        return rtol, atol
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    return rtol, max(atol, 2.0 * RED_UNIT[dtype] * rms)
+
+
+def expert_grad_tols(fw, bw, dtype):
+    """Per-element tolerances of dW1 and dW2 from the oracle's operands:
+    dW1[e] = x_e^T dA_e, dW2[e] = H_e^T dYp_e over the expert's rows."""
+    off = fw["offsets"]
+    E = len(off) - 1
+    n1 = np.zeros(bw["dW1"].shape)
+    n2 = np.zeros(bw["dW2"].shape)
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            n1[e] = term_norm(fw["x_perm"][lo:hi], bw["dA"][lo:hi])
+            n2[e] = term_norm(fw["H"][lo:hi], bw["dYp"][lo:hi])
+    return terms_tol(n1, dtype), terms_tol(n2, dtype)
 
 
 def assert_close(name, got, ref, tol):
@@ -75,9 +113,10 @@ def assert_close(name, got, ref, tol):
     bad = err > atol + rtol * np.abs(ref)
     if bad.any():
         i = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(ref))), err.shape)
+        at = atol if np.ndim(atol) == 0 else np.broadcast_to(atol, err.shape)[i]
         raise AssertionError(
             f"{name}: {int(bad.sum())}/{bad.size} elements outside rtol={rtol} "
-            f"atol={atol}; worst at {i}: gpu={got[i]!r} oracle={ref[i]!r}")
+            f"atol={at}; worst at {i}: gpu={got[i]!r} oracle={ref[i]!r}")
 
 
 def run_layer(M, w, inp, route_margin=0.0, bwd=True):
@@ -139,8 +178,14 @@ def check_layer_full(res, fw, bw, w, check_bwd=True):
     assert_close("out", to_f64(res["out"]), fw["out"], tol)
     if check_bwd:
         assert_close("dX", to_f64(res["dX"]), bw["dX"], tol)
-        for key in ("dWr", "db", "dW1", "dW2"):
-            assert_close(key, to_f64(res[key]), bw[key], red_tol(bw[key], tol))
+        dz = bw["dz"]
+        x = fw["x"]
+        assert_close("dWr", to_f64(res["dWr"]), bw["dWr"], terms_tol(term_norm(x, dz), tol))
+        assert_close("db", to_f64(res["db"]), bw["db"],
+                     terms_tol(np.sqrt((dz * dz).sum(axis=0)), tol))
+        t1, t2 = expert_grad_tols(fw, bw, tol)
+        assert_close("dW1", to_f64(res["dW1"]), bw["dW1"], t1)
+        assert_close("dW2", to_f64(res["dW2"]), bw["dW2"], t2)
     return R
 
 
