@@ -113,83 +113,125 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, int* s_tiles, Til
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
-constexpr int BK = 64;
+// Main loop: a ring of kStages LDS stages of BK = 32.  Full K tiles travel
+// from HBM straight into LDS (global_load_lds_dwordx4: each lane's 16 bytes
+// land at M0 + 16 * lane), so each lane picks the global chunk that belongs
+// at its LDS slot; a stage is waited for with the vector-memory counter of
+// the loads issued after it.  Operands keep their HBM orientation in LDS:
+//   KC (K contiguous) tile [rows][32]: 16-byte chunk q of a row stored at
+//      chunk q ^ ((row >> 2) & 3); MFMA fragments are plain 16-byte reads.
+//   MN (M or N contiguous) tile [32][R]: chunk c of k-row k stored at chunk
+//      c ^ 4 (k & 3); fragments come from two ds_read_b64_tr_b16, which
+//      transpose 4 x 4 blocks of 16-bit elements across each 16-lane group.
+// Rows (KC) or column chunks (MN) past the tile's M or N edge are clamped
+// to the last valid one; they only feed outputs that are never stored.  A
+// final partial K tile goes through registers with zero fill.
+constexpr int BK = 32;
+constexpr int kStages = 4;
 
-// element offset of (row, 8-element chunk) in a K-contiguous [rows][64] tile
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+
+__device__ __forceinline__ int kc_off(int row, int q) {
+  return row * BK + ((q ^ ((row >> 2) & 3)) << 3);
+}
+template <int R>
+__device__ __forceinline__ int mn_off(int k, int m) {
+  return k * R + ((((m >> 3) ^ ((k & 3) << 2))) << 3) + (m & 7);
 }
 
-// K-contiguous operand: R tile rows, element (row, k) at base + row*ld + k
-template <int R>
-__device__ __forceinline__ void load_kc(const uint16_t* base, int ld, int row0, int rlim,
-                                        int k0, int klim, u32x4 (&reg)[R / 32]) {
+// One operand tile of R rows (M or N extent) per stage.
+template <bool KC, int R>
+struct Operand {
+  static_assert(KC || R >= 128, "MN swizzle needs at least 16 chunks per k-row");
+  static constexpr int kChunks = R * BK / 8;      // 16-byte chunks per stage
+  static constexpr int kLoads = kChunks / 256;    // 1 KB wave loads per wave
+  static constexpr int kElems = R * BK;
+  const uint16_t* base;
+  int64_t src[kLoads];  // element offsets of this lane's chunks, K tile 0
+  int64_t kstep;        // element offset of one K tile
+  int ld, mn0, lim;
+
+  __device__ __forceinline__ void init(const uint16_t* b, int ld_, int mn0_, int lim_, int w,
+                                       int lane) {
+    base = b;
+    ld = ld_;
+    mn0 = mn0_;
+    lim = lim_;
 #pragma unroll
-  for (int i = 0; i < R / 32; ++i) {
-    const int c = threadIdx.x + i * 256;
-    const int row = c >> 3, q = c & 7;
-    const int gr = row0 + row, gk = k0 + q * 8;
-    reg[i] = (gr < rlim && gk < klim) ? ld16(base + (int64_t)gr * ld + gk)
-                                      : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < kLoads; ++j) {
+      const int p = (w * kLoads + j) * kWave + lane;  // physical chunk of the stage
+      if constexpr (KC) {
+        const int row = p >> 2, q = (p & 3) ^ ((row >> 2) & 3);
+        src[j] = (int64_t)min(mn0 + row, lim - 1) * ld + q * 8;
+      } else {
+        const int k = p / (R / 8), c = (p % (R / 8)) ^ ((k & 3) << 2);
+        src[j] = (int64_t)k * ld + min(mn0 + c * 8, lim - 8);
+      }
+    }
+    kstep = KC ? (int64_t)BK : (int64_t)BK * ld;
   }
-}
-template <int R>
-__device__ __forceinline__ void store_kc(uint16_t* s, const u32x4 (&reg)[R / 32]) {
+  // direct HBM -> LDS copy of K tile kt into the stage at LDS byte address lds
+  __device__ __forceinline__ void issue(int kt, uint32_t lds, uint32_t wslot) const {
 #pragma unroll
-  for (int i = 0; i < R / 32; ++i) {
-    const int c = threadIdx.x + i * 256;
-    const int row = c >> 3, q = c & 7;
-    *reinterpret_cast<u32x4*>(s + swz(row, q)) = reg[i];
-  }
-}
-// MN-contiguous operand: element (k, mn) at base + k*ld + mn.  Unit = 4 K
-// rows x 8 MN columns, transposed into 8 LDS rows of 4 K values.
-template <int R>
-__device__ __forceinline__ void load_mnc(const uint16_t* base, int ld, int mn0, int mnlim,
-                                         int k0, int klim, u32x4 (&reg)[R / 128][4]) {
-#pragma unroll
-  for (int i = 0; i < R / 128; ++i) {
-    const int u = threadIdx.x + i * 256;
-    const int mc = u % (R / 8), kq = u / (R / 8);
-    const int gm = mn0 + mc * 8;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int gk = k0 + kq * 4 + r;
-      reg[i][r] = (gm < mnlim && gk < klim) ? ld16(base + (int64_t)gk * ld + gm)
-                                            : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < kLoads; ++j) {
+      const uint32_t dst = lds + (wslot * kLoads + j) * 1024u;
+      const uint16_t* gp = base + src[j] + (int64_t)kt * kstep;
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                   :: "v"(gp), "s"(dst) : "memory", "m0");
     }
   }
-}
-template <int R>
-__device__ __forceinline__ void store_mnc(uint16_t* s, const u32x4 (&reg)[R / 128][4]) {
+  // partial K tile [k0, klim) through registers, zero outside
+  __device__ __forceinline__ void tail(uint16_t* s, int k0, int klim) const {
 #pragma unroll
-  for (int i = 0; i < R / 128; ++i) {
-    const int u = threadIdx.x + i * 256;
-    const int mc = u % (R / 8), kq = u / (R / 8);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int sh = (c & 1) * 16;
-      const uint32_t e0 = (reg[i][0][c >> 1] >> sh) & 0xFFFFu;
-      const uint32_t e1 = (reg[i][1][c >> 1] >> sh) & 0xFFFFu;
-      const uint32_t e2 = (reg[i][2][c >> 1] >> sh) & 0xFFFFu;
-      const uint32_t e3 = (reg[i][3][c >> 1] >> sh) & 0xFFFFu;
-      const int row = mc * 8 + c;
-      *reinterpret_cast<u32x2*>(s + swz(row, kq >> 1) + (kq & 1) * 4) =
-          u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+    for (int i = 0; i < kChunks / 256; ++i) {
+      const int c = threadIdx.x + i * 256;
+      if constexpr (KC) {
+        const int row = c >> 2, q = c & 3;
+        const int gr = mn0 + row, gk = k0 + q * 8;
+        const u32x4 v = (gr < lim && gk < klim) ? ld16(base + (int64_t)gr * ld + gk)
+                                                : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(s + kc_off(row, q)) = v;
+      } else {
+        const int k = c / (R / 8), cc = c % (R / 8);
+        const int gk = k0 + k, gm = mn0 + cc * 8;
+        const u32x4 v = (gk < klim && gm < lim) ? ld16(base + (int64_t)gk * ld + gm)
+                                                : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(s + mn_off<R>(k, cc * 8)) = v;
+      }
     }
   }
-}
+  // MFMA 32x32x16 fragment of the 32 rows starting at mb, k sub-step kk:
+  // lane l gets the 8 k values 8 (l / 32) .. +7 of row mb + l % 32
+  __device__ __forceinline__ bf16x8 frag(const uint16_t* s, int mb, int kk, int lane) const {
+    if constexpr (KC) {
+      return *reinterpret_cast<const bf16x8*>(s + kc_off(mb + (lane & 31), kk * 2 + (lane >> 5)));
+    } else {
+      const int G = lane >> 4, a4 = (lane >> 2) & 3, b4 = lane & 3;
+      const int m = mb + (G & 1) * 16 + 4 * b4;
+      const int k = kk * 16 + (G >> 1) * 8 + a4;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(s + mn_off<R>(k, m)));
+      const v4s hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(s + mn_off<R>(k + 4, m)));
+      const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, both);
+    }
+  }
+};
 
 template <int MODE, bool B_KC, int EPI, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr bool A_KC = (MODE == MODE_ROW);
-  // operand tiles, double buffered; reused as the epilogue staging area
-  __shared__ __align__(16) uint16_t smem[2 * BM * BK + 2 * BN * BK];
+  constexpr bool BKC = (MODE == MODE_ROW) && B_KC;
+  using OpA = Operand<A_KC, BM>;
+  using OpB = Operand<BKC, BN>;
+  constexpr int kStageElems = OpA::kElems + OpB::kElems;
+  // the operand ring; reused as the epilogue staging area
+  __shared__ __align__(16) uint16_t smem[kStages * kStageElems];
   __shared__ int s_tiles[MODE == MODE_ROW ? 257 : 1];
-  uint16_t (*sA)[BM * BK] = reinterpret_cast<uint16_t (*)[BM * BK]>(smem);
-  uint16_t (*sB)[BN * BK] = reinterpret_cast<uint16_t (*)[BN * BK]>(smem + 2 * BM * BK);
 
   Tile t;
   if (!decode_tile<MODE, BM, BN>(g, s_tiles, t)) return;
@@ -206,7 +248,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
-  const int h = lane >> 5, r = lane & 31;
+
+  OpA opa;
+  OpB opb;
+  opa.init(A, g.lda, t.m0, t.M, w, lane);
+  opb.init(B, g.ldb, t.n0, g.N, w, lane);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(smem));
+  const uint32_t wslot = __builtin_amdgcn_readfirstlane((uint32_t)w);
+  auto issue = [&](int kt) {
+    const uint32_t sa = lds0 + (uint32_t)(kt % kStages) * kStageElems * 2u;
+    opa.issue(kt, sa, wslot);
+    opb.issue(kt, sa + OpA::kElems * 2u, wslot);
+  };
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -214,58 +268,51 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  // register staging of the next K tile
-  u32x4 ra_kc[A_KC ? BM / 32 : 1];
-  u32x4 ra_mn[A_KC ? 1 : BM / 128][4];
-  u32x4 rb_kc[B_KC ? BN / 32 : 1];
-  u32x4 rb_mn[B_KC ? 1 : BN / 128][4];
-
-  auto gload = [&](int k0) {
-    if constexpr (A_KC) load_kc<BM>(A, g.lda, t.m0, t.M, k0, t.K, ra_kc);
-    else load_mnc<BM>(A, g.lda, t.m0, t.M, k0, t.K, ra_mn);
-    if constexpr (MODE == MODE_ROW) {
-      if constexpr (B_KC) load_kc<BN>(B, g.ldb, t.n0, g.N, k0, t.K, rb_kc);
-      else load_mnc<BN>(B, g.ldb, t.n0, g.N, k0, t.K, rb_mn);
-    } else {
-      load_mnc<BN>(B, g.ldb, t.n0, g.N, k0, t.K, rb_mn);
-    }
-  };
-  auto lstore = [&](int buf) {
-    if constexpr (A_KC) store_kc<BM>(sA[buf], ra_kc);
-    else store_mnc<BM>(sA[buf], ra_mn);
-    if constexpr (B_KC) store_kc<BN>(sB[buf], rb_kc);
-    else store_mnc<BN>(sB[buf], rb_mn);
-  };
-
-  const int nk = (t.K + BK - 1) / BK;
-  if (nk > 0) {
-    gload(0);
-    lstore(0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) gload((kt + 1) * BK);
+  auto compute = [&](const uint16_t* sa) {
+    const uint16_t* sb = sa + OpA::kElems;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 af[TM], bfv[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sA[buf] + swz(wm * WM + i * 32 + r, kk * 2 + h));
+      for (int i = 0; i < TM; ++i) af[i] = opa.frag(sa, wm * WM + i * 32, kk, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfv[j] = *reinterpret_cast<const bf16x8*>(sB[buf] + swz(wn * WN + j * 32 + r, kk * 2 + h));
+      for (int j = 0; j < TN; ++j) bfv[j] = opb.frag(sb, wn * WN + j * 32, kk, lane);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
     }
-    if (more) lstore(buf ^ 1);
-    __syncthreads();
-  }
+  };
 
+  constexpr int kPer = OpA::kLoads + OpB::kLoads;  // loads per wave per stage
+  const int nfull = t.K / BK;
+  const int ntile = nfull + (t.K % BK != 0 ? 1 : 0);
+#pragma unroll
+  for (int s0 = 0; s0 < kStages - 1; ++s0)
+    if (s0 < nfull) issue(s0);
+  for (int kt = 0; kt < ntile; ++kt) {
+    uint16_t* st = smem + (kt % kStages) * kStageElems;
+    if (kt < nfull) {
+      // tile kt has landed once at most the loads of the tiles issued
+      // after it (up to kStages - 2 of them) are outstanding
+      if (kt + kStages - 2 < nfull)
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"((kStages - 2) * kPer) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      // the partial last tile, through registers; its stage was last read
+      // kStages iterations ago and has no copy in flight
+      opa.tail(st, kt * BK, t.K);
+      opb.tail(st + OpA::kElems, kt * BK, t.K);
+    }
+    __syncthreads();  // tile kt is complete in LDS; stage kt-1 is free
+    if (kt + kStages - 1 < nfull) issue(kt + kStages - 1);
+    compute(st);
+  }
+  __syncthreads();  // the staging below overwrites the ring
+
+  const int h = lane >> 5, r = lane & 31;
   // Epilogue through LDS: each wave stages 32 rows x WN columns of its
   // accumulators (D[i][j] sits in lane j + 32*((i/4)%2), register
   // (i%4) + 4*(i/8)), then every lane handles 8 consecutive columns of a row
