@@ -268,47 +268,85 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  auto compute = [&](const uint16_t* sa) {
-    const uint16_t* sb = sa + OpA::kElems;
+  // Fragments are double-buffered in registers: the MFMAs of one 16-wide k
+  // step run on set c while the fragments of the next k step (possibly in
+  // the next stage) are read into set c ^ 1, one read after each MFMA.
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto ring = [&](int kt) { return smem + (kt % kStages) * kStageElems; };
+  auto load_frags = [&](int c, const uint16_t* st, int kk) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[TM], bfv[TN];
+    for (int i = 0; i < TM; ++i) fa[c][i] = opa.frag(st, wm * WM + i * 32, kk, lane);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = opa.frag(sa, wm * WM + i * 32, kk, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfv[j] = opb.frag(sb, wn * WN + j * 32, kk, lane);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
-    }
+    for (int j = 0; j < TN; ++j) fb[c][j] = opb.frag(st + OpA::kElems, wn * WN + j * 32, kk, lane);
   };
+  auto step = [&](int c, const uint16_t* nst, int nkk) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0, 0, 0);
+        const int q = i * TN + j;
+        if (q < TM) fa[c ^ 1][q] = opa.frag(nst, wm * WM + q * 32, nkk, lane);
+        else if (q < TM + TN)
+          fb[c ^ 1][q - TM] = opb.frag(nst + OpA::kElems, wn * WN + (q - TM) * 32, nkk, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  static_assert(TM * TN >= TM + TN, "one fragment read per MFMA");
 
-  constexpr int kPer = OpA::kLoads + OpB::kLoads;  // loads per wave per stage
+  // K tiles: nfull full tiles copied straight into LDS, then at most one
+  // partial tile written through registers.  The ring holds kStages tiles;
+  // tile kt + kStages is issued into tile kt's stage once every wave has
+  // read all of tile kt's fragments (the barrier inside iteration kt).
+  constexpr int kPer = OpA::kLoads + OpB::kLoads;  // loads per wave per tile
+  constexpr int KS = BK / 16;                      // k steps per tile
   const int nfull = t.K / BK;
   const int ntile = nfull + (t.K % BK != 0 ? 1 : 0);
+  auto write_tail = [&](int kt) {
+    opa.tail(ring(kt), kt * BK, t.K);
+    opb.tail(ring(kt) + OpA::kElems, kt * BK, t.K);
+  };
+  if (ntile > 0) {
 #pragma unroll
-  for (int s0 = 0; s0 < kStages - 1; ++s0)
-    if (s0 < nfull) issue(s0);
+    for (int s0 = 0; s0 < kStages; ++s0)
+      if (s0 < nfull) issue(s0);
+    if (nfull >= kStages)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"((kStages - 1) * kPer) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (nfull == 0) write_tail(0);
+    __syncthreads();
+    load_frags(0, ring(0), 0);
+  }
   for (int kt = 0; kt < ntile; ++kt) {
-    uint16_t* st = smem + (kt % kStages) * kStageElems;
-    if (kt < nfull) {
-      // tile kt has landed once at most the loads of the tiles issued
-      // after it (up to kStages - 2 of them) are outstanding
-      if (kt + kStages - 2 < nfull)
-        asm volatile("s_waitcnt vmcnt(%0)" :: "n"((kStages - 2) * kPer) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else {
-      // the partial last tile, through registers; its stage was last read
-      // kStages iterations ago and has no copy in flight
-      opa.tail(st, kt * BK, t.K);
-      opb.tail(st + OpA::kElems, kt * BK, t.K);
+    const uint16_t* st = ring(kt);
+#pragma unroll
+    for (int kk = 0; kk < KS - 1; ++kk) step(kk & 1, st, kk + 1);
+    const bool more = kt + 1 < ntile;
+    if (more) {
+      if (kt + 1 < nfull) {
+        // tile kt+1 has landed once at most the tiles issued after it
+        // (up to kStages - 2) are outstanding
+        if (kt + kStages - 1 < nfull)
+          asm volatile("s_waitcnt vmcnt(%0)" :: "n"((kStages - 2) * kPer) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else {
+        // tile kt+1 is the partial one; its stage was last read in
+        // iteration kt+1-kStages and receives no copy
+        write_tail(kt + 1);
+      }
+      __syncthreads();
+      if (kt + kStages < nfull) issue(kt + kStages);
     }
-    __syncthreads();  // tile kt is complete in LDS; stage kt-1 is free
-    if (kt + kStages - 1 < nfull) issue(kt + kStages - 1);
-    compute(st);
+    // after the last tile the reads below re-read this tile (unused)
+    step((KS - 1) & 1, more ? ring(kt + 1) : st, 0);
+    if constexpr (((KS - 1) & 1) == 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[0][i] = fa[1][i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[0][j] = fb[1][j];
+    }
   }
   __syncthreads();  // the staging below overwrites the ring
 
