@@ -46,9 +46,98 @@ def parse():
                     help="workload: C0..C4 or its name (default C1)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kernel", default=None,
-                    help="kernel timed for the roofline (default: the up-projection GEMM)")
+                    help="kernel timed for the roofline (default: GEMM_DH, the dA = "
+                         "(dYp W2^T) * gelu'(A) GEMM, the longest per launch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="before the warmup, run one plain device-to-device copy of BYTES "
+                         "(calibration of the HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="instead of running: read the rocprofv3 --pmc FETCH_SIZE and "
+                         "WRITE_SIZE outputs of a run with --copy-probe and print the "
+                         "per-launch HBM traffic of --kernel as a JSON line")
     return ap.parse_args()
+
+
+# name fragment of each timed kernel in a rocprofv3 trace (template arguments:
+# mode, B K-contiguous, epilogue)
+KERNEL_NAMES = {"GEMM_UP": "gemm_bf16_kernel<0, false, 1,",
+                "GEMM_DOWN": "gemm_bf16_kernel<0, false, 0,",
+                "GEMM_DH": "gemm_bf16_kernel<0, true, 2,",
+                "GEMM_DX": "gemm_bf16_kernel<0, true, 0,"}
+GEMM_SOURCES = ("expert_router_gemm_softmax_amd/csrc/gemm.hip",
+                "expert_router_gemm_softmax_amd/csrc/gemm.h",
+                "expert_router_gemm_softmax_amd/csrc/common.h")
+COUNTERS_GLOB = "profiles/*_hbm_counters.md"
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def summarize_counters(a, w):
+    """Per-launch HBM bytes of --kernel from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by bytes-copied / counter of the --copy-probe copy
+    (the largest device copy dispatch in the same run)."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Dispatch_Id"], r["Kernel_Name"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return vals
+
+    frag = KERNEL_NAMES[a.kernel or "GEMM_DH"]
+    out = {"kernel": a.kernel or "GEMM_DH", "workload": w.name,
+           "gemm_source_sha256_16": gemm_source_hash(), "copy_probe_bytes": a.copy_probe}
+    total = 0.0
+    for d, counter in zip(a.summarize_counters, ("FETCH_SIZE", "WRITE_SIZE")):
+        vals = per_dispatch(d, counter)
+        copies = [v for (i, n), v in vals.items() if "copyBuffer" in n]
+        ks = [v for (i, n), v in vals.items() if frag in n]
+        if not copies or not ks:
+            raise SystemExit(f"{counter}: copy probe or kernel not found in {d}")
+        factor = a.copy_probe / (max(copies) * 1024.0)
+        kib = sum(ks) / len(ks)
+        key = counter.lower()
+        out[f"{key}_kib_per_launch"] = round(kib, 1)
+        out[f"{key}_copy_kib"] = round(max(copies), 1)
+        out[f"{key}_factor"] = round(factor, 4)
+        out[f"{key}_launches"] = len(ks)
+        total += kib * 1024.0 * factor
+    out["traffic_bytes_per_launch"] = round(total)
+    print(json.dumps(out))
+    return 0
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch recorded under profiles/ for this kernel and
+    workload, or None when there is none or the GEMM source has changed."""
+    import glob
+    want = gemm_source_hash()
+    for f in sorted(glob.glob(os.path.join(ROOT, COUNTERS_GLOB))):
+        for line in open(f):
+            line = line.strip()
+            if not line.startswith("{"):
+                continue
+            try:
+                rec = json.loads(line)
+            except ValueError:
+                continue
+            if (rec.get("kernel") == kernel and rec.get("workload") == workload
+                    and rec.get("gemm_source_sha256_16") == want):
+                return rec.get("traffic_bytes_per_launch")
+    return None
 
 
 def dev(a):
@@ -100,11 +189,13 @@ def main():
     import numpy as np
     import torch
 
-    import expert_router_gemm_softmax_amd as M
     import workloads as W
+    w = W.get(a.config)
+    if a.summarize_counters:
+        return summarize_counters(a, w)
+    import expert_router_gemm_softmax_amd as M
 
     torch.cuda.set_device(0)
-    w = W.get(a.config)
     log(f"[bench] workload {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} {w.dtype} "
         f"cf={w.cf}")
     inp = W.make_inputs(w, seed=a.seed)
@@ -145,13 +236,20 @@ def main():
             M.moe_grouped_ffn_bwd(cfg, d["x_perm"], offsets, d["W1"], d["W2"], A, H, dYp,
                                   dXp, dW1, dW2, ws)
 
+    if a.copy_probe:
+        src = torch.empty(a.copy_probe, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(a.warmup):
         step()
     torch.cuda.synchronize()
     R = int(offsets[-1].item())
     log(f"[bench] warmup done, R={R} kept rows of {w.T * w.k}")
 
-    kernel = a.kernel or "GEMM_UP"
+    kernel = a.kernel or "GEMM_DH"
     M.moe_prof_arm(kernel, a.steps)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -178,7 +276,8 @@ def main():
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
         achieved = flops[kernel] / avg_s / 1e12 if avg_s > 0 else 0.0
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": recorded_traffic(kernel, w.name),
                 "kernel": kernel, "avg_ms": round(avg_s * 1e3, 5)}
     else:
         roof = {"bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
