@@ -32,7 +32,7 @@ KERNELS = dict(ROUTE=0, PERMUTE_COUNT=1, PERMUTE_SCAN=2, PERMUTE_SCATTER=3,
                GEMM_UP=4, GEMM_DOWN=5, COMBINE=6, COMBINE_BWD=7, GEMM_DH=8,
                GEMM_DX=9, GEMM_DW2=10, GEMM_DW1=11, UNPERMUTE_BWD=12,
                ROUTE_BWD_DZ=13, ROUTE_BWD_DX=14, ROUTE_BWD_DW=15, SCHEDULE=16,
-               ROUTE_PREP=17, PERMUTE_COPY=18)
+               ROUTE_PREP=17, PERMUTE_COPY=18, ROUTE_LOGITS=19)
 
 
 class MoeLibraryError(ImportError):

@@ -162,9 +162,8 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* Wr, const float* b,
   MOE_TRY(need(idx, z.Tk, 4));
   MOE_TRY(need(gate, z.Tk, 4));
   MOE_TRY(need_ws(c, ws, ws_bytes));
-  void* wrT = ws_ptr<void>(ws, ws_layout(c).wrT);
   clear_stale_error();
-  return launch_route(c, x, Wr, b, probs, idx, gate, wrT, S(stream));
+  return launch_route(c, x, Wr, b, probs, idx, gate, ws, S(stream));
 }
 
 int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx, int32_t* counts,
@@ -330,8 +329,7 @@ int moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const void* x, void*
   const hipStream_t s = S(stream);
   const WsLayout L = ws_layout(c);
   clear_stale_error();
-  MOE_TRY(launch_route(c, x, w->Wr, w->b, ctx->probs, ctx->idx, ctx->gate,
-                       ws_ptr<void>(ws, L.wrT), s));
+  MOE_TRY(launch_route(c, x, w->Wr, w->b, ctx->probs, ctx->idx, ctx->gate, ws, s));
   MOE_TRY(launch_permute(c, x, ctx->idx, ctx->counts, ctx->offsets, ctx->row_of,
                          ctx->src_of, ctx->x_perm, ws, s));
   MOE_TRY(launch_ffn_fwd(c, ctx->x_perm, ctx->offsets, w->W1, w->W2, ctx->A, ctx->H, ctx->Y,

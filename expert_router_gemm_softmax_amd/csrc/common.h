@@ -75,15 +75,20 @@ template <> struct St<uint16_t> {
 };
 
 // ------------------------------------------------------------------ GELU (tanh form)
+// tanh(u) = 1 - 2 / (e^{2u} + 1): hardware exp and reciprocal, absolute
+// error ~1e-7; saturates to +-1 (e^{2u} overflowing to inf gives 1)
+__device__ __forceinline__ float tanh_fast(float u) {
+  return 1.0f - __fdividef(2.0f, __expf(2.0f * u) + 1.0f);
+}
 // gelu(a) = 0.5 a (1 + tanh(u)),  u = sqrt(2/pi) (a + 0.044715 a^3)
 __device__ __forceinline__ float gelu_tanh(float a) {
   const float u = 0.7978845608028654f * (a + 0.044715f * a * a * a);
-  return 0.5f * a * (1.0f + tanhf(u));
+  return 0.5f * a * (1.0f + tanh_fast(u));
 }
 // d gelu / da = 0.5 (1 + tanh u) + 0.5 a (1 - tanh^2 u) sqrt(2/pi) (1 + 3*0.044715 a^2)
 __device__ __forceinline__ float gelu_tanh_grad(float a) {
   const float u = 0.7978845608028654f * (a + 0.044715f * a * a * a);
-  const float th = tanhf(u);
+  const float th = tanh_fast(u);
   return 0.5f * (1.0f + th) +
          0.5f * a * (1.0f - th * th) * 0.7978845608028654f *
              (1.0f + 0.134145f * a * a);
@@ -108,25 +113,29 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // One workspace buffer serves every entry point; each region is 256-byte
 // aligned.  Regions:
 //   wrT      [Epad, d] s        router weights transposed, zero rows >= E
+//   zf       [T, Epad] f32      fast router logits x Wr (no bias); then the
+//                               canonical logits of the rescoring worklist
+//   wl_*                        router rescoring worklist: count, tokens [T],
+//                               candidate counts [T], candidates [T, Epad]
 //   perm_blk [nblk_perm, E] i32 per-block expert histograms / bases
 //   tiles    [E+1] i32          grouped-GEMM M-tile prefix per expert
 //   dz       [T, E] f32         router logit gradient (float storage)
 //   dzb      [T, 2*Ep] bf16     dz split into bf16 high and low parts
 //   wrp      [d, 2*Ep] bf16     Wr twice side by side, zero padded (bf16)
 //   dwr_part [nchunk, d, Nw] f32 per-token-chunk partial sums of x^T dz
-//   db_part  [nblk_dz, E] f32   per-block partial sums of dz
+//   db_part  [E, nblk_dz] f32   per-block partial sums of dz
 //   dgate    [T, k] f32         combine-backward gate gradient
 //   dYp, dA, dXp                backward row gradients (Rmax rows, s)
 //   dxe      [T, d] f32         unpermute-sum of dXp (router backward)
 struct WsLayout {
-  size_t wrT, perm_blk, tiles, dz, dzb, wrp, dwr_part, db_part, dgate, dYp, dA, dXp, dxe, total;
+  size_t wrT, zf, wl_count, wl_tok, wl_n, wl_e, perm_blk, tiles, dz, dzb, wrp, dwr_part, db_part, dgate, dYp, dA, dXp, dxe, total;
   int nblk_perm;
   int nblk_dz;
   int dwr_chunks, dwr_chunk, dwr_n;
 };
 
 constexpr int kPermTokens = 256;  // tokens per permute block
-constexpr int kDzTokens = 64;     // tokens per router-backward dz block
+constexpr int kDzTokens = 16;     // tokens per router-backward dz block
 
 inline int64_t rows_max(const moe_cfg& c) {
   const int64_t tk = c.T * c.k;
@@ -170,6 +179,11 @@ inline WsLayout ws_layout(const moe_cfg& c) {
     return o;
   };
   L.wrT = take((size_t)route_epad(c.E) * c.d * s);
+  L.zf = take((size_t)c.T * route_epad(c.E) * 4);
+  L.wl_count = take(4);
+  L.wl_tok = take((size_t)c.T * 4);
+  L.wl_n = take((size_t)c.T * 4);
+  L.wl_e = take((size_t)c.T * route_epad(c.E) * 4);
   L.perm_blk = take((size_t)L.nblk_perm * c.E * 4);
   L.tiles = take((size_t)(c.E + 1) * 4 * 4);
   L.dz = take(bf ? 0 : (size_t)c.T * c.E * 4);
@@ -213,7 +227,7 @@ void note_launch_error(int kernel_id, hipError_t e);
 // ------------------------------------------------------------------ launchers
 // (each validates nothing: the C-ABI layer in api.hip has done that)
 int launch_route(const moe_cfg& c, const void* x, const void* Wr, const float* b,
-                 float* probs, int32_t* idx, float* gate, void* wrT, hipStream_t s);
+                 float* probs, int32_t* idx, float* gate, void* ws, hipStream_t s);
 int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
                    int32_t* counts, int32_t* offsets, int32_t* row_of,
                    int32_t* src_of, void* x_perm, void* ws, hipStream_t s);

@@ -31,6 +31,8 @@ struct GemmArgs {
   int lda, ldb, ldc;     // leading dims (elements)
   int64_t b_estride;     // ROW: elements between experts' B
   int64_t c_estride;     // KRAG: elements between groups' C
+  int bm, bn;            // ROW one-group problems with K-contiguous B and an
+                         // fp32 epilogue: block tile (64 or 128 each); 0 = auto
   int ntn, ntm;          // filled by the launcher
 };
 

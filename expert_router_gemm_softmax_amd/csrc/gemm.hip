@@ -279,20 +279,24 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[c][j] = opb.frag(st + OpA::kElems, wn * WN + j * 32, kk, lane);
   };
+  auto read_frag = [&](int c, const uint16_t* nst, int nkk, int f) {
+    if (f < TM) fa[c][f] = opa.frag(nst, wm * WM + f * 32, nkk, lane);
+    else fb[c][f - TM] = opb.frag(nst + OpA::kElems, wn * WN + (f - TM) * 32, nkk, lane);
+  };
   auto step = [&](int c, const uint16_t* nst, int nkk) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0, 0, 0);
+        // fragment q after MFMA q; the last MFMA is followed by any rest
         const int q = i * TN + j;
-        if (q < TM) fa[c ^ 1][q] = opa.frag(nst, wm * WM + q * 32, nkk, lane);
-        else if (q < TM + TN)
-          fb[c ^ 1][q - TM] = opb.frag(nst + OpA::kElems, wn * WN + (q - TM) * 32, nkk, lane);
+#pragma unroll
+        for (int f = 0; f < TM + TN; ++f)
+          if (f == q || (q == TM * TN - 1 && f > q)) read_frag(c ^ 1, nst, nkk, f);
         __builtin_amdgcn_sched_barrier(0);
       }
   };
-  static_assert(TM * TN >= TM + TN, "one fragment read per MFMA");
 
   // K tiles: nfull full tiles copied straight into LDS, then at most one
   // partial tile written through registers.  The ring holds kStages tiles;
@@ -548,6 +552,10 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
     // one-group problems choose freely; grouped ones follow the schedule
     BM = g.offsets ? row_bm(c) : (use_big_tile(c, MODE_KRAG, g.M, g.N, 1) ? 256 : 128);
     BN = BM;
+    if constexpr (B_KC && EPI == EPI_F32) {
+      if (g.bm) BM = g.bm;
+      if (g.bn) BN = g.bn;
+    }
   } else {
     BM = BN = use_big_tile(c, MODE_KRAG, g.M, g.N, g.E) ? 256 : 128;
   }
@@ -561,9 +569,22 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
   }
   if (nblk == 0) return MOE_OK;
   const int grid = grid8(nblk);
-  if (!bf)
+  if (!bf) {
     MOE_LAUNCH(kid, s, gemm_f32_kernel<MODE, B_KC, EPI><<<grid, 256, 0, s>>>(g));
-  else if (BM == 256)
+    return MOE_OK;
+  }
+  if constexpr (MODE == MODE_ROW && B_KC && EPI == EPI_F32) {
+    if (BM == 64 && BN == 64)
+      MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 64, 64><<<grid, 256, 0, s>>>(g));
+    else if (BM == 64 && BN == 128)
+      MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 64, 128><<<grid, 256, 0, s>>>(g));
+    else if (BM == 128 && BN == 64)
+      MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 128, 64><<<grid, 256, 0, s>>>(g));
+    else
+      MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 128, 128><<<grid, 256, 0, s>>>(g));
+    return MOE_OK;
+  }
+  if (BM == 256)
     MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 256, 256><<<grid, 256, 0, s>>>(g));
   else
     MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 128, 128><<<grid, 256, 0, s>>>(g));
@@ -599,6 +620,8 @@ int launch_gemm(int kid, int mode, bool b_kc, int epi, const moe_cfg& c, GemmArg
     return run_gemm<MODE_KRAG, false, EPI_F32>(kid, c, g, s);
   if (mode == MODE_ROW && b_kc && epi == EPI_ADDF32)
     return run_gemm<MODE_ROW, true, EPI_ADDF32>(kid, c, g, s);
+  if (mode == MODE_ROW && b_kc && epi == EPI_F32)
+    return run_gemm<MODE_ROW, true, EPI_F32>(kid, c, g, s);
   return MOE_ERR_UNIMPLEMENTED;
 }
 

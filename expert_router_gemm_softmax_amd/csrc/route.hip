@@ -6,58 +6,62 @@
 //
 // Decision rule.  The decision is defined on the canonical logit
 // z = RN_fp32(sum_i x_i Wr_ie + b_e) with the sum in fp64.  The fast path
-// computes zf with fp32 accumulation (bf16 MFMA, or fp32 VALU for float
-// storage).  If every gap between neighbours in the top-(k+1) of zf is at
-// least tau, the order of zf is the canonical order (|zf - z| < tau/2).
-// Otherwise every expert whose zf lies within tau of the (k+1)-th value or
-// above it is rescored in fp64 and the top-k is taken among those: any
-// expert below that band has k+1 experts canonically above it.
+// computes zf with fp32 accumulation.  If every gap between neighbours in
+// the top-(k+1) of zf is at least tau, the order of zf is the canonical
+// order (|zf - z| < tau/2).  Otherwise every expert whose zf lies within
+// tau of the (k+1)-th value or above it is rescored in fp64 and the top-k
+// is taken among those: any expert below that band has k+1 experts
+// canonically above it.
 //
-// Layout: one block = 4 waves x 32 tokens.  The bf16 logits use
-// v_mfma_f32_32x32x16_bf16 with tokens on M and experts on N (padded to a
-// multiple of 32); each lane streams its token row straight from HBM
-// (64 contiguous bytes per 64-wide K chunk: the K order inside a chunk is
-// permuted identically for both operands), the transposed router weights
-// are staged through LDS once per block and shared by its 4 waves.
-#include "common.h"
+// Two kernels.  The fast logits x Wr come from the grouped GEMM (one group
+// of T rows, the transposed router weights as a K-contiguous operand, fp32
+// epilogue into a [T, Epad] workspace matrix): the router is a skinny GEMM
+// whose cost is reading x once.  The select kernel then takes 32 tokens per
+// wave: softmax statistics and top-(k+1) per token (one lane per token),
+// fp64 rescoring of uncertain tokens (one wave per token), and coalesced
+// writes of probabilities, experts and gates.
+#include "gemm.h"
 
 #include <float.h>
 
 namespace moe {
 
-int launch_transpose_wr(const moe_cfg& c, const void* Wr, void* wrT, hipStream_t s);
+int launch_transpose_wr(const moe_cfg& c, const void* Wr, void* wrT, int* wl_count,
+                        hipStream_t s);
 
 namespace {
 
+struct RouteWorklist {
+  int* count;  // number of uncertain tokens
+  int* tok;    // [T] their token indices
+  int* n;      // [T] their candidate counts
+  int* e;      // [T, Epad] their candidate experts, ascending
+};
+
 constexpr int kRW = 4;     // waves per block
 constexpr int kRT = 32;    // tokens per wave
-constexpr int kRBK = 64;   // K chunk
-constexpr int kRBKP = 72;  // LDS row of the staged weight chunk (elements)
 
 struct RouteSmem {
   int zs_stride;  // floats per token row of logits
-  size_t zs_off, stats_off, idx_off, uz_off, ue_off, total;
+  size_t zs_off, stats_off, idx_off, total;
 };
 
-__host__ __device__ inline RouteSmem route_smem(int Epad, int k, int elem) {
+__host__ __device__ inline RouteSmem route_smem(int Epad, int k) {
   RouteSmem m{};
   m.zs_stride = Epad + 1;
-  size_t zs = (size_t)kRW * kRT * m.zs_stride * 4;
-  size_t sb = elem == 2 ? (size_t)2 * Epad * kRBKP * 2 : 0;
-  size_t u = zs > sb ? zs : sb;
+  const size_t u = (size_t)kRW * kRT * m.zs_stride * 4;
   m.zs_off = 0;
   m.stats_off = (u + 15) / 16 * 16;
   m.idx_off = m.stats_off + (size_t)3 * kRW * kRT * 4;
-  m.uz_off = m.idx_off + (size_t)kRW * kRT * k * 4;
-  m.ue_off = m.uz_off + (size_t)kRW * Epad * 4;
-  m.total = m.ue_off + (size_t)kRW * Epad * 4;
+  m.total = m.idx_off + (size_t)kRW * kRT * k * 4;
   return m;
 }
 
 // wrT[e][i] = Wr[i][e] for e < E, zero rows for E <= e < Epad.
 template <typename T>
 __global__ void transpose_wr_kernel(const T* __restrict__ Wr, T* __restrict__ wrT,
-                                    int d, int E, int Epad) {
+                                    int d, int E, int Epad, int* __restrict__ wl_count) {
+  if (wl_count && blockIdx.x == 0 && threadIdx.x == 0) *wl_count = 0;
   const int64_t n = (int64_t)Epad * d;
   for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < n;
        o += (int64_t)gridDim.x * blockDim.x) {
@@ -66,129 +70,15 @@ __global__ void transpose_wr_kernel(const T* __restrict__ Wr, T* __restrict__ wr
   }
 }
 
-// bf16 logits of the wave's 32 tokens into zs (fp32 accumulate, + bias).
-template <int NT>
-__device__ __forceinline__ void logits_mfma(const uint16_t* __restrict__ x,
-                                            const uint16_t* __restrict__ wrT,
-                                            const float* __restrict__ bias,
-                                            int64_t T_, int d, int E, int64_t t_w,
-                                            uint16_t* sB, float* zs, int zs_stride) {
-  constexpr int Epad = 32 * NT;
-  const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
-  const int64_t tr = t_w + r;
-  const bool row_ok = tr < T_;
-  const uint16_t* xrow = x + (row_ok ? tr : 0) * (int64_t)d;
-  const int nkc = (d + kRBK - 1) / kRBK;
-
-  f32x16 acc[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x16{};
-
-  u32x4 a_cur[4], a_nxt[4], b_nxt[NT];
-  auto load_a = [&](int kc, u32x4 (&a)[4]) {
-    const int k0 = kc * kRBK + h * 32;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int kq = k0 + q * 8;
-      a[q] = (row_ok && kq < d) ? ld16(xrow + kq) : u32x4{0, 0, 0, 0};
-    }
-  };
-  // Epad rows x 8 chunks of 16 bytes per K chunk; NT chunks per thread
-  auto load_b = [&](int kc, u32x4 (&bq)[NT]) {
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int c = threadIdx.x + i * 256;
-      const int e = c >> 3, q = c & 7;
-      const int kq = kc * kRBK + q * 8;
-      bq[i] = kq < d ? ld16(wrT + (int64_t)e * d + kq) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_b = [&](int buf, const u32x4 (&bq)[NT]) {
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int c = threadIdx.x + i * 256;
-      const int e = c >> 3, q = c & 7;
-      *reinterpret_cast<u32x4*>(sB + ((size_t)buf * Epad + e) * kRBKP + q * 8) = bq[i];
-    }
-  };
-
-  // Token rows stream two K chunks ahead of the MFMAs: three register sets
-  // with fixed roles (a rotating copy would wait on the loads in flight);
-  // the router weights go through the LDS double buffer one chunk ahead.
-  u32x4 a_2[4];
-  auto step = [&](int kc, u32x4 (&acur)[4], u32x4 (&afar)[4]) {
-    if (kc >= nkc) return;
-    const int buf = kc & 1;
-    const bool more = kc + 1 < nkc;
-    if (kc + 2 < nkc) load_a(kc + 2, afar);
-    if (more) load_b(kc + 1, b_nxt);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, acur[kk]);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const u32x4 bv = *reinterpret_cast<const u32x4*>(
-            sB + ((size_t)buf * Epad + n * 32 + r) * kRBKP + (h * 4 + kk) * 8);
-        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            a, __builtin_bit_cast(bf16x8, bv), acc[n], 0, 0, 0);
-      }
-    }
-    if (more) store_b(buf ^ 1, b_nxt);
-    __syncthreads();
-  };
-  load_a(0, a_cur);
-  if (nkc > 1) load_a(1, a_nxt);
-  load_b(0, b_nxt);
-  store_b(0, b_nxt);
-  __syncthreads();
-  for (int kc = 0; kc < nkc; kc += 3) {
-    step(kc, a_cur, a_2);
-    step(kc + 1, a_nxt, a_cur);
-    step(kc + 2, a_2, a_nxt);
-  }
-  // D[i][j]: token i = 8*(v/4) + 4*h + v%4, expert j = n*32 + r
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int j = n * 32 + r;
-    if (j < E) {
-      const float bj = bias ? bias[j] : 0.0f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = 8 * (v >> 2) + 4 * h + (v & 3);
-        zs[i * zs_stride + j] = acc[n][v] + bj;
-      }
-    }
-  }
-}
-
-// fp32 logits (VALU): lane (token r, parity h) sums experts e = h, h+2, ...
-__device__ __forceinline__ void logits_valu(const float* __restrict__ x,
-                                            const float* __restrict__ wrT,
-                                            const float* __restrict__ bias,
-                                            int64_t T_, int d, int E, int64_t t_w,
-                                            float* zs, int zs_stride) {
-  const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
-  const int64_t tr = t_w + r;
-  if (tr < T_) {
-    const float* xrow = x + tr * (int64_t)d;
-    for (int e = h; e < E; e += 2) {
-      const float* wr = wrT + (int64_t)e * d;
-      float acc = 0.0f;
-      for (int i = 0; i < d; ++i) acc += xrow[i] * wr[i];
-      zs[r * zs_stride + e] = acc + (bias ? bias[e] : 0.0f);
-    }
-  }
-  __syncthreads();
-}
-
-template <typename T, int NT, int KL>
+template <typename T, int KL>
 __global__ __launch_bounds__(256) void route_kernel(
-    const T* __restrict__ x, const T* __restrict__ wrT, const float* __restrict__ bias,
-    float* __restrict__ probs, int32_t* __restrict__ idx_out,
-    float* __restrict__ gate_out, int64_t T_, int d, int E, int Epad, int k,
+    const float* __restrict__ zf, const T* __restrict__ x, const T* __restrict__ wrT,
+    const float* __restrict__ bias, float* __restrict__ probs, int32_t* __restrict__ idx_out,
+    float* __restrict__ gate_out, int* __restrict__ wl_count, int* __restrict__ wl_tok,
+    int* __restrict__ wl_n, int* __restrict__ wl_e, int64_t T_, int d, int E, int Epad, int k,
     float tau) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const RouteSmem L = route_smem(Epad, k, (int)sizeof(T));
+  const RouteSmem L = route_smem(Epad, k);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t_w = (int64_t)blockIdx.x * (kRW * kRT) + (int64_t)w * kRT;
   float* zs = reinterpret_cast<float*>(smem + L.zs_off) + (size_t)w * kRT * L.zs_stride;
@@ -196,19 +86,17 @@ __global__ __launch_bounds__(256) void route_kernel(
   float* s_sum = s_max + kRW * kRT;
   float* s_thr = s_sum + kRW * kRT;
   int32_t* s_idx = reinterpret_cast<int32_t*>(smem + L.idx_off) + (size_t)w * kRT * k;
-  float* s_uz = reinterpret_cast<float*>(smem + L.uz_off) + (size_t)w * Epad;
-  int32_t* s_ue = reinterpret_cast<int32_t*>(smem + L.ue_off) + (size_t)w * Epad;
 
-  // ---- phase 1: fast logits
-  if constexpr (sizeof(T) == 2) {
-    logits_mfma<NT>(reinterpret_cast<const uint16_t*>(x),
-                    reinterpret_cast<const uint16_t*>(wrT), bias, T_, d, E, t_w,
-                    reinterpret_cast<uint16_t*>(smem + L.zs_off), zs, L.zs_stride);
-    __syncthreads();
-  } else {
-    logits_valu(reinterpret_cast<const float*>(x), reinterpret_cast<const float*>(wrT),
-                bias, T_, d, E, t_w, zs, L.zs_stride);
+  // ---- phase 1: fast logits of the wave's tokens (+ bias) into LDS
+  {
+    const int64_t rem = T_ - t_w;
+    const int nv = rem <= 0 ? 0 : (rem < kRT ? (int)rem : kRT);
+    for (int o = lane; o < nv * E; o += kWave) {
+      const int tt = o / E, e = o - tt * E;
+      zs[tt * L.zs_stride + e] = zf[(t_w + tt) * Epad + e] + (bias ? bias[e] : 0.0f);
+    }
   }
+  __syncthreads();
 
   // ---- phase 2: softmax statistics and top-(k+1) of the fast logits
   bool flag = false;
@@ -248,71 +136,30 @@ __global__ __launch_bounds__(256) void route_kernel(
   }
   __syncthreads();
 
-  // ---- phase 3: canonical fp64 rescoring where the fast order is uncertain
+  // ---- phase 3: tokens whose fast order is uncertain go to the rescoring
+  // worklist with their candidate experts (ascending); their idx and gate
+  // written below are provisional and replaced by route_rescore_kernel
   uint64_t fm = __ballot(flag);
   while (fm) {
     const int tl = __builtin_ctzll(fm);
     fm &= fm - 1;
-    const int64_t t = t_w + tl;
     const float thr = s_thr[tl];
-    int nU = 0;
-    for (int base = 0; base < E; base += 64) {
+    int slot = 0;
+    if (lane == 0) slot = atomicAdd(wl_count, 1);
+    slot = __shfl(slot, 0, kWave);
+    int n = 0;
+    for (int base = 0; base < E; base += kWave) {
       const int e = base + lane;
       const bool in = e < E && zs[tl * L.zs_stride + e] >= thr;
-      uint64_t um = __ballot(in);
-      while (um) {
-        const int ee = base + __builtin_ctzll(um);
-        um &= um - 1;
-        // fp64 dot product of the token row with the expert's weights:
-        // 16-byte vectors, every lane's loads issued before their use
-        constexpr int V = St<T>::kVec;
-        const T* xr = x + t * (int64_t)d;
-        const T* wr = wrT + (int64_t)ee * d;
-        const int nch = d / V;
-        double acc = 0.0;
-        for (int c0 = lane; c0 < nch; c0 += 4 * 64) {
-          u32x4 xv[4], wv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c = c0 + q * 64;
-            if (c < nch) {
-              xv[q] = ld16(xr + c * V);
-              wv[q] = ld16(wr + c * V);
-            }
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (c0 + q * 64 >= nch) continue;
-            float xf[V], wf[V];
-            St<T>::unpack(xv[q], xf);
-            St<T>::unpack(wv[q], wf);
-#pragma unroll
-            for (int i = 0; i < V; ++i) acc += (double)xf[i] * (double)wf[i];
-          }
-        }
-        acc = wave_sum_d(acc);
-        if (lane == 0) {
-          s_uz[nU] = (float)(acc + (double)(bias ? bias[ee] : 0.0f));
-          s_ue[nU] = ee;
-        }
-        ++nU;
-      }
+      const uint64_t um = __ballot(in);
+      if (in) wl_e[(int64_t)slot * Epad + n + __popcll(um & ((1ull << lane) - 1ull))] = e;
+      n += __popcll(um);
     }
     if (lane == 0) {
-      for (int j = 0; j < k; ++j) {
-        int best = -1;
-        for (int u = 0; u < nU; ++u) {
-          if (s_ue[u] < 0) continue;
-          if (best < 0 || s_uz[u] > s_uz[best] ||
-              (s_uz[u] == s_uz[best] && s_ue[u] < s_ue[best]))
-            best = u;
-        }
-        s_idx[tl * k + j] = s_ue[best];
-        s_ue[best] = -1;
-      }
+      wl_tok[slot] = (int)(t_w + tl);
+      wl_n[slot] = n;
     }
   }
-  __syncthreads();
 
   // ---- phase 4: probabilities, chosen experts and gates (coalesced writes)
   const int64_t rem = T_ - t_w;
@@ -329,35 +176,146 @@ __global__ __launch_bounds__(256) void route_kernel(
   }
 }
 
-template <typename T, int NT, int KL>
-int launch_route_t(const moe_cfg& c, const T* x, const T* Wr, const float* b,
-                   float* probs, int32_t* idx, float* gate, T* wrT, hipStream_t s) {
-  const int Epad = 32 * NT;
-  int rc = launch_transpose_wr(c, Wr, wrT, s);
+// Canonical rescoring of the worklist: one wave per uncertain token.  Each
+// candidate's logit is RN_fp32(fp64 sum of x_i Wr_ie + b_e), two candidates
+// at a time with all their 16-byte loads in flight; then the top-k among
+// the candidates (z descending, expert ascending) replaces the token's
+// provisional experts and gates.  wl_z (the fast-logit workspace, no longer
+// needed) holds the canonical logits.
+template <typename T>
+__global__ __launch_bounds__(256) void route_rescore_kernel(
+    const int* __restrict__ wl_count, const int* __restrict__ wl_tok,
+    const int* __restrict__ wl_n, const int* __restrict__ wl_e, float* __restrict__ wl_z,
+    const T* __restrict__ x, const T* __restrict__ wrT, const float* __restrict__ bias,
+    const float* __restrict__ probs, int32_t* __restrict__ idx_out,
+    float* __restrict__ gate_out, int d, int E, int Epad, int k) {
+  constexpr int V = St<T>::kVec;
+  constexpr int CPL = 4;  // 16-byte chunks per lane per pass
+  const int lane = threadIdx.x & 63;
+  const int count = *wl_count;
+  const int nch = d / V;
+  for (int slot = blockIdx.x * 4 + (threadIdx.x >> 6); slot < count; slot += gridDim.x * 4) {
+    const int64_t t = wl_tok[slot];
+    const int n = wl_n[slot];
+    const int* cand = wl_e + (int64_t)slot * Epad;
+    float* cz = wl_z + (int64_t)slot * Epad;
+    const T* xr = x + t * d;
+    for (int c0 = 0; c0 < n; c0 += 2) {
+      const int e0 = cand[c0];
+      const int e1 = c0 + 1 < n ? cand[c0 + 1] : e0;
+      const T* w0 = wrT + (int64_t)e0 * d;
+      const T* w1 = wrT + (int64_t)e1 * d;
+      double a0 = 0.0, a1 = 0.0;
+      for (int g = lane; g < nch; g += CPL * kWave) {
+        u32x4 xv[CPL], v0[CPL], v1[CPL];
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+          const int c = g + q * kWave;
+          if (c < nch) {
+            xv[q] = ld16(xr + c * V);
+            v0[q] = ld16(w0 + c * V);
+            v1[q] = ld16(w1 + c * V);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+          if (g + q * kWave >= nch) continue;
+          float xf[V], f0[V], f1[V];
+          St<T>::unpack(xv[q], xf);
+          St<T>::unpack(v0[q], f0);
+          St<T>::unpack(v1[q], f1);
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            a0 += (double)xf[i] * (double)f0[i];
+            a1 += (double)xf[i] * (double)f1[i];
+          }
+        }
+      }
+      a0 = wave_sum_d(a0);
+      a1 = wave_sum_d(a1);
+      if (lane == 0) {
+        cz[c0] = (float)(a0 + (double)(bias ? bias[e0] : 0.0f));
+        if (c0 + 1 < n) cz[c0 + 1] = (float)(a1 + (double)(bias ? bias[e1] : 0.0f));
+      }
+    }
+    if (lane == 0) {
+      uint64_t used[4] = {0, 0, 0, 0};  // n <= Epad <= 256
+      for (int j = 0; j < k; ++j) {
+        int best = -1;
+        float bz = 0.0f;
+        int be = 0;
+        for (int u = 0; u < n; ++u) {
+          if ((used[u >> 6] >> (u & 63)) & 1ull) continue;
+          const float zu = cz[u];
+          const int eu = cand[u];
+          if (best < 0 || zu > bz || (zu == bz && eu < be)) {
+            best = u;
+            bz = zu;
+            be = eu;
+          }
+        }
+        used[best >> 6] |= 1ull << (best & 63);
+        idx_out[t * k + j] = be;
+        gate_out[t * k + j] = probs[t * E + be];
+      }
+    }
+  }
+}
+
+template <typename T, int KL>
+int launch_route_t(const moe_cfg& c, const T* x, const T* Wr, const float* b, float* probs,
+                   int32_t* idx, float* gate, T* wrT, float* zf, const RouteWorklist& wl,
+                   hipStream_t s) {
+  const int Epad = route_epad(c.E);
+  int rc = launch_transpose_wr(c, Wr, wrT, wl.count, s);
+  if (rc != MOE_OK) return rc;
+  // zf = x wrT^T: one group of T rows, N = Epad, K = d
+  GemmArgs g{};
+  g.E = 1;
+  g.M = (int)c.T;
+  g.N = Epad;
+  g.K = c.d;
+  g.A = x;
+  g.lda = c.d;
+  g.B = wrT;
+  g.ldb = c.d;
+  g.C = zf;
+  g.ldc = Epad;
+  g.bn = Epad <= 64 ? 64 : 128;
+  g.bm = ceil_div(c.T, 128) * ceil_div(Epad, g.bn) >= 256 ? 128 : 64;
+  rc = launch_gemm(MOE_KERNEL_ROUTE_LOGITS, MODE_ROW, true, EPI_F32, c, g, s);
   if (rc != MOE_OK) return rc;
   const float tau = c.route_margin > 0.0f ? c.route_margin : 1e-3f;
-  const RouteSmem L = route_smem(Epad, c.k, (int)sizeof(T));
+  const RouteSmem L = route_smem(Epad, c.k);
   const int grid = (int)ceil_div(c.T, kRW * kRT);
   MOE_LAUNCH(MOE_KERNEL_ROUTE, s,
-             route_kernel<T, NT, KL><<<grid, 256, L.total, s>>>(
-                 x, wrT, b, probs, idx, gate, c.T, c.d, c.E, Epad, c.k, tau));
+             route_kernel<T, KL><<<grid, 256, L.total, s>>>(
+                 zf, x, wrT, b, probs, idx, gate, wl.count, wl.tok, wl.n, wl.e, c.T, c.d,
+                 c.E, Epad, c.k, tau));
+  const int rgrid = (int)std::min<int64_t>(ceil_div(c.T, 4), 2048);
+  MOE_LAUNCH(MOE_KERNEL_ROUTE, s,
+             route_rescore_kernel<T><<<rgrid, 256, 0, s>>>(
+                 wl.count, wl.tok, wl.n, wl.e, zf, x, wrT, b, probs, idx, gate, c.d, c.E,
+                 Epad, c.k));
   return MOE_OK;
 }
 
-template <typename T, int NT>
+template <typename T>
 int route_kl(const moe_cfg& c, const T* x, const T* Wr, const float* b, float* probs,
-             int32_t* idx, float* gate, T* wrT, hipStream_t s) {
-  if (c.k <= 1) return launch_route_t<T, NT, 2>(c, x, Wr, b, probs, idx, gate, wrT, s);
-  if (c.k <= 2) return launch_route_t<T, NT, 3>(c, x, Wr, b, probs, idx, gate, wrT, s);
-  if (c.k <= 4) return launch_route_t<T, NT, 5>(c, x, Wr, b, probs, idx, gate, wrT, s);
-  if (c.k <= 8) return launch_route_t<T, NT, 9>(c, x, Wr, b, probs, idx, gate, wrT, s);
-  if (c.k <= 16) return launch_route_t<T, NT, 17>(c, x, Wr, b, probs, idx, gate, wrT, s);
-  return launch_route_t<T, NT, 33>(c, x, Wr, b, probs, idx, gate, wrT, s);
+             int32_t* idx, float* gate, T* wrT, float* zf, const RouteWorklist& wl,
+             hipStream_t s) {
+  if (c.k <= 1) return launch_route_t<T, 2>(c, x, Wr, b, probs, idx, gate, wrT, zf, wl, s);
+  if (c.k <= 2) return launch_route_t<T, 3>(c, x, Wr, b, probs, idx, gate, wrT, zf, wl, s);
+  if (c.k <= 4) return launch_route_t<T, 5>(c, x, Wr, b, probs, idx, gate, wrT, zf, wl, s);
+  if (c.k <= 8) return launch_route_t<T, 9>(c, x, Wr, b, probs, idx, gate, wrT, zf, wl, s);
+  if (c.k <= 16) return launch_route_t<T, 17>(c, x, Wr, b, probs, idx, gate, wrT, zf, wl, s);
+  return launch_route_t<T, 33>(c, x, Wr, b, probs, idx, gate, wrT, zf, wl, s);
 }
 
 }  // namespace
 
-int launch_transpose_wr(const moe_cfg& c, const void* Wr, void* wrT, hipStream_t s) {
+int launch_transpose_wr(const moe_cfg& c, const void* Wr, void* wrT, int* wl_count,
+                        hipStream_t s) {
   const int Epad = route_epad(c.E);
   const int64_t n = (int64_t)Epad * c.d;
   const int tgrid = (int)std::min<int64_t>(ceil_div(n, 256), 4096);
@@ -365,39 +323,35 @@ int launch_transpose_wr(const moe_cfg& c, const void* Wr, void* wrT, hipStream_t
     MOE_LAUNCH(MOE_KERNEL_ROUTE_PREP, s,
                transpose_wr_kernel<uint16_t><<<tgrid, 256, 0, s>>>(
                    static_cast<const uint16_t*>(Wr), static_cast<uint16_t*>(wrT), c.d, c.E,
-                   Epad));
+                   Epad, wl_count));
   else
     MOE_LAUNCH(MOE_KERNEL_ROUTE_PREP, s,
                transpose_wr_kernel<float><<<tgrid, 256, 0, s>>>(
-                   static_cast<const float*>(Wr), static_cast<float*>(wrT), c.d, c.E, Epad));
+                   static_cast<const float*>(Wr), static_cast<float*>(wrT), c.d, c.E, Epad,
+                   wl_count));
   return MOE_OK;
 }
 
-int route_smem_bytes(int E, int k, int elem) {
-  return (int)route_smem(route_epad(E), k, elem).total;
+int route_smem_bytes(int E, int k) {
+  return (int)route_smem(route_epad(E), k).total;
 }
 
 int launch_route(const moe_cfg& c, const void* x, const void* Wr, const float* b,
-                 float* probs, int32_t* idx, float* gate, void* wrT, hipStream_t s) {
+                 float* probs, int32_t* idx, float* gate, void* ws, hipStream_t s) {
   if (c.T == 0) return MOE_OK;
-  const int nt = (c.E + 31) / 32;
-  if (c.dtype == MOE_FP32) {
-    // VALU logits: only the LDS row stride depends on the padding
-    auto xf = static_cast<const float*>(x);
-    auto wf = static_cast<const float*>(Wr);
-    auto tf = static_cast<float*>(wrT);
-    if (nt <= 1) return route_kl<float, 1>(c, xf, wf, b, probs, idx, gate, tf, s);
-    if (nt <= 2) return route_kl<float, 2>(c, xf, wf, b, probs, idx, gate, tf, s);
-    if (nt <= 4) return route_kl<float, 4>(c, xf, wf, b, probs, idx, gate, tf, s);
-    return route_kl<float, 8>(c, xf, wf, b, probs, idx, gate, tf, s);
-  }
-  auto xb = static_cast<const uint16_t*>(x);
-  auto wb = static_cast<const uint16_t*>(Wr);
-  auto tb = static_cast<uint16_t*>(wrT);
-  if (nt <= 1) return route_kl<uint16_t, 1>(c, xb, wb, b, probs, idx, gate, tb, s);
-  if (nt <= 2) return route_kl<uint16_t, 2>(c, xb, wb, b, probs, idx, gate, tb, s);
-  if (nt <= 4) return route_kl<uint16_t, 4>(c, xb, wb, b, probs, idx, gate, tb, s);
-  return route_kl<uint16_t, 8>(c, xb, wb, b, probs, idx, gate, tb, s);
+  const WsLayout L = ws_layout(c);
+  RouteWorklist wl;
+  wl.count = ws_ptr<int>(ws, L.wl_count);
+  wl.tok = ws_ptr<int>(ws, L.wl_tok);
+  wl.n = ws_ptr<int>(ws, L.wl_n);
+  wl.e = ws_ptr<int>(ws, L.wl_e);
+  float* zf = ws_ptr<float>(ws, L.zf);
+  if (c.dtype == MOE_FP32)
+    return route_kl<float>(c, static_cast<const float*>(x), static_cast<const float*>(Wr), b,
+                           probs, idx, gate, ws_ptr<float>(ws, L.wrT), zf, wl, s);
+  return route_kl<uint16_t>(c, static_cast<const uint16_t*>(x),
+                            static_cast<const uint16_t*>(Wr), b, probs, idx, gate,
+                            ws_ptr<uint16_t>(ws, L.wrT), zf, wl, s);
 }
 
 }  // namespace moe

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
   for (int i = 0; i < 4; ++i) sdb[w][lane + 64 * i] = dbacc[i];
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256)
-    db_part[(int64_t)blockIdx.x * E + e] = (sdb[0][e] + sdb[1][e]) + (sdb[2][e] + sdb[3][e]);
+    db_part[(int64_t)e * gridDim.x + blockIdx.x] =
+        (sdb[0][e] + sdb[1][e]) + (sdb[2][e] + sdb[3][e]);
 }
 
 // wrp[i][e] = wrp[i][Ep + e] = Wr[i][e] (zero for E <= e < Ep)
@@ -91,7 +92,7 @@ __global__ void stack_wr_kernel(const uint16_t* __restrict__ Wr, uint16_t* __res
 }
 
 // dWr[i][e] = sum over chunks (fixed order) of part[c][i][e] (+ the low half)
-// and db[e] = sum over blocks of db_part[b][e]
+// and db[e] = sum over blocks of db_part[e][b]
 template <typename T>
 __global__ __launch_bounds__(256) void route_bwd_reduce_kernel(
     const float* __restrict__ part, const float* __restrict__ db_part, T* __restrict__ dWr,
@@ -118,19 +119,18 @@ __global__ __launch_bounds__(256) void route_bwd_reduce_kernel(
     }
     dWr[o] = St<T>::from_f(s);
   }
-  if (blockIdx.x == 0 && db != nullptr)
-    for (int e = threadIdx.x; e < E; e += 256) {
+  // db[e]: one wave per expert over its row of block partials (lane-strided
+  // fixed-order sums, then the fixed wave tree)
+  if (db != nullptr) {
+    const int lane = threadIdx.x & 63;
+    for (int e = blockIdx.x * 4 + (threadIdx.x >> 6); e < E; e += gridDim.x * 4) {
+      const float* row = db_part + (int64_t)e * nblk_dz;
       float s = 0.0f;
-      for (int b0 = 0; b0 < nblk_dz; b0 += 8) {
-        float v8[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          v8[q] = b0 + q < nblk_dz ? db_part[(int64_t)(b0 + q) * E + e] : 0.0f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) s += v8[q];
-      }
-      db[e] = s;
+      for (int b = lane; b < nblk_dz; b += kWave) s += row[b];
+      s = wave_sum(s);
+      if (lane == 0) db[e] = s;
     }
+  }
 }
 
 template <typename T>

@@ -114,7 +114,8 @@ const char* moe_last_error(void);
  * fast fp32 logits are used where the top-(k+1) gaps exceed
  * cfg->route_margin, and every logit that can change the decision is
  * recomputed in fp64 otherwise.  Workspace: ws of ws_bytes >=
- * moe_workspace_bytes(cfg) (holds a transposed copy of Wr). */
+ * moe_workspace_bytes(cfg) (holds a transposed copy of Wr and the fast
+ * logits). */
 int moe_route(const moe_cfg* cfg, const void* x, const void* Wr,
               const float* b, float* probs, int32_t* idx, float* gate,
               void* ws, size_t ws_bytes, moe_stream_t stream);
@@ -262,7 +263,7 @@ int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* x,
  * the number of launches recorded.  Process-wide state: not for use from
  * several threads at once.  Kernel ids: */
 typedef enum {
-  MOE_KERNEL_ROUTE = 0,
+  MOE_KERNEL_ROUTE = 0,          /* softmax, top-k, certification */
   MOE_KERNEL_PERMUTE_COUNT = 1,
   MOE_KERNEL_PERMUTE_SCAN = 2,
   MOE_KERNEL_PERMUTE_SCATTER = 3,
@@ -281,7 +282,8 @@ typedef enum {
   MOE_KERNEL_SCHEDULE = 16,
   MOE_KERNEL_ROUTE_PREP = 17,    /* router weight transpose / stacking */
   MOE_KERNEL_PERMUTE_COPY = 18,  /* x -> x_perm row copy */
-  MOE_KERNEL_COUNT_ = 19
+  MOE_KERNEL_ROUTE_LOGITS = 19,  /* fast router logits x Wr (GEMM) */
+  MOE_KERNEL_COUNT_ = 20
 } moe_kernel_id;
 
 int moe_prof_arm(int kernel_id, int max_launches);
