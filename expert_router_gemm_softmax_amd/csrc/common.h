@@ -117,6 +117,8 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 //                               canonical logits of the rescoring worklist
 //   wl_*                        router rescoring worklist: count, tokens [T],
 //                               candidate counts [T], candidates [T, Epad]
+//   gpart                       fp32 partial tiles of the grouped GEMMs'
+//                               split-K tail (bf16 storage)
 //   perm_blk [nblk_perm, E] i32 per-block expert histograms / bases
 //   tiles    [E+1] i32          grouped-GEMM M-tile prefix per expert
 //   dz       [T, E] f32         router logit gradient (float storage)
@@ -128,13 +130,16 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 //   dYp, dA, dXp                backward row gradients (Rmax rows, s)
 //   dxe      [T, d] f32         unpermute-sum of dXp (router backward)
 struct WsLayout {
-  size_t wrT, zf, wl_count, wl_tok, wl_n, wl_e, perm_blk, tiles, dz, dzb, wrp, dwr_part, db_part, dgate, dYp, dA, dXp, dxe, total;
+  size_t wrT, zf, wl_count, wl_tok, wl_n, wl_e, gpart, perm_blk, tiles, dz, dzb, wrp, dwr_part, db_part, dgate, dYp, dA, dXp, dxe, total;
   int nblk_perm;
   int nblk_dz;
   int dwr_chunks, dwr_chunk, dwr_n;
 };
 
 constexpr int kPermTokens = 256;  // tokens per permute block
+// fp32 partial tiles of the grouped GEMM's split-K tail: at most one tile
+// per CU (256) of up to 256 x 256
+constexpr size_t kGemmPartFloats = (size_t)256 * 256 * 256;
 constexpr int kDzTokens = 16;     // tokens per router-backward dz block
 
 inline int64_t rows_max(const moe_cfg& c) {
@@ -184,6 +189,7 @@ inline WsLayout ws_layout(const moe_cfg& c) {
   L.wl_tok = take((size_t)c.T * 4);
   L.wl_n = take((size_t)c.T * 4);
   L.wl_e = take((size_t)c.T * route_epad(c.E) * 4);
+  L.gpart = take(c.dtype == MOE_BF16 ? kGemmPartFloats * 4 : 0);
   L.perm_blk = take((size_t)L.nblk_perm * c.E * 4);
   L.tiles = take((size_t)(c.E + 1) * 4 * 4);
   L.dz = take(bf ? 0 : (size_t)c.T * c.E * 4);
@@ -212,6 +218,17 @@ void note_launch_error(int kernel_id, hipError_t e);
 
 // Launch, then check that launch.  Entry points clear any error state left
 // by earlier, unrelated HIP calls of the process before their first launch.
+// A launch whose timing belongs to an enclosing prof_begin/prof_end pair.
+#define MOE_LAUNCH_NP(kid, ...)                                       \
+  do {                                                                \
+    __VA_ARGS__;                                                      \
+    hipError_t e_ = hipGetLastError();                                \
+    if (e_ != hipSuccess) {                                           \
+      ::moe::note_launch_error((kid), e_);                            \
+      return MOE_ERR_LAUNCH;                                          \
+    }                                                                 \
+  } while (0)
+
 #define MOE_LAUNCH(kid, stream, ...)                                  \
   do {                                                                \
     ::moe::prof_begin((kid), (stream));                               \

@@ -33,6 +33,9 @@ struct GemmArgs {
   int64_t c_estride;     // KRAG: elements between groups' C
   int bm, bn;            // ROW one-group problems with K-contiguous B and an
                          // fp32 epilogue: block tile (64 or 128 each); 0 = auto
+  float* part;           // ROW, bf16: workspace for the split-K tail (fp32
+                         // partial tiles, kGemmPartFloats); nullptr = no split
+  int slots;             // filled by the launcher: concurrent blocks per round
   int ntn, ntm;          // filled by the launcher
 };
 

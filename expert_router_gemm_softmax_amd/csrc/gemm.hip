@@ -26,6 +26,7 @@
 namespace moe {
 
 constexpr int kGroupM = 4;  // M tiles per traversal group
+constexpr int BK_ALL = 32;  // K tile of the bf16 kernels
 
 namespace {
 
@@ -53,48 +54,56 @@ __device__ __forceinline__ void group_mn(int lid, int num_m, int ntn, int& mt, i
 struct Tile {
   int e, m0, n0, M, K;
   int64_t row0;  // ROW: first row of the expert; KRAG: first K row
+  int kofs;      // split-K part: first K element of the part (0 otherwise)
 };
 
-template <int MODE, int BM, int BN>
-__device__ __forceinline__ bool decode_tile(const GemmArgs& g, int* s_tiles, Tile& t) {
+// Number of output tiles (and of M tiles for ROW).  ROW problems with a
+// schedule load it into s_tiles (block-wide, synchronising).
+template <int MODE, int BM>
+__device__ __forceinline__ int tile_count(const GemmArgs& g, int* s_tiles, int& num_m) {
   if constexpr (MODE == MODE_ROW) {
+    if (!g.offsets) {
+      num_m = (g.M + BM - 1) / BM;
+    } else {
+      for (int i = threadIdx.x; i <= g.E; i += blockDim.x) s_tiles[i] = g.tiles[i];
+      __syncthreads();
+      num_m = s_tiles[g.E];
+    }
+    return num_m * g.ntn;
+  } else {
+    num_m = g.ntm;
+    return g.E * g.ntm * g.ntn;
+  }
+}
+
+// Logical tile lid -> tile.
+template <int MODE, int BM, int BN>
+__device__ __forceinline__ void tile_of(const GemmArgs& g, const int* s_tiles, int num_m, int lid,
+                                        Tile& t) {
+  t.kofs = 0;
+  if constexpr (MODE == MODE_ROW) {
+    int mt, nt;
+    group_mn(lid, num_m, g.ntn, mt, nt);
     if (!g.offsets) {  // one group of g.M rows
-      const int num_m = (g.M + BM - 1) / BM;
-      int lid;
-      if (!xcd_logical(num_m * g.ntn, lid)) return false;
-      int mt, nt;
-      group_mn(lid, num_m, g.ntn, mt, nt);
       t.e = 0;
       t.row0 = 0;
       t.M = g.M;
       t.m0 = mt * BM;
-      t.n0 = nt * BN;
-      t.K = g.K;
-      return true;
+    } else {
+      int lo = 0, hi = g.E - 1;  // last e with s_tiles[e] <= mt
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tiles[mid] <= mt) lo = mid; else hi = mid - 1;
+      }
+      t.e = lo;
+      t.row0 = g.offsets[lo];
+      t.M = g.offsets[lo + 1] - (int)t.row0;
+      t.m0 = (mt - s_tiles[lo]) * BM;
     }
-    for (int i = threadIdx.x; i <= g.E; i += blockDim.x) s_tiles[i] = g.tiles[i];
-    __syncthreads();
-    const int num_m = s_tiles[g.E];
-    int lid;
-    if (!xcd_logical(num_m * g.ntn, lid)) return false;
-    int mt, nt;
-    group_mn(lid, num_m, g.ntn, mt, nt);
-    int lo = 0, hi = g.E - 1;  // last e with s_tiles[e] <= mt
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_tiles[mid] <= mt) lo = mid; else hi = mid - 1;
-    }
-    t.e = lo;
-    t.row0 = g.offsets[lo];
-    t.M = g.offsets[lo + 1] - (int)t.row0;
-    t.m0 = (mt - s_tiles[lo]) * BM;
     t.n0 = nt * BN;
     t.K = g.K;
-    return true;
   } else {
     const int per_e = g.ntm * g.ntn;
-    int lid;
-    if (!xcd_logical(g.E * per_e, lid)) return false;
     t.e = lid / per_e;
     int mt, nt;
     group_mn(lid - t.e * per_e, g.ntm, g.ntn, mt, nt);
@@ -108,8 +117,118 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, int* s_tiles, Til
     t.M = g.M;
     t.m0 = mt * BM;
     t.n0 = nt * BN;
-    return true;
   }
+}
+
+// Split-K tail of ROW problems.  Tiles run in full rounds of one tile per
+// CU (g.slots = 256); the rem tiles of the last, partial round are each
+// split into sp parts along K (sp = slots / rem, at most the number of K
+// tiles), so that every CU ends with the same share of work.  The parts
+// write fp32 partial tiles that gemm_fixup_kernel sums in part order.
+struct Split {
+  int full, rem, sp;
+};
+template <int MODE>
+__device__ __forceinline__ Split split_of(const GemmArgs& g, int ntotal) {
+  Split p{ntotal, 0, 1};
+  if constexpr (MODE == MODE_ROW) {
+    if (g.part != nullptr && g.slots > 0) {
+      const int full = ntotal / g.slots * g.slots;
+      const int rem = ntotal - full;
+      const int nkt = (g.K + BK_ALL - 1) / BK_ALL;
+      int sp = rem > 0 ? g.slots / rem : 1;
+      if (sp > nkt) sp = nkt;
+      if (sp > 1) p = Split{full, rem, sp};
+    }
+  }
+  return p;
+}
+
+// This block's work: a whole tile (part < 0) or one K part of a tail tile.
+// Whole tiles take the first block ids and the parts the ids after them,
+// each range dealt XCD-contiguously, so that with blocks dispatched in id
+// order every CU receives the same mix of whole tiles and parts.
+template <int MODE, int BM, int BN>
+__device__ __forceinline__ bool decode_work(const GemmArgs& g, int* s_tiles, Tile& t, int& part,
+                                            int& pid) {
+  int num_m;
+  const int ntotal = tile_count<MODE, BM>(g, s_tiles, num_m);
+  const Split sp = split_of<MODE>(g, ntotal);
+  const int per_full = (sp.full + 7) >> 3;
+  const int bid = blockIdx.x;
+  part = -1;
+  pid = 0;
+  int lid;
+  if (bid < 8 * per_full) {
+    lid = (bid & 7) * per_full + (bid >> 3);
+    if (lid >= sp.full) return false;
+  } else {
+    const int nparts = sp.rem * sp.sp;
+    const int per_part = (nparts + 7) >> 3;
+    const int b2 = bid - 8 * per_full;
+    if ((b2 >> 3) >= per_part) return false;
+    const int u = (b2 & 7) * per_part + (b2 >> 3);
+    if (u >= nparts) return false;
+    lid = sp.full + u / sp.sp;
+    part = u % sp.sp;
+    pid = u;
+  }
+  tile_of<MODE, BM, BN>(g, s_tiles, num_m, lid, t);
+  if (part >= 0) {
+    const int nkt = (t.K + BK_ALL - 1) / BK_ALL;
+    const int per = (nkt + sp.sp - 1) / sp.sp;
+    const int kb = min(part * per, nkt), ke = min(kb + per, nkt);
+    t.kofs = kb * BK_ALL;
+    t.K = min(t.K, ke * BK_ALL) - t.kofs;  // may be 0: the part writes zeros
+  }
+  return true;
+}
+
+// Epilogue of 8 consecutive outputs of one row at element offset o.
+template <int EPI>
+__device__ __forceinline__ void epi_write8(const GemmArgs& g, int64_t o, float (&v8)[8]) {
+  if constexpr (EPI == EPI_F32) {
+    float* C = static_cast<float*>(g.C) + o;
+    *reinterpret_cast<f32x4*>(C) = *reinterpret_cast<const f32x4*>(v8);
+    *reinterpret_cast<f32x4*>(C + 4) = *reinterpret_cast<const f32x4*>(v8 + 4);
+  } else if constexpr (EPI == EPI_STORE) {
+    st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
+  } else if constexpr (EPI == EPI_GELU) {
+    const u32x4 ab = St<uint16_t>::pack(v8);
+    st16(static_cast<uint16_t*>(g.C) + o, ab);
+    float a8[8];
+    St<uint16_t>::unpack(ab, a8);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a8[q] = gelu_tanh(a8[q]);
+    st16(static_cast<uint16_t*>(g.C2) + o, St<uint16_t>::pack(a8));
+  } else if constexpr (EPI == EPI_ADDF32) {
+    const float* ad = static_cast<const float*>(g.Aux) + o;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(ad);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(ad + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v8[q] += a0[q];
+      v8[q + 4] += a1[q];
+    }
+    st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
+  } else {
+    float x8[8];
+    St<uint16_t>::unpack(ld16(static_cast<const uint16_t*>(g.Aux) + o), x8);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v8[q] *= gelu_tanh_grad(x8[q]);
+    st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
+  }
+}
+
+// Non-split problems (KRAG, fp32 storage): one block per tile.
+template <int MODE, int BM, int BN>
+__device__ __forceinline__ bool decode_tile(const GemmArgs& g, int* s_tiles, Tile& t) {
+  int num_m;
+  const int ntotal = tile_count<MODE, BM>(g, s_tiles, num_m);
+  int lid;
+  if (!xcd_logical(ntotal, lid)) return false;
+  tile_of<MODE, BM, BN>(g, s_tiles, num_m, lid, t);
+  return true;
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
@@ -126,8 +245,11 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, int* s_tiles, Til
 // Rows (KC) or column chunks (MN) past the tile's M or N edge are clamped
 // to the last valid one; they only feed outputs that are never stored.  A
 // final partial K tile goes through registers with zero fill.
-constexpr int BK = 32;
-constexpr int kStages = 4;
+constexpr int BK = BK_ALL;
+// stages of the ring: 4 for the 256 x 256 tile (1 block per CU); 3 for
+// smaller tiles, so that three blocks fit a CU's LDS
+template <int BM, int BN>
+constexpr int ring_stages() { return BM * BN >= 256 * 256 ? 4 : 3; }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
@@ -229,20 +351,24 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   using OpA = Operand<A_KC, BM>;
   using OpB = Operand<BKC, BN>;
   constexpr int kStageElems = OpA::kElems + OpB::kElems;
+  constexpr int kStages = ring_stages<BM, BN>();
   // the operand ring; reused as the epilogue staging area
   __shared__ __align__(16) uint16_t smem[kStages * kStageElems];
   __shared__ int s_tiles[MODE == MODE_ROW ? 257 : 1];
 
   Tile t;
-  if (!decode_tile<MODE, BM, BN>(g, s_tiles, t)) return;
+  int part, pid;
+  if (!decode_work<MODE, BM, BN>(g, s_tiles, t, part, pid)) return;
   if constexpr (MODE == MODE_ROW) {
     if (t.m0 >= t.M) return;
   }
 
-  const uint16_t* A = static_cast<const uint16_t*>(g.A) + t.row0 * g.lda;
+  // operand origins, advanced to the first K element of a split part
+  const uint16_t* A = static_cast<const uint16_t*>(g.A) + t.row0 * g.lda + t.kofs;
   const uint16_t* B;
   if constexpr (MODE == MODE_ROW)
-    B = static_cast<const uint16_t*>(g.B) + (int64_t)t.e * g.b_estride;
+    B = static_cast<const uint16_t*>(g.B) + (int64_t)t.e * g.b_estride +
+        (BKC ? (int64_t)t.kofs : (int64_t)t.kofs * g.ldb);
   else
     B = static_cast<const uint16_t*>(g.B) + t.row0 * g.ldb;
 
@@ -367,6 +493,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   int64_t cbase;
   if constexpr (MODE == MODE_ROW) cbase = t.row0 * g.ldc;
   else cbase = (int64_t)t.e * g.c_estride;
+  float* ptile = part >= 0 ? g.part + (int64_t)pid * BM * BN : nullptr;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -378,48 +505,54 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int p = 0; p < 32 / RPP; ++p) {
       const int rl = p * RPP + lane / LPR, cl = (lane % LPR) * 8;
-      const int row = t.m0 + wm * WM + i * 32 + rl;
-      const int col = t.n0 + wn * WN + cl;
-      if (row < t.M && col < g.N) {
-        float v8[8];
-        *reinterpret_cast<f32x4*>(v8) = *reinterpret_cast<const f32x4*>(stage + rl * SP + cl);
-        *reinterpret_cast<f32x4*>(v8 + 4) =
-            *reinterpret_cast<const f32x4*>(stage + rl * SP + cl + 4);
-        const int64_t o = cbase + (int64_t)row * g.ldc + col;
-        if constexpr (EPI == EPI_F32) {
-          float* C = static_cast<float*>(g.C) + o;
-          *reinterpret_cast<f32x4*>(C) = *reinterpret_cast<const f32x4*>(v8);
-          *reinterpret_cast<f32x4*>(C + 4) = *reinterpret_cast<const f32x4*>(v8 + 4);
-        } else if constexpr (EPI == EPI_STORE) {
-          st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
-        } else if constexpr (EPI == EPI_GELU) {
-          const u32x4 ab = St<uint16_t>::pack(v8);
-          st16(static_cast<uint16_t*>(g.C) + o, ab);
-          float a8[8];
-          St<uint16_t>::unpack(ab, a8);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) a8[q] = gelu_tanh(a8[q]);
-          st16(static_cast<uint16_t*>(g.C2) + o, St<uint16_t>::pack(a8));
-        } else if constexpr (EPI == EPI_ADDF32) {
-          const float* ad = static_cast<const float*>(g.Aux) + o;
-          const f32x4 a0 = *reinterpret_cast<const f32x4*>(ad);
-          const f32x4 a1 = *reinterpret_cast<const f32x4*>(ad + 4);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v8[q] += a0[q];
-            v8[q + 4] += a1[q];
-          }
-          st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
-        } else {
-          float x8[8];
-          St<uint16_t>::unpack(ld16(static_cast<const uint16_t*>(g.Aux) + o), x8);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) v8[q] *= gelu_tanh_grad(x8[q]);
-          st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
-        }
+      float v8[8];
+      *reinterpret_cast<f32x4*>(v8) = *reinterpret_cast<const f32x4*>(stage + rl * SP + cl);
+      *reinterpret_cast<f32x4*>(v8 + 4) = *reinterpret_cast<const f32x4*>(stage + rl * SP + cl + 4);
+      const int tr = wm * WM + i * 32 + rl, tc = wn * WN + cl;  // in the tile
+      if (ptile) {  // split part: the whole fp32 tile, unmasked
+        float* q = ptile + tr * BN + tc;
+        *reinterpret_cast<f32x4*>(q) = *reinterpret_cast<const f32x4*>(v8);
+        *reinterpret_cast<f32x4*>(q + 4) = *reinterpret_cast<const f32x4*>(v8 + 4);
+      } else {
+        const int row = t.m0 + tr, col = t.n0 + tc;
+        if (row < t.M && col < g.N) epi_write8<EPI>(g, cbase + (int64_t)row * g.ldc + col, v8);
       }
     }
     __syncthreads();
+  }
+}
+
+// Sums the split-K parts of the tail tiles (in part order) and applies the
+// epilogue; a no-op when the problem had no split tail.
+template <int EPI, int BM, int BN>
+__global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
+  __shared__ int s_tiles[257];
+  int num_m;
+  const int ntotal = tile_count<MODE_ROW, BM>(g, s_tiles, num_m);
+  const Split sp = split_of<MODE_ROW>(g, ntotal);
+  if (sp.sp <= 1) return;
+  constexpr int CPR = BN / 8;  // 8-column chunks per tile row
+  const int64_t items = (int64_t)sp.rem * BM * CPR;
+  for (int64_t it = blockIdx.x * 256 + threadIdx.x; it < items; it += (int64_t)gridDim.x * 256) {
+    const int i = (int)(it / (BM * CPR));
+    const int in = (int)(it - (int64_t)i * BM * CPR);
+    const int tr = in / CPR, tc = (in % CPR) * 8;
+    Tile t;
+    tile_of<MODE_ROW, BM, BN>(g, s_tiles, num_m, sp.full + i, t);
+    const int row = t.m0 + tr, col = t.n0 + tc;
+    if (row >= t.M || col >= g.N) continue;
+    float v8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const float* q = g.part + ((int64_t)i * sp.sp) * BM * BN + tr * BN + tc;
+    for (int p = 0; p < sp.sp; ++p, q += BM * BN) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(q);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(q + 4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v8[u] += a[u];
+        v8[u + 4] += b[u];
+      }
+    }
+    epi_write8<EPI>(g, t.row0 * g.ldc + (int64_t)row * g.ldc + col, v8);
   }
 }
 
@@ -568,6 +701,17 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
     nblk = (int64_t)g.E * g.ntm * g.ntn;
   }
   if (nblk == 0) return MOE_OK;
+  if constexpr (MODE == MODE_ROW) {
+    // split-K tail for the bf16 kernels: whole tiles, then up to one block
+    // per CU for the parts
+    if (bf && g.part != nullptr && (BM == 256 || BM == 128) && BN == BM) {
+      g.slots = 256;  // CUs
+      nblk = grid8(nblk) + g.slots;
+    } else {
+      g.part = nullptr;
+      g.slots = 0;
+    }
+  }
   const int grid = grid8(nblk);
   if (!bf) {
     MOE_LAUNCH(kid, s, gemm_f32_kernel<MODE, B_KC, EPI><<<grid, 256, 0, s>>>(g));
@@ -583,6 +727,22 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
     else
       MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 128, 128><<<grid, 256, 0, s>>>(g));
     return MOE_OK;
+  }
+  if constexpr (MODE == MODE_ROW) {
+    if (g.part != nullptr) {
+      // the GEMM and its tail fixup are timed as one launch
+      const int fgrid = (int)std::min<int64_t>(ceil_div((int64_t)g.slots * BM * BN / 8, 256), 2048);
+      prof_begin(kid, s);
+      if (BM == 256) {
+        MOE_LAUNCH_NP(kid, gemm_bf16_kernel<MODE, B_KC, EPI, 256, 256><<<grid, 256, 0, s>>>(g));
+        MOE_LAUNCH_NP(kid, gemm_fixup_kernel<EPI, 256, 256><<<fgrid, 256, 0, s>>>(g));
+      } else {
+        MOE_LAUNCH_NP(kid, gemm_bf16_kernel<MODE, B_KC, EPI, 128, 128><<<grid, 256, 0, s>>>(g));
+        MOE_LAUNCH_NP(kid, gemm_fixup_kernel<EPI, 128, 128><<<fgrid, 256, 0, s>>>(g));
+      }
+      prof_end(kid, s);
+      return MOE_OK;
+    }
   }
   if (BM == 256)
     MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 256, 256><<<grid, 256, 0, s>>>(g));
@@ -637,6 +797,7 @@ int launch_ffn_fwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
   g.offsets = offsets;
   g.tiles = tiles;
   g.E = c.E;
+  g.part = ws_ptr<float>(ws, L.gpart);
   // A = x_perm W1 ; H = gelu(A)
   g.A = x_perm; g.B = W1; g.C = A; g.C2 = H;
   g.N = c.f; g.K = c.d; g.lda = c.d; g.ldb = c.f; g.ldc = c.f;
@@ -662,6 +823,7 @@ int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
   g.offsets = offsets;
   g.tiles = tiles;
   g.E = c.E;
+  g.part = ws_ptr<float>(ws, L.gpart);
   if (rows_max(c) > 0) {
     rc = schedule(c, offsets, tiles, s);
     if (rc != MOE_OK) return rc;
@@ -679,6 +841,7 @@ int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
     if (rc != MOE_OK) return rc;
   }
   // dW2[e] = H_e^T dYp_e : M = f, N = d
+  g.part = nullptr;
   g.A = H; g.B = dYp; g.C = dW2; g.Aux = nullptr;
   g.M = c.f; g.N = c.d; g.lda = c.f; g.ldb = c.d; g.ldc = c.d;
   g.c_estride = (int64_t)c.f * c.d;
