@@ -123,7 +123,8 @@ __device__ __forceinline__ void tile_of(const GemmArgs& g, const int* s_tiles, i
 // Split-K tail of ROW problems.  Tiles run in full rounds of one tile per
 // CU (g.slots = 256); the rem tiles of the last, partial round are each
 // split into sp parts along K (sp = slots / rem, at most the number of K
-// tiles), so that every CU ends with the same share of work.  The parts
+// tiles; no split below 3 parts), so that every CU ends with about the same
+// share of work.  The parts
 // write fp32 partial tiles that gemm_fixup_kernel sums in part order.
 struct Split {
   int full, rem, sp;
@@ -138,7 +139,8 @@ __device__ __forceinline__ Split split_of(const GemmArgs& g, int ntotal) {
       const int nkt = (g.K + BK_ALL - 1) / BK_ALL;
       int sp = rem > 0 ? g.slots / rem : 1;
       if (sp > nkt) sp = nkt;
-      if (sp > 1) p = Split{full, rem, sp};
+      // halves do not repay the partial-tile traffic and the fixup
+      if (sp >= 3) p = Split{full, rem, sp};
     }
   }
   return p;
