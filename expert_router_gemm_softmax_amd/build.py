@@ -8,7 +8,9 @@ exist yet)
 Each csrc/*.hip is compiled by hipcc for --offload-arch=gfx950 into
 _build/ at the repository root, then linked into
 expert_router_gemm_softmax_amd/libmoe.so.  hipcc cross-compiles without a
-GPU.  Packed fp32 VALU ops are disabled for the device code.
+GPU.  Packed fp32 VALU ops are disabled for the device code.  Symbols are
+hidden by default: the library exports only the C entry points of
+include/moe.h.
 """
 from __future__ import annotations
 
@@ -30,7 +32,7 @@ SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm.hip", "combine.hip",
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
-CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
 

@@ -9,18 +9,19 @@ namespace moe {
 namespace {
 
 constexpr int kCW = 4;   // waves per block
-constexpr int kCPL = 8;  // 16-byte chunks per lane in one pass over a row
+constexpr int kCPL = 8;     // 16-byte chunks per lane in one pass over a row
+constexpr int kBwdCPL = 4;  // the same for combine backward (fewer registers)
 
 // Loads the chunks of one pass (chunk c = g0 + s*64 + lane) of row r of src
 // into v; chunks past the row end, and every chunk of a dropped row
 // (r < 0), are not loaded.
-template <typename T>
+template <typename T, int CPL>
 __device__ __forceinline__ void load_pass(const T* __restrict__ src, int64_t r, int d, int g0,
-                                          int nch, int lane, u32x4 (&v)[kCPL]) {
+                                          int nch, int lane, u32x4 (&v)[CPL]) {
   constexpr int V = St<T>::kVec;
   if (r < 0) return;
 #pragma unroll
-  for (int s = 0; s < kCPL; ++s) {
+  for (int s = 0; s < CPL; ++s) {
     const int c = g0 + s * kWave + lane;
     if (c < nch) v[s] = ld16(src + r * d + c * V);
   }
@@ -99,13 +100,13 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
        t += (int64_t)gridDim.x * kCW) {
     const int32_t* rows = row_of + t * k;
     float mine = 0.0f;  // lane j < k: dgate[t, j]
-    for (int g0 = 0; g0 < nch; g0 += kWave * kCPL) {
-      u32x4 gv[kCPL];
+    for (int g0 = 0; g0 < nch; g0 += kWave * kBwdCPL) {
+      u32x4 gv[kBwdCPL];
       load_pass(dOut, t, d, g0, nch, lane, gv);
       for (int j = 0; j < k; j += 2) {
         const int32_t r0 = rows[j];
         const int32_t r1 = j + 1 < k ? rows[j + 1] : -1;
-        u32x4 y0[kCPL], y1[kCPL];
+        u32x4 y0[kBwdCPL], y1[kBwdCPL];
         load_pass(Y, r0, d, g0, nch, lane, y0);
         load_pass(Y, r1, d, g0, nch, lane, y1);
 #pragma unroll
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
           const float gj = gate[t * k + j + h];
           float pp = 0.0f;
 #pragma unroll
-          for (int s = 0; s < kCPL; ++s) {
+          for (int s = 0; s < kBwdCPL; ++s) {
             const int c = g0 + s * kWave + lane;
             if (c >= nch) continue;
             float g[V], y[V], o[V];

@@ -39,6 +39,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* The library is built with hidden visibility; only these entry points are
+ * exported. */
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -80,25 +88,25 @@ typedef struct moe_cfg {
  * integer, so decimal factors such as 1.1 are not pushed up by binary
  * rounding.  cf < 0 returns MOE_NO_CAPACITY.
  * Distributed-training tutorial, section "The Capacity Factor". */
-int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double cf);
+MOE_API int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double cf);
 
 /* Rmax = min(T*k, E*C) (T*k without a capacity); -1 on invalid cfg. */
-int64_t moe_rows_max(const moe_cfg* cfg);
+MOE_API int64_t moe_rows_max(const moe_cfg* cfg);
 
 /* Bytes of device workspace that any entry point taking `ws` needs for
  * this cfg (the layer entry points need the most; one buffer of this size
  * serves all of them).  0 on invalid cfg. */
-size_t moe_workspace_bytes(const moe_cfg* cfg);
+MOE_API size_t moe_workspace_bytes(const moe_cfg* cfg);
 
 /* Human-readable text of a moe_status (static storage). */
-const char* moe_status_str(int status);
+MOE_API const char* moe_status_str(int status);
 
 /* Validates cfg alone (the checks every entry point starts with). */
-int moe_check_cfg(const moe_cfg* cfg);
+MOE_API int moe_check_cfg(const moe_cfg* cfg);
 
 /* Text naming the kernel and HIP error of this thread's last
  * MOE_ERR_LAUNCH ("" if none since the last entry-point call). */
-const char* moe_last_error(void);
+MOE_API const char* moe_last_error(void);
 
 /* ---------------------------------------------------------------- forward */
 
@@ -116,7 +124,7 @@ const char* moe_last_error(void);
  * recomputed in fp64 otherwise.  Workspace: ws of ws_bytes >=
  * moe_workspace_bytes(cfg) (holds a transposed copy of Wr and the fast
  * logits). */
-int moe_route(const moe_cfg* cfg, const void* x, const void* Wr,
+MOE_API int moe_route(const moe_cfg* cfg, const void* x, const void* Wr,
               const float* b, float* probs, int32_t* idx, float* gate,
               void* ws, size_t ws_bytes, moe_stream_t stream);
 
@@ -132,7 +140,7 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* Wr,
  *   src_of  [Rmax] int32 t*k + j of the assignment in each row
  *   x_perm  [Rmax,d] s   x_perm[r] = x[src_of[r] / k] (bitwise copy)
  * Workspace: ws of ws_bytes >= moe_workspace_bytes(cfg). */
-int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx,
+MOE_API int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx,
                 int32_t* counts, int32_t* offsets, int32_t* row_of,
                 int32_t* src_of, void* x_perm, void* ws, size_t ws_bytes,
                 moe_stream_t stream);
@@ -146,7 +154,7 @@ int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx,
  *   Y = H W2[e]           [Rmax,d] s
  * W1 [E,d,f] s, W2 [E,f,d] s.  offsets lives on the device and is never
  * read back by the host.  Workspace as above. */
-int moe_grouped_ffn(const moe_cfg* cfg, const void* x_perm,
+MOE_API int moe_grouped_ffn(const moe_cfg* cfg, const void* x_perm,
                     const int32_t* offsets, const void* W1, const void* W2,
                     void* A, void* H, void* Y, void* ws, size_t ws_bytes,
                     moe_stream_t stream);
@@ -156,7 +164,7 @@ int moe_grouped_ffn(const moe_cfg* cfg, const void* x_perm,
  *   out[t] = sum over kept j (ascending) of gate[t,j] * Y[row_of[t,j]],
  * fp32 accumulation, one rounding to s; 0 for a token with every
  * assignment dropped.  out [T,d] s. */
-int moe_combine(const moe_cfg* cfg, const void* Y, const int32_t* row_of,
+MOE_API int moe_combine(const moe_cfg* cfg, const void* Y, const int32_t* row_of,
                 const float* gate, void* out, moe_stream_t stream);
 
 /* --------------------------------------------------------------- backward
@@ -168,7 +176,7 @@ int moe_combine(const moe_cfg* cfg, const void* Y, const int32_t* row_of,
  *   dYp[row_of[t,j]] = RN_s(gate[t,j] * dOut[t])  [Rmax,d] s
  *   dgate[t,j]       = <dOut[t], Y[row_of[t,j]]>  [T,k] float (0 if dropped)
  */
-int moe_combine_bwd(const moe_cfg* cfg, const void* dOut, const void* Y,
+MOE_API int moe_combine_bwd(const moe_cfg* cfg, const void* dOut, const void* Y,
                     const int32_t* row_of, const float* gate, void* dYp,
                     float* dgate, moe_stream_t stream);
 
@@ -183,7 +191,7 @@ int moe_combine_bwd(const moe_cfg* cfg, const void* dOut, const void* Y,
  * data-parallel group ("Two gradient reductions over two different
  * groups"); that reduction spans GPUs and is the caller's.  Workspace as
  * above. */
-int moe_grouped_ffn_bwd(const moe_cfg* cfg, const void* x_perm,
+MOE_API int moe_grouped_ffn_bwd(const moe_cfg* cfg, const void* x_perm,
                         const int32_t* offsets, const void* W1,
                         const void* W2, const void* A, const void* H,
                         const void* dYp, void* dXp, void* dW1, void* dW2,
@@ -191,7 +199,7 @@ int moe_grouped_ffn_bwd(const moe_cfg* cfg, const void* x_perm,
 
 /* B2 inverse of the permute for gradients:
  *   dXe[t] = sum over kept j of dXp[row_of[t,j]]   [T,d] float */
-int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp,
+MOE_API int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp,
                       const int32_t* row_of, float* dXe, moe_stream_t stream);
 
 /* B1 router backward (the router is a shared parameter with an ordinary
@@ -202,7 +210,7 @@ int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp,
  *   dWr = x^T dz                         [d,E] s
  *   dX  = sum_{kept j} dXp[row_of[t,j]] + dz Wr^T   [T,d] s
  * (the unpermute-sum of B2 is fused in).  Workspace as above. */
-int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr,
+MOE_API int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr,
                   const float* probs, const int32_t* idx,
                   const int32_t* row_of, const float* dgate, const void* dXp,
                   void* dX, void* dWr, float* db, void* ws, size_t ws_bytes,
@@ -244,14 +252,14 @@ typedef struct moe_grads {
 
 /* Forward of the layer: moe_route, moe_permute, moe_grouped_ffn and
  * moe_combine in sequence on `stream`; out [T,d] s. */
-int moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const void* x,
+MOE_API int moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const void* x,
                   void* out, const moe_ctx* ctx, void* ws, size_t ws_bytes,
                   moe_stream_t stream);
 
 /* Backward of the layer from the saved ctx: moe_combine_bwd,
  * moe_grouped_ffn_bwd and moe_route_bwd (dYp, dA, dXp and dgate live in
  * the workspace); dX [T,d] s. */
-int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* x,
+MOE_API int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* x,
                   const void* dOut, const moe_ctx* ctx, void* dX,
                   const moe_grads* g, void* ws, size_t ws_bytes,
                   moe_stream_t stream);
@@ -286,8 +294,8 @@ typedef enum {
   MOE_KERNEL_COUNT_ = 20
 } moe_kernel_id;
 
-int moe_prof_arm(int kernel_id, int max_launches);
-int moe_prof_read(float* total_ms, int* launches);
+MOE_API int moe_prof_arm(int kernel_id, int max_launches);
+MOE_API int moe_prof_read(float* total_ms, int* launches);
 
 #ifdef __cplusplus
 }

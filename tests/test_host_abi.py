@@ -33,6 +33,22 @@ def test_library_exports_every_declared_function(repo_root):
     assert set(names) <= set(B._SIGS), set(names) - set(B._SIGS)
 
 
+def test_library_exports_only_the_c_entry_points(repo_root):
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", M.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    funcs = sorted({ln.split()[-1] for ln in out.splitlines()
+                    if len(ln.split()) == 3 and ln.split()[1] in ("T", "W")})
+    declared = set(_declared_functions(repo_root))
+    extra = [f for f in funcs if f not in declared and not f.startswith("_init")
+             and not f.startswith("_fini")]
+    assert not extra, extra
+
+
 def test_library_is_in_tree_and_for_gfx950(repo_root):
     assert os.path.dirname(M.LIB_PATH) == os.path.join(repo_root,
                                                         "expert_router_gemm_softmax_amd")
