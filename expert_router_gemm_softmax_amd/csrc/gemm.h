@@ -32,7 +32,8 @@ struct GemmArgs {
   int64_t b_estride;     // ROW: elements between experts' B
   int64_t c_estride;     // KRAG: elements between groups' C
   int bm, bn;            // ROW one-group problems with K-contiguous B and an
-                         // fp32 epilogue: block tile (64 or 128 each); 0 = auto
+                         // fp32 or fp32-add epilogue: block tile (64 or 128
+                         // each for fp32, 128 x 128 for fp32-add); 0 = auto
   float* part;           // ROW, bf16: workspace for the split-K tail (fp32
                          // partial tiles, kGemmPartFloats); nullptr = no split
   int slots;             // filled by the launcher: concurrent blocks per round

@@ -687,9 +687,9 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
     // one-group problems choose freely; grouped ones follow the schedule
     BM = g.offsets ? row_bm(c) : (use_big_tile(c, MODE_KRAG, g.M, g.N, 1) ? 256 : 128);
     BN = BM;
-    if constexpr (B_KC && EPI == EPI_F32) {
-      if (g.bm) BM = g.bm;
-      if (g.bn) BN = g.bn;
+    if constexpr (B_KC && (EPI == EPI_F32 || EPI == EPI_ADDF32)) {
+      if (!g.offsets && g.bm) BM = g.bm;
+      if (!g.offsets && g.bn) BN = g.bn;
     }
   } else {
     BM = BN = use_big_tile(c, MODE_KRAG, g.M, g.N, g.E) ? 256 : 128;

@@ -175,6 +175,9 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
     g.ldc = c.d;
     g.Aux = dxe;
     g.part = ws_ptr<float>(ws, L.gpart);
+    // short K (2 Ep): the epilogue's fp32 reads dominate, so use tiles that
+    // fit three blocks per CU and overlap it with other blocks' MFMAs
+    g.bm = g.bn = 128;
     rc = launch_gemm(MOE_KERNEL_ROUTE_BWD_DX, MODE_ROW, true, EPI_ADDF32, c, g, s);
     if (rc != MOE_OK) return rc;
     // dWr partials = x^T [dz_hi | dz_lo] over uniform token chunks
