@@ -106,6 +106,28 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// Exclusive scan of v over a block of 256 threads (4 waves); *total gets
+// the block's sum.  Every thread of the block must call it; s_wave is 4
+// ints of shared memory.
+__device__ __forceinline__ int block_exclusive_scan_256(int v, int* s_wave, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
+  __syncthreads();  // s_wave may still be read by an earlier call
+  if (lane == 63) s_wave[w] = incl;
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < w) base += s_wave[i];
+  *total = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+  return base + incl - v;
+}
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

@@ -638,17 +638,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 }
 
 // tiles[e] = sum_{e' < e} ceil(m_e' / BM); tiles[E] = number of M tiles
-__global__ void gemm_schedule_kernel(const int32_t* __restrict__ offsets,
-                                     int32_t* __restrict__ tiles, int E, int BM) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    int32_t acc = 0;
-    for (int e = 0; e < E; ++e) {
-      tiles[e] = acc;
-      const int m = offsets[e + 1] - offsets[e];
-      acc += (m + BM - 1) / BM;
-    }
-    tiles[E] = acc;
-  }
+// (one thread per expert, E <= 256, block scan)
+__global__ __launch_bounds__(256) void gemm_schedule_kernel(const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ tiles, int E,
+                                                            int BM) {
+  __shared__ int s_wave[4];
+  const int e = threadIdx.x;
+  const int m = e < E ? offsets[e + 1] - offsets[e] : 0;
+  int tot;
+  const int ex = block_exclusive_scan_256((m + BM - 1) / BM, s_wave, &tot);
+  if (e < E) tiles[e] = ex;
+  if (e == 0) tiles[E] = tot;
 }
 
 constexpr int kFM = 64, kFN = 64;    // fp32 block tile
@@ -755,7 +755,7 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
 
 int schedule(const moe_cfg& c, const int32_t* offsets, int32_t* tiles, hipStream_t s) {
   MOE_LAUNCH(MOE_KERNEL_SCHEDULE, s,
-             gemm_schedule_kernel<<<1, 64, 0, s>>>(offsets, tiles, c.E, row_bm(c)));
+             gemm_schedule_kernel<<<1, 256, 0, s>>>(offsets, tiles, c.E, row_bm(c)));
   return MOE_OK;
 }
 

@@ -14,6 +14,7 @@ namespace moe {
 namespace {
 
 constexpr int kPW = kPermTokens / kWave;  // waves per permute block
+static_assert(kPermTokens == 256, "the scatter kernel's offset scan is a 256-thread scan");
 
 // per-block expert histogram: blk[b][e] = #assignments of block b to e
 __global__ __launch_bounds__(kPermTokens) void permute_count_kernel(
@@ -32,47 +33,69 @@ __global__ __launch_bounds__(kPermTokens) void permute_count_kernel(
     blk[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// Column scan over blocks (blk becomes each block's starting position per
-// expert), counts, and offsets = exclusive scan of min(count, C).
+// Column scan over blocks, one block per expert: blk[b][e] becomes block b's
+// first position among the assignments to e, and counts[e] their total.
+// With no token blocks it writes zero offsets instead (the scatter kernel,
+// which writes them otherwise, is not launched).
 __global__ __launch_bounds__(256) void permute_scan_kernel(
-    int32_t* __restrict__ blk, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int nblk, int E, int64_t cap) {
-  __shared__ int32_t kept[256];
-  const int e = threadIdx.x;
-  if (e < E) {
-    int32_t run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int32_t v = blk[(int64_t)b * E + e];
-      blk[(int64_t)b * E + e] = run;
-      run += v;
+    int32_t* __restrict__ blk, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int nblk, int E) {
+  __shared__ int s_wave[4];
+  const int e = blockIdx.x;
+  if (nblk == 0) {
+    if (threadIdx.x == 0) {
+      counts[e] = 0;
+      offsets[e] = 0;
+      if (e == 0) offsets[E] = 0;
     }
-    counts[e] = run;
-    kept[e] = (cap >= 0 && run > cap) ? (int32_t)cap : run;
+    return;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t o = 0;
-    for (int i = 0; i < E; ++i) {
-      offsets[i] = o;
-      o += kept[i];
-    }
-    offsets[E] = o;
+  int carry = 0;
+  for (int b0 = 0; b0 < nblk; b0 += 256) {
+    const int b = b0 + threadIdx.x;
+    const int v = b < nblk ? blk[(int64_t)b * E + e] : 0;
+    int tot;
+    const int ex = block_exclusive_scan_256(v, s_wave, &tot);
+    if (b < nblk) blk[(int64_t)b * E + e] = carry + ex;
+    carry += tot;
   }
+  if (threadIdx.x == 0) counts[e] = carry;
 }
 
 // Rank every assignment among the assignments to the same expert in token
 // order, drop beyond capacity, and write the maps.
 __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ blk,
-    const int32_t* __restrict__ offsets, int32_t* __restrict__ row_of,
-    int32_t* __restrict__ src_of, int64_t T_, int E, int k, int64_t cap) {
+    const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ src_of, int64_t T_, int E, int k,
+    int64_t cap) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);  // [kPW][E]
   int32_t* wbase = reinterpret_cast<int32_t*>(mask + kPW * E);            // [kPW][E]
+  int32_t* s_off = wbase + kPW * E;                                       // [E]
+  __shared__ int s_wave[4];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t0 = (int64_t)blockIdx.x * kPermTokens;
   const int64_t t = t0 + threadIdx.x;
   const bool valid = t < T_;
+
+  // offsets = exclusive scan of min(counts, C) (E <= 256, one per thread);
+  // block 0 publishes them
+  {
+    const int e = threadIdx.x;
+    int kept = 0;
+    if (e < E) {
+      const int32_t cnt = counts[e];
+      kept = (cap >= 0 && cnt > cap) ? (int32_t)cap : cnt;
+    }
+    int tot;
+    const int ex = block_exclusive_scan_256(kept, s_wave, &tot);
+    if (e < E) s_off[e] = ex;
+    if (blockIdx.x == 0) {
+      if (e < E) offsets[e] = ex;
+      if (e == 0) offsets[E] = tot;
+    }
+  }
 
   for (int i = threadIdx.x; i < kPW * E; i += blockDim.x) mask[i] = 0ull;
   __syncthreads();
@@ -102,7 +125,7 @@ __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
                           __popcll(mask[w * E + e] & lt);
       int32_t row = -1;
       if (cap < 0 || pos < cap) {
-        row = (int32_t)(offsets[e] + pos);
+        row = (int32_t)(s_off[e] + pos);
         src_of[row] = (int32_t)(t * k + j);
       }
       row_of[t * k + j] = row;
@@ -157,13 +180,12 @@ int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
                permute_count_kernel<<<nblk, kPermTokens, c.E * 4, s>>>(idx, blk, c.T,
                                                                       c.E, c.k));
   MOE_LAUNCH(MOE_KERNEL_PERMUTE_SCAN, s,
-             permute_scan_kernel<<<1, 256, 0, s>>>(blk, counts, offsets, nblk, c.E,
-                                                  c.capacity));
+             permute_scan_kernel<<<c.E, 256, 0, s>>>(blk, counts, offsets, nblk, c.E));
   if (nblk > 0) {
-    const size_t sm = (size_t)kPW * c.E * 8 + (size_t)kPW * c.E * 4;
+    const size_t sm = (size_t)kPW * c.E * 8 + (size_t)kPW * c.E * 4 + (size_t)c.E * 4;
     MOE_LAUNCH(MOE_KERNEL_PERMUTE_SCATTER, s,
                permute_scatter_kernel<<<nblk, kPermTokens, sm, s>>>(
-                   idx, blk, offsets, row_of, src_of, c.T, c.E, c.k, c.capacity));
+                   idx, blk, counts, offsets, row_of, src_of, c.T, c.E, c.k, c.capacity));
     const int g = (int)std::min<int64_t>(ceil_div(c.T, 4), 65536);
     if (c.dtype == MOE_BF16)
       MOE_LAUNCH(MOE_KERNEL_PERMUTE_COPY, s,
