@@ -36,6 +36,9 @@ SMALL_CASES = [
     (1, 64, 8, 2, 64, "bf16", 1.0, "zero"),         # a single token
     (200, 64, 4, 4, 64, "bf16", None, "normal"),    # k == E
     (260, 48, 130, 8, 40, "bf16", None, "normal"),  # E > 128: 8 router tiles, k = 8
+    (300, 64, 256, 16, 64, "bf16", None, "normal"), # E = 256 (largest), k = 16
+    (100, 64, 40, 32, 64, "bf16", 1.0, "normal"),   # k = 32 (largest), drops
+    (200, 64, 100, 4, 64, "f32", 1.0, "zipf"),      # fp32 router over 100 experts
 ]
 
 
