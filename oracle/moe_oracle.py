@@ -24,7 +24,8 @@ What is computed, and where the pages say so:
 * Expert FFN = per-expert feed-forward weights ("Sharded by expert"), here
   W1 (d x f) -> tanh-GELU -> W2 (f x d), no biases.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent (numbered as in the design doc; R8
+(bias) and R9 (FFN form) are stated with the inputs and the FFN above):
   R1 softmax over all E logits, then top-k; gate = probability of the chosen
      expert, not renormalised.
   R2 selection is made on the fp32 logit z; ties go to the lower expert
@@ -40,11 +41,19 @@ Readings taken where the pages are silent (each also listed in the design doc):
      renormalised; a token with every assignment dropped gets out = 0.
   R7 counts = routed assignments per expert before the drop; offsets scan
      the kept counts (compact ragged layout of R rows).
-  R8 storage rounding (round-to-nearest-even) at A, H, Y, out, dYp, dA, dXp,
+  R10 storage rounding (round-to-nearest-even) at A, H, Y, out, dYp, dA, dXp,
      dX, dW1, dW2, dWr to the activation type s; probs, gates, dgate, dXe,
      db are fp32.  Everything between storage points is fp64.
-  R9 L = <out, dOut>; index/top-k/capacity steps are piecewise constant and
+  R11 L = <out, dOut>; index/top-k/capacity steps are piecewise constant and
      carry no gradient.
+  R16 auxiliary load-balancing loss (the balancing penalty of the tutorial's
+     section "The Capacity Factor", coefficient alpha, 0.01 in its EP
+     configuration block): the pages give no formula; this reading is the
+     standard published balancing loss L_aux = alpha * E * sum_e f_e P_e with
+     f_e = counts_e / (T k) (routed assignments before the drop) and P_e the
+     mean router probability of expert e over the tokens.  f is piecewise
+     constant, so the gradient flows through P only and joins dgate before
+     the softmax backward.  Drop rate = 1 - R / (T k).
 
 Every floating-point result here is fp64 arithmetic on exactly converted
 inputs followed by one rounding at the storage point; ``exact=True`` turns
@@ -199,7 +208,7 @@ def gelu_tanh_grad(a) -> np.ndarray:
 
 def expert_ffn_fwd(xe, W1e, W2e, rnd):
     """One expert over its rows: A = xe W1e, H = gelu(A), Y = H W2e, each
-    rounded at its storage point (R8)."""
+    rounded at its storage point (R10)."""
     A = rnd(np.asarray(xe, np.float64) @ np.asarray(W1e, np.float64))
     H = rnd(gelu_tanh(A))
     Y = rnd(H @ np.asarray(W2e, np.float64))
@@ -260,18 +269,47 @@ def unpermute_bwd(dXp, row_of) -> np.ndarray:
     return acc
 
 
-def router_dz(probs, idx, row_of, dg) -> np.ndarray:
-    """Softmax backward: dp[t, idx[t,j]] = dgate[t,j] for kept j (else 0);
+def router_dz(probs, idx, row_of, dg, aux=None) -> np.ndarray:
+    """Softmax backward: dp[t, idx[t,j]] = dgate[t,j] for kept j (else 0),
+    plus the load-balancing gradient aux[e] (aux_dp) when given;
     dz = p * (dp - sum_e p dp)."""
     probs = np.asarray(probs, np.float64)
     T, E = probs.shape
     dp = np.zeros((T, E), dtype=np.float64)
+    if aux is not None:
+        dp += np.asarray(aux, np.float64)[None, :]
     row_of = np.asarray(row_of)
     for j in range(row_of.shape[1]):
         m = row_of[:, j] >= 0
-        dp[np.nonzero(m)[0], np.asarray(idx)[m, j]] = np.asarray(dg)[m, j]
+        dp[np.nonzero(m)[0], np.asarray(idx)[m, j]] += np.asarray(dg)[m, j]
     s = (probs * dp).sum(axis=1, keepdims=True)
     return probs * (dp - s)
+
+
+def aux_loss(probs, counts, k: int, coeff: float) -> float:
+    """Load-balancing loss alpha * E * sum_e f_e P_e (reading R16)."""
+    probs = np.asarray(probs, np.float64)
+    T, E = probs.shape
+    if T == 0:
+        return 0.0
+    f = np.asarray(counts, np.float64) / (T * k)
+    P = probs.sum(axis=0) / T
+    return float(coeff * E * np.dot(f, P))
+
+
+def aux_dp(counts, T: int, k: int, coeff: float) -> np.ndarray:
+    """dL_aux / dp[t, e] = alpha * E * f_e / T, the same for every token."""
+    E = len(counts)
+    if T == 0:
+        return np.zeros(E)
+    return coeff * E * np.asarray(counts, np.float64) / (T * k) / T
+
+
+def drop_rate(offsets, T: int, k: int) -> float:
+    """Fraction of the T k assignments dropped by the capacity limit."""
+    if T * k == 0:
+        return 0.0
+    return 1.0 - float(np.asarray(offsets)[-1]) / (T * k)
 
 
 def route_bwd(x, Wr, dz, dXe, rnd, r32):
@@ -327,12 +365,16 @@ def layer_fwd(inp: Dict[str, np.ndarray], w, exact: bool = False,
             fw["x_perm"][lo:hi], to_f64(inp["W1"][e]), to_f64(inp["W2"][e]), rnd)
     fw.update(A=A, H=H, Y=Y, R=R)
     fw["out"] = combine(Y, fw["row_of"], fw["gate"], rnd)
+    if w.kind == "layer":
+        fw["aux_loss"] = aux_loss(fw["probs"], fw["counts"], w.k, w.aux_coeff)
+        fw["drop_rate"] = drop_rate(fw["offsets"], w.T, w.k)
     return fw
 
 
 def layer_bwd(inp: Dict[str, np.ndarray], w, fw: Dict[str, np.ndarray],
               exact: bool = False) -> Dict[str, np.ndarray]:
-    """Backward of the layer for upstream gradient dOut (L = <out, dOut>)."""
+    """Backward of the layer for upstream gradient dOut (L = <out, dOut>,
+    plus the load-balancing loss when w.aux_coeff > 0)."""
     rnd = rounder(w.dtype, exact)
     r32 = rounder("f32", exact)
     dOut = to_f64(inp["dOut"])
@@ -351,7 +393,8 @@ def layer_bwd(inp: Dict[str, np.ndarray], w, fw: Dict[str, np.ndarray],
     bw = dict(dYp=dYp, dgate=dg, dXp=dXp, dA=dA, dW1=dW1, dW2=dW2)
     if w.kind == "layer":
         dXe = r32(unpermute_bwd(dXp, fw["row_of"]))
-        dz = router_dz(fw["probs"], fw["idx"], fw["row_of"], dg)
+        aux = aux_dp(fw["counts"], w.T, w.k, w.aux_coeff) if w.aux_coeff > 0 else None
+        dz = router_dz(fw["probs"], fw["idx"], fw["row_of"], dg, aux)
         dX, dWr, db = route_bwd(fw["x"], to_f64(inp["Wr"]), dz, dXe, rnd, r32)
         bw.update(dXe=dXe, dz=dz, dX=dX, dWr=dWr, db=db)
     return bw

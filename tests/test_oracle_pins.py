@@ -297,8 +297,9 @@ def test_zero_capacity_drops_everything():
 
 # ------------------------------------------------------------------ layer bwd
 def _loss(inp, w):
+    """L = <out, dOut> + the load-balancing loss (zero when w.aux_coeff = 0)."""
     fw = O.layer_fwd(inp, w, exact=True)
-    return float(np.sum(fw["out"] * inp["dOut"])), fw
+    return float(np.sum(fw["out"] * inp["dOut"])) + fw["aux_loss"], fw
 
 
 def _min_topk_gap(z, k):
@@ -307,12 +308,14 @@ def _min_topk_gap(z, k):
     return np.min(zs[:, :kk - 1] - zs[:, 1:kk]) if kk > 1 else np.inf
 
 
-@pytest.mark.parametrize("T,d,E,k,f,cf", [(10, 4, 3, 2, 5, None),
-                                          (12, 5, 4, 2, 6, 0.75),
-                                          (7, 3, 4, 1, 4, 1.0),
-                                          (6, 4, 5, 3, 3, None)])
-def test_backward_matches_central_finite_differences(T, d, E, k, f, cf):
-    w = W.custom(T, d, E, k, f, cf=cf)
+@pytest.mark.parametrize("T,d,E,k,f,cf,aux", [(10, 4, 3, 2, 5, None, 0.0),
+                                              (12, 5, 4, 2, 6, 0.75, 0.0),
+                                              (7, 3, 4, 1, 4, 1.0, 0.0),
+                                              (6, 4, 5, 3, 3, None, 0.0),
+                                              (12, 5, 4, 2, 6, 0.75, 0.3),
+                                              (9, 4, 5, 1, 3, None, 2.0)])
+def test_backward_matches_central_finite_differences(T, d, E, k, f, cf, aux):
+    w = W.custom(T, d, E, k, f, cf=cf, aux_coeff=aux)
     seed = 0
     while True:      # pick a seed whose routing margins exceed the step by far
         inp = _exact_inputs(T, d, E, k, f, seed=seed)
@@ -407,3 +410,52 @@ def test_named_workload_capacities():
         w = W.get(name)
         assert O.capacity(w.T, w.k, w.E, w.cf) == C
     assert O.capacity(W.get("C2").T, 2, 64, W.get("C2").cf) is None
+
+
+# ------------------------------------------------------- load-balancing loss
+def test_aux_loss_uniform_routing_is_the_coefficient():
+    # every expert gets T k / E assignments and probability 1/E: E * sum 1/E^2 = 1
+    T, E, k = 12, 4, 2
+    probs = np.full((T, E), 1.0 / E)
+    counts = np.full(E, T * k // E)
+    assert abs(O.aux_loss(probs, counts, k, 0.01) - 0.01) < 1e-15
+
+
+def test_aux_loss_collapsed_routing_is_E_times_the_coefficient():
+    # top-1, every token on expert 0 with probability 1: f_0 = P_0 = 1
+    T, E = 9, 6
+    probs = np.zeros((T, E))
+    probs[:, 0] = 1.0
+    counts = np.zeros(E)
+    counts[0] = T
+    assert abs(O.aux_loss(probs, counts, 1, 0.5) - 0.5 * E) < 1e-12
+
+
+def test_aux_gradient_matches_finite_differences_through_the_softmax():
+    rng = np.random.default_rng(3)
+    T, E, k = 5, 6, 2
+    z = rng.standard_normal((T, E))
+    counts = rng.integers(0, 4, size=E)
+    coeff = 0.7
+    no_route = -np.ones((T, k), dtype=np.int32)       # no gate gradient
+    idx = np.zeros((T, k), dtype=np.int32)
+    dz = O.router_dz(O.softmax(z), idx, no_route, np.zeros((T, k)),
+                     O.aux_dp(counts, T, k, coeff))
+    h = 1e-6
+    fd = np.zeros_like(z)
+    for i in np.ndindex(z.shape):
+        for sgn in (+1, -1):
+            zz = z.copy()
+            zz[i] += sgn * h
+            fd[i] += sgn * O.aux_loss(O.softmax(zz), counts, k, coeff) / (2 * h)
+    np.testing.assert_allclose(dz, fd, rtol=1e-6, atol=1e-9)
+
+
+def test_drop_rate_closed_forms():
+    idx = np.array([[0, 1], [0, 1], [0, 2], [0, 3]], dtype=np.int32)
+    _, off_inf, _, _ = O.assign(idx, 4, None)
+    assert O.drop_rate(off_inf, 4, 2) == 0.0
+    _, off_1, _, _ = O.assign(idx, 4, 1)      # expert 0 keeps 1 of 4, expert 1 1 of 2
+    assert O.drop_rate(off_1, 4, 2) == 1.0 - 4 / 8
+    _, off_0, _, _ = O.assign(idx, 4, 0)
+    assert O.drop_rate(off_0, 4, 2) == 1.0

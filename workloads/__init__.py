@@ -55,6 +55,7 @@ class Workload:
     zipf_s: float = 1.2
     dirichlet_alpha: float = 0.5
     pool_experts: int = 0  # size of the whole expert pool ('ep_share' only)
+    aux_coeff: float = 0.0  # load-balancing loss coefficient (0 = none)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -84,9 +85,9 @@ def get(name: str) -> Workload:
 
 
 def custom(T, d, E, k, f, dtype="f32", cf=None, bias="zero",
-           kind="layer", name="custom", w_std=0.02) -> Workload:
+           kind="layer", name="custom", w_std=0.02, aux_coeff=0.0) -> Workload:
     return Workload(name, T=T, d=d, E=E, k=k, f=f, dtype=dtype, cf=cf,
-                    bias=bias, kind=kind, w_std=w_std)
+                    bias=bias, kind=kind, w_std=w_std, aux_coeff=aux_coeff)
 
 
 # ---------------------------------------------------------------- storage
