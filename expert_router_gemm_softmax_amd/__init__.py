@@ -11,7 +11,8 @@ from .binding import (KERNELS, MOE_BF16, MOE_FP32, MOE_NO_CAPACITY, MoeCfg, MoeC
                       make_cfg, moe_capacity, moe_check_cfg, moe_combine,
                       moe_combine_bwd, moe_grouped_ffn, moe_grouped_ffn_bwd,
                       moe_layer_bwd, moe_layer_fwd, moe_permute, moe_prof_arm,
-                      moe_prof_read, moe_route, moe_route_bwd, moe_rows_max,
+                      moe_prof_read, moe_route, moe_route_bwd, moe_router_aux,
+                      moe_rows_max,
                       moe_unpermute_bwd, moe_workspace_bytes, status_str)
 from .layer import MoeLayer
 

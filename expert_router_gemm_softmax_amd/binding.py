@@ -32,7 +32,7 @@ KERNELS = dict(ROUTE=0, PERMUTE_COUNT=1, PERMUTE_SCAN=2, PERMUTE_SCATTER=3,
                GEMM_UP=4, GEMM_DOWN=5, COMBINE=6, COMBINE_BWD=7, GEMM_DH=8,
                GEMM_DX=9, GEMM_DW2=10, GEMM_DW1=11, UNPERMUTE_BWD=12,
                ROUTE_BWD_DZ=13, ROUTE_BWD_DX=14, ROUTE_BWD_DW=15, SCHEDULE=16,
-               ROUTE_PREP=17, PERMUTE_COPY=18, ROUTE_LOGITS=19)
+               ROUTE_PREP=17, PERMUTE_COPY=18, ROUTE_LOGITS=19, ROUTE_AUX=20)
 
 
 class MoeLibraryError(ImportError):
@@ -49,11 +49,11 @@ class MoeError(RuntimeError):
 class MoeCfg(ctypes.Structure):
     _fields_ = [("T", c_int64), ("d", c_int32), ("E", c_int32), ("k", c_int32),
                 ("f", c_int32), ("dtype", c_int32), ("capacity", c_int64),
-                ("route_margin", c_float), ("flags", c_uint32)]
+                ("route_margin", c_float), ("flags", c_uint32), ("aux_coeff", c_float)]
 
     def __repr__(self):
         return (f"MoeCfg(T={self.T}, d={self.d}, E={self.E}, k={self.k}, f={self.f}, "
-                f"dtype={self.dtype}, capacity={self.capacity})")
+                f"dtype={self.dtype}, capacity={self.capacity}, aux_coeff={self.aux_coeff})")
 
 
 class MoeWeights(ctypes.Structure):
@@ -62,7 +62,8 @@ class MoeWeights(ctypes.Structure):
 
 class MoeCtx(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("probs", "idx", "gate", "counts", "offsets",
-                                         "row_of", "src_of", "x_perm", "A", "H", "Y")]
+                                         "row_of", "src_of", "x_perm", "A", "H", "Y",
+                                         "aux")]
 
 
 class MoeGrads(ctypes.Structure):
@@ -85,7 +86,8 @@ _SIGS = {
     "moe_combine_bwd": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_ffn_bwd": (c_int, [_CFG] + [_P] * 11 + [c_size_t, _P]),
     "moe_unpermute_bwd": (c_int, [_CFG, _P, _P, _P, _P]),
-    "moe_route_bwd": (c_int, [_CFG] + [_P] * 11 + [c_size_t, _P]),
+    "moe_router_aux": (c_int, [_CFG, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_route_bwd": (c_int, [_CFG] + [_P] * 12 + [c_size_t, _P]),
     "moe_layer_fwd": (c_int, [_CFG, POINTER(MoeWeights), _P, _P, POINTER(MoeCtx), _P,
                               c_size_t, _P]),
     "moe_layer_bwd": (c_int, [_CFG, POINTER(MoeWeights), _P, _P, POINTER(MoeCtx), _P,
@@ -166,12 +168,14 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def make_cfg(T, d, E, k, f, dtype="bf16", capacity=None, route_margin=0.0) -> MoeCfg:
-    """capacity: None = no limit, else an int >= 0."""
+def make_cfg(T, d, E, k, f, dtype="bf16", capacity=None, route_margin=0.0,
+             aux_coeff=0.0) -> MoeCfg:
+    """capacity: None = no limit, else an int >= 0; aux_coeff: weight of the
+    load-balancing loss (0 = none)."""
     dt = {"bf16": MOE_BF16, "f32": MOE_FP32, MOE_BF16: MOE_BF16, MOE_FP32: MOE_FP32}[dtype]
     return MoeCfg(T=int(T), d=int(d), E=int(E), k=int(k), f=int(f), dtype=dt,
                   capacity=MOE_NO_CAPACITY if capacity is None else int(capacity),
-                  route_margin=float(route_margin), flags=0)
+                  route_margin=float(route_margin), flags=0, aux_coeff=float(aux_coeff))
 
 
 def moe_capacity(T, k, E, cf) -> int:
@@ -233,11 +237,18 @@ def moe_unpermute_bwd(cfg, dXp, row_of, dXe, stream=None):
         byref(cfg), _ptr(dXp), _ptr(row_of), _ptr(dXe), _stream(stream)))
 
 
-def moe_route_bwd(cfg, x, Wr, probs, idx, row_of, dgate, dXp, dX, dWr, db, ws,
+def moe_router_aux(cfg, probs, counts, offsets, aux, ws, stream=None):
+    _check("moe_router_aux", lib.moe_router_aux(
+        byref(cfg), _ptr(probs), _ptr(counts), _ptr(offsets), _ptr(aux), _ptr(ws),
+        _nbytes(ws), _stream(stream)))
+
+
+def moe_route_bwd(cfg, x, Wr, probs, idx, row_of, counts, dgate, dXp, dX, dWr, db, ws,
                   stream=None):
+    """counts may be None when cfg.aux_coeff is 0."""
     _check("moe_route_bwd", lib.moe_route_bwd(
-        byref(cfg), _ptr(x), _ptr(Wr), _ptr(probs), _ptr(idx), _ptr(row_of), _ptr(dgate),
-        _ptr(dXp), _ptr(dX), _ptr(dWr), _ptr(db), _ptr(ws), _nbytes(ws),
+        byref(cfg), _ptr(x), _ptr(Wr), _ptr(probs), _ptr(idx), _ptr(row_of), _ptr(counts),
+        _ptr(dgate), _ptr(dXp), _ptr(dX), _ptr(dWr), _ptr(db), _ptr(ws), _nbytes(ws),
         _stream(stream)))
 
 

@@ -27,7 +27,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm.hip", "combine.hip",
+SOURCES = ["api.hip", "route.hip", "route_aux.hip", "permute.hip", "gemm.hip", "combine.hip",
            "route_bwd.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

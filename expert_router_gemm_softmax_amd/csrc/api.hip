@@ -2,6 +2,7 @@
 // the step sequence of the layer forward and backward, and opt-in kernel
 // timing.  Every entry point validates everything before it enqueues
 // anything; on an error nothing is enqueued and nothing is written.
+#include <float.h>
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
@@ -63,6 +64,7 @@ int check_cfg(const moe_cfg* c) {
   if (c->flags != 0) return MOE_ERR_ARG;
   if (c->T * c->k > 0x7fffffffLL) return MOE_ERR_SHAPE;
   if (!(c->route_margin == c->route_margin)) return MOE_ERR_ARG;  // NaN
+  if (!(c->aux_coeff >= 0.0f && c->aux_coeff <= FLT_MAX)) return MOE_ERR_ARG;  // NaN, <0, inf
   const size_t s = elem_bytes(*c);
   if ((c->d * s) % 16 != 0 || (c->f * s) % 16 != 0) return MOE_ERR_ALIGN;
   return MOE_OK;
@@ -266,10 +268,25 @@ int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp, const int32_t* row_of
   return launch_unpermute_bwd(c, dXp, row_of, dXe, S(stream));
 }
 
+int moe_router_aux(const moe_cfg* cfg, const float* probs, const int32_t* counts,
+                   const int32_t* offsets, float* aux, void* ws, size_t ws_bytes,
+                   moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_cfg& c = *cfg;
+  const Sizes z = sizes(c);
+  MOE_TRY(need(probs, z.TE, 4));
+  MOE_TRY(need(counts, (size_t)c.E * 4, 4));
+  MOE_TRY(need(offsets, z.E1, 4));
+  MOE_TRY(need(aux, 2 * sizeof(float), 4));
+  MOE_TRY(need_ws(c, ws, ws_bytes));
+  clear_stale_error();
+  return launch_route_aux(c, probs, counts, offsets, aux, ws, S(stream));
+}
+
 int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr, const float* probs,
-                  const int32_t* idx, const int32_t* row_of, const float* dgate,
-                  const void* dXp, void* dX, void* dWr, float* db, void* ws, size_t ws_bytes,
-                  moe_stream_t stream) {
+                  const int32_t* idx, const int32_t* row_of, const int32_t* counts,
+                  const float* dgate, const void* dXp, void* dX, void* dWr, float* db,
+                  void* ws, size_t ws_bytes, moe_stream_t stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_cfg& c = *cfg;
   const Sizes z = sizes(c);
@@ -278,6 +295,7 @@ int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr, const float
   MOE_TRY(need(probs, z.TE, 4));
   MOE_TRY(need(idx, z.Tk, 4));
   MOE_TRY(need(row_of, z.Tk, 4));
+  if (c.aux_coeff > 0.0f) MOE_TRY(need(counts, (size_t)c.E * 4, 4));
   MOE_TRY(need(dgate, z.Tk, 4));
   MOE_TRY(need(dXp, z.Rd, 16));
   MOE_TRY(need(dX, z.Td, 16));
@@ -285,7 +303,7 @@ int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr, const float
   if (db) MOE_TRY(need(db, (size_t)c.E * 4, 4));
   MOE_TRY(need_ws(c, ws, ws_bytes));
   clear_stale_error();
-  return launch_route_bwd(c, x, Wr, probs, idx, row_of, dgate, dXp, dX, dWr, db, ws,
+  return launch_route_bwd(c, x, Wr, probs, idx, row_of, counts, dgate, dXp, dX, dWr, db, ws,
                           S(stream));
 }
 
@@ -303,6 +321,7 @@ static int check_ctx(const moe_cfg& c, const moe_ctx* x) {
   MOE_TRY(need(x->A, z.Rf, 16));
   MOE_TRY(need(x->H, z.Rf, 16));
   MOE_TRY(need(x->Y, z.Rd, 16));
+  if (x->aux) MOE_TRY(need(x->aux, 2 * sizeof(float), 4));
   return MOE_OK;
 }
 
@@ -332,6 +351,8 @@ int moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const void* x, void*
   MOE_TRY(launch_route(c, x, w->Wr, w->b, ctx->probs, ctx->idx, ctx->gate, ws, s));
   MOE_TRY(launch_permute(c, x, ctx->idx, ctx->counts, ctx->offsets, ctx->row_of,
                          ctx->src_of, ctx->x_perm, ws, s));
+  if (ctx->aux)
+    MOE_TRY(launch_route_aux(c, ctx->probs, ctx->counts, ctx->offsets, ctx->aux, ws, s));
   MOE_TRY(launch_ffn_fwd(c, ctx->x_perm, ctx->offsets, w->W1, w->W2, ctx->A, ctx->H, ctx->Y,
                          ws, s));
   return launch_combine(c, ctx->Y, ctx->row_of, ctx->gate, out, s);
@@ -363,8 +384,8 @@ int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* x, const
   MOE_TRY(launch_combine_bwd(c, dOut, ctx->Y, ctx->row_of, ctx->gate, dYp, dgate, s));
   MOE_TRY(launch_ffn_bwd(c, ctx->x_perm, ctx->offsets, w->W1, w->W2, ctx->A, ctx->H, dYp,
                          dXp, g->dW1, g->dW2, ws, s));
-  return launch_route_bwd(c, x, w->Wr, ctx->probs, ctx->idx, ctx->row_of, dgate, dXp, dX,
-                          g->dWr, g->db, ws, s);
+  return launch_route_bwd(c, x, w->Wr, ctx->probs, ctx->idx, ctx->row_of, ctx->counts, dgate,
+                          dXp, dX, g->dWr, g->db, ws, s);
 }
 
 const char* moe_last_error(void) { return g_last_error; }

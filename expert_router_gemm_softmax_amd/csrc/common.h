@@ -152,8 +152,10 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 //   dYp, dA, dXp                backward row gradients (Rmax rows, s)
 //   dxe      [T, d] f32         unpermute-sum of dXp (router backward)
 struct WsLayout {
-  size_t wrT, zf, wl_count, wl_tok, wl_n, wl_e, gpart, perm_blk, tiles, dz, dzb, wrp, dwr_part, db_part, dgate, dYp, dA, dXp, dxe, total;
+  size_t wrT, zf, wl_count, wl_tok, wl_n, wl_e, gpart, perm_blk, tiles, aux_part, dz, dzb, wrp,
+      dwr_part, db_part, dgate, dYp, dA, dXp, dxe, total;
   int nblk_perm;
+  int nblk_aux;
   int nblk_dz;
   int dwr_chunks, dwr_chunk, dwr_n;
 };
@@ -163,6 +165,7 @@ constexpr int kPermTokens = 256;  // tokens per permute block
 // per CU (256) of up to 256 x 256
 constexpr size_t kGemmPartFloats = (size_t)256 * 256 * 256;
 constexpr int kDzTokens = 16;     // tokens per router-backward dz block
+constexpr int kAuxTokens = 64;    // tokens per block of the balancing-loss column sums
 
 inline int64_t rows_max(const moe_cfg& c) {
   const int64_t tk = c.T * c.k;
@@ -188,6 +191,7 @@ inline WsLayout ws_layout(const moe_cfg& c) {
   const int64_t T1 = c.T > 0 ? c.T : 1;
   L.nblk_perm = (int)ceil_div(T1, kPermTokens);
   L.nblk_dz = (int)ceil_div(T1, kDzTokens);
+  L.nblk_aux = (int)ceil_div(T1, kAuxTokens);
   // dWr = x^T dz as a k-ragged GEMM over uniform token chunks: enough chunks
   // for ~1024 blocks of 128 x 128 output tiles, at least 256 tokens each
   const bool bf = c.dtype == MOE_BF16;
@@ -214,6 +218,7 @@ inline WsLayout ws_layout(const moe_cfg& c) {
   L.gpart = take(c.dtype == MOE_BF16 ? kGemmPartFloats * 4 : 0);
   L.perm_blk = take((size_t)L.nblk_perm * c.E * 4);
   L.tiles = take((size_t)(c.E + 1) * 4 * 4);
+  L.aux_part = take((size_t)L.nblk_aux * c.E * 4);
   L.dz = take(bf ? 0 : (size_t)c.T * c.E * 4);
   L.dzb = take(bf ? (size_t)c.T * 2 * bwd_ep(c.E) * 2 : 0);
   L.wrp = take(bf ? (size_t)c.d * 2 * bwd_ep(c.E) * 2 : 0);
@@ -267,6 +272,8 @@ void note_launch_error(int kernel_id, hipError_t e);
 // (each validates nothing: the C-ABI layer in api.hip has done that)
 int launch_route(const moe_cfg& c, const void* x, const void* Wr, const float* b,
                  float* probs, int32_t* idx, float* gate, void* ws, hipStream_t s);
+int launch_route_aux(const moe_cfg& c, const float* probs, const int32_t* counts,
+                     const int32_t* offsets, float* aux, void* ws, hipStream_t s);
 int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
                    int32_t* counts, int32_t* offsets, int32_t* row_of,
                    int32_t* src_of, void* x_perm, void* ws, hipStream_t s);
@@ -286,7 +293,7 @@ int launch_unpermute_bwd(const moe_cfg& c, const void* dXp, const int32_t* row_o
                          float* dXe, hipStream_t s, int kernel_id = MOE_KERNEL_UNPERMUTE_BWD);
 int launch_route_bwd(const moe_cfg& c, const void* x, const void* Wr,
                      const float* probs, const int32_t* idx, const int32_t* row_of,
-                     const float* dgate, const void* dXp, void* dX, void* dWr,
-                     float* db, void* ws, hipStream_t s);
+                     const int32_t* counts, const float* dgate, const void* dXp, void* dX,
+                     void* dWr, float* db, void* ws, hipStream_t s);
 
 }  // namespace moe

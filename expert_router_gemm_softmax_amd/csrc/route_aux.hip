@@ -1,0 +1,97 @@
+// Routing diagnostics and the auxiliary load-balancing loss.  The
+// distributed-training tutorial (section "The Capacity Factor") adds a
+// balancing penalty, weighted by a small coefficient, that evens out the
+// experts' token loads, and watches the drop rate and the expert load
+// distribution.  The loss is the standard balancing loss over the fraction
+// of assignments each expert receives and its mean router probability:
+//   L = alpha * E * sum_e f_e P_e,  f_e = counts[e] / (T k),
+//   P_e = (1/T) sum_t probs[t, e]
+// and the drop rate is 1 - R / (T k) with R = offsets[E] the kept rows.
+// The expert loads are counts itself.
+//
+// Two kernels: per-block column sums of probs over kAuxTokens tokens (one
+// thread per expert, rows read coalesced across experts), then one block
+// that sums the partials in block order, forms the loss with a fixed tree
+// over experts (fp64) and writes aux[0] = L, aux[1] = drop rate.  The sums
+// have a fixed order, so the result is deterministic.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void route_aux_part_kernel(const float* __restrict__ probs,
+                                                              float* __restrict__ part,
+                                                              int64_t T_, int E) {
+  const int e = threadIdx.x;
+  if (e >= E) return;
+  const int64_t t0 = (int64_t)blockIdx.x * kAuxTokens;
+  const int n = (int)(T_ - t0 < kAuxTokens ? T_ - t0 : kAuxTokens);
+  const float* p = probs + t0 * E + e;
+  float s = 0.0f;
+  int t = 0;
+  // eight rows' loads in flight per step; summed in token order
+  for (; t + 8 <= n; t += 8) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = p[(int64_t)(t + q) * E];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s += v[q];
+  }
+  for (; t < n; ++t) s += p[(int64_t)t * E];
+  part[(int64_t)e * gridDim.x + blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void route_aux_final_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, float* __restrict__ aux, int nblk, int64_t T_,
+    int E, int k, float coeff) {
+  __shared__ double red[256];
+  const int e = threadIdx.x;
+  double term = 0.0;
+  if (e < E) {
+    const float* pe = part + (int64_t)e * nblk;
+    double s = 0.0;
+    for (int b = 0; b < nblk; ++b) s += (double)pe[b];
+    term = (double)counts[e] * s;  // counts_e * T P_e
+  }
+  red[e] = term;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (e < h) red[e] += red[e + h];
+    __syncthreads();
+  }
+  if (e == 0) {
+    const double tk = (double)T_ * (double)k;
+    aux[0] = (float)((double)coeff * (double)E * red[0] / (tk * (double)T_));
+    aux[1] = (float)(1.0 - (double)offsets[E] / tk);
+  }
+}
+
+// aux[0] = aux[1] = 0 for an empty batch
+__global__ void route_aux_zero_kernel(float* __restrict__ aux) {
+  if (threadIdx.x < 2) aux[threadIdx.x] = 0.0f;
+}
+
+}  // namespace
+
+int launch_route_aux(const moe_cfg& c, const float* probs, const int32_t* counts,
+                     const int32_t* offsets, float* aux, void* ws, hipStream_t s) {
+  if (c.T == 0) {
+    MOE_LAUNCH(MOE_KERNEL_ROUTE_AUX, s, route_aux_zero_kernel<<<1, 64, 0, s>>>(aux));
+    return MOE_OK;
+  }
+  const WsLayout L = ws_layout(c);
+  float* part = ws_ptr<float>(ws, L.aux_part);
+  // both kernels are timed as one launch
+  prof_begin(MOE_KERNEL_ROUTE_AUX, s);
+  MOE_LAUNCH_NP(MOE_KERNEL_ROUTE_AUX,
+                route_aux_part_kernel<<<L.nblk_aux, 256, 0, s>>>(probs, part, c.T, c.E));
+  MOE_LAUNCH_NP(MOE_KERNEL_ROUTE_AUX,
+                route_aux_final_kernel<<<1, 256, 0, s>>>(part, counts, offsets, aux,
+                                                         L.nblk_aux, c.T, c.E, c.k,
+                                                         c.aux_coeff));
+  prof_end(MOE_KERNEL_ROUTE_AUX, s);
+  return MOE_OK;
+}
+
+}  // namespace moe

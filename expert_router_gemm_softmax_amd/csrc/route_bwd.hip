@@ -3,7 +3,10 @@
 // parallel", section "Sharded by expert, replicated everywhere else");
 // index, top-k and capacity steps are piecewise constant and pass no
 // gradient.
-//   dp[t, idx[t,j]] = dgate[t,j] for kept j;  dz = p * (dp - sum_e p dp)
+//   dp[t, e] = a_e + dgate[t,j] if e = idx[t,j] for a kept j, else a_e
+//   dz = p * (dp - sum_e p dp)
+// where a_e = alpha E counts[e] / (T k T) is the gradient of the
+// load-balancing loss (zero when its coefficient alpha is zero).
 //   dX  = sum_{kept j} dXp[row_of[t,j]] + dz Wr^T
 //   dWr = x^T dz,  db = sum_t dz
 // Both products run on the grouped GEMM kernels.  For bf16 storage dz is
@@ -20,16 +23,23 @@ namespace {
 
 // dz for kDzTokens tokens per block (one wave per token); writes dz (fp32
 // storage) or its bf16 hi/lo split (bf16 storage), and the block's partial
-// sums of dz for db.
+// sums of dz for db.  counts may be NULL when aux_scale is zero.
 template <bool BF>
 __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
     const float* __restrict__ probs, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ row_of, const float* __restrict__ dgate,
-    float* __restrict__ dz, uint16_t* __restrict__ dzb, float* __restrict__ db_part,
-    int64_t T_, int E, int Ep, int k) {
+    const int32_t* __restrict__ row_of, const int32_t* __restrict__ counts,
+    const float* __restrict__ dgate, float* __restrict__ dz, uint16_t* __restrict__ dzb,
+    float* __restrict__ db_part, int64_t T_, int E, int Ep, int k, float aux_scale) {
   __shared__ float sdb[4][256];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float dbacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // balancing-loss gradient, the same for every token
+  float a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    a[i] = aux_scale != 0.0f && e < E ? aux_scale * (float)counts[e] : 0.0f;
+  }
   const int64_t t0 = (int64_t)blockIdx.x * kDzTokens;
   for (int tt = w; tt < kDzTokens; tt += 4) {
     const int64_t t = t0 + tt;
@@ -39,7 +49,7 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
       p[i] = e < E ? probs[t * E + e] : 0.0f;
-      dp[i] = 0.0f;
+      dp[i] = a[i];
     }
     for (int j = 0; j < k; ++j) {
       if (row_of[t * k + j] < 0) continue;
@@ -47,7 +57,7 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
       const float g = dgate[t * k + j];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (e == lane + 64 * i) dp[i] = g;
+        if (e == lane + 64 * i) dp[i] += g;
     }
     float sp = 0.0f;
 #pragma unroll
@@ -135,8 +145,9 @@ __global__ __launch_bounds__(256) void route_bwd_reduce_kernel(
 
 template <typename T>
 int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
-                const int32_t* idx, const int32_t* row_of, const float* dgate, const T* dXp,
-                T* dX, T* dWr, float* db, void* ws, hipStream_t s) {
+                const int32_t* idx, const int32_t* row_of, const int32_t* counts,
+                const float* dgate, const T* dXp, T* dX, T* dWr, float* db, void* ws,
+                hipStream_t s) {
   constexpr bool BF = sizeof(T) == 2;
   const WsLayout L = ws_layout(c);
   const int Ep = bwd_ep(c.E);
@@ -146,10 +157,16 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
   float* part = ws_ptr<float>(ws, L.dwr_part);
   float* dbp = ws_ptr<float>(ws, L.db_part);
   const int nblk = c.T > 0 ? (int)ceil_div(c.T, kDzTokens) : 0;
+  // a_e = aux_scale counts[e]
+  const float aux_scale =
+      c.aux_coeff > 0.0f && c.T > 0
+          ? (float)((double)c.aux_coeff * c.E / ((double)c.T * c.k * (double)c.T))
+          : 0.0f;
   if (nblk > 0)
     MOE_LAUNCH(MOE_KERNEL_ROUTE_BWD_DZ, s,
-               route_bwd_dz_kernel<BF><<<nblk, 256, 0, s>>>(probs, idx, row_of, dgate, dz,
-                                                           dzb, dbp, c.T, c.E, Ep, c.k));
+               route_bwd_dz_kernel<BF><<<nblk, 256, 0, s>>>(probs, idx, row_of, counts, dgate,
+                                                           dz, dzb, dbp, c.T, c.E, Ep, c.k,
+                                                           aux_scale));
   if constexpr (BF) {
     const int64_t n = (int64_t)c.d * 2 * Ep;
     MOE_LAUNCH(MOE_KERNEL_ROUTE_PREP, s,
@@ -209,16 +226,18 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
 
 int launch_route_bwd(const moe_cfg& c, const void* x, const void* Wr,
                      const float* probs, const int32_t* idx, const int32_t* row_of,
-                     const float* dgate, const void* dXp, void* dX, void* dWr, float* db,
-                     void* ws, hipStream_t s) {
+                     const int32_t* counts, const float* dgate, const void* dXp, void* dX,
+                     void* dWr, float* db, void* ws, hipStream_t s) {
   if (c.dtype == MOE_BF16)
     return route_bwd_t<uint16_t>(c, static_cast<const uint16_t*>(x),
-                                 static_cast<const uint16_t*>(Wr), probs, idx, row_of, dgate,
+                                 static_cast<const uint16_t*>(Wr), probs, idx, row_of, counts,
+                                 dgate,
                                  static_cast<const uint16_t*>(dXp),
                                  static_cast<uint16_t*>(dX), static_cast<uint16_t*>(dWr), db,
                                  ws, s);
   return route_bwd_t<float>(c, static_cast<const float*>(x), static_cast<const float*>(Wr),
-                            probs, idx, row_of, dgate, static_cast<const float*>(dXp),
+                            probs, idx, row_of, counts, dgate,
+                            static_cast<const float*>(dXp),
                             static_cast<float*>(dX), static_cast<float*>(dWr), db, ws, s);
 }
 

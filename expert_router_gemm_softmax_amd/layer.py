@@ -14,9 +14,13 @@ class MoeLayer:
 
     Weights are device tensors: Wr [d,E], b [E] float32 (or None),
     W1 [E,d,f], W2 [E,f,d], all of the activation dtype (bf16 or fp32).
+    With diagnostics (the default when cfg.aux_coeff > 0) every forward also
+    writes saved["aux"] = [load-balancing loss, drop rate]; the expert loads
+    are saved["counts"].  The backward adds the loss's gradient whenever
+    cfg.aux_coeff > 0.
     """
 
-    def __init__(self, cfg: B.MoeCfg, Wr, b, W1, W2, device="cuda"):
+    def __init__(self, cfg: B.MoeCfg, Wr, b, W1, W2, device="cuda", diagnostics=None):
         self.cfg = cfg
         T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f
         self.sdt = torch.bfloat16 if cfg.dtype == B.MOE_BF16 else torch.float32
@@ -32,6 +36,9 @@ class MoeLayer:
             offsets=e(E + 1, dt=torch.int32), row_of=e(T, k, dt=torch.int32),
             src_of=e(self.Rmax, dt=torch.int32), x_perm=e(self.Rmax, d),
             A=e(self.Rmax, f), H=e(self.Rmax, f), Y=e(self.Rmax, d))
+        if diagnostics is None:
+            diagnostics = cfg.aux_coeff > 0
+        self.saved["aux"] = e(2, dt=torch.float32) if diagnostics else None
         self.ws = torch.empty(B.moe_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
         self.weights = B.MoeWeights(Wr=B._ptr(Wr), b=B._ptr(b), W1=B._ptr(W1),
                                     W2=B._ptr(W2))

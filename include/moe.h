@@ -81,6 +81,10 @@ typedef struct moe_cfg {
   float route_margin; /* router certification margin (logit units); <= 0
                          selects the default 1e-3.  See moe_route. */
   uint32_t flags;     /* must be 0 */
+  float aux_coeff;    /* coefficient alpha >= 0 of the auxiliary
+                         load-balancing loss (0 = none); see moe_router_aux.
+                         When > 0, moe_route_bwd and moe_layer_bwd add its
+                         gradient. */
 } moe_cfg;
 
 /* Capacity of the capacity-factor rule: C = ceil(cf * T * k / E).  A value
@@ -167,6 +171,23 @@ MOE_API int moe_grouped_ffn(const moe_cfg* cfg, const void* x_perm,
 MOE_API int moe_combine(const moe_cfg* cfg, const void* Y, const int32_t* row_of,
                 const float* gate, void* out, moe_stream_t stream);
 
+/* Routing diagnostics and the auxiliary load-balancing loss.  The
+ * distributed-training tutorial (section "The Capacity Factor") adds a
+ * balancing penalty that pulls the experts' token loads together
+ * (coefficient 0.01 in its EP configuration block) and asks for the drop
+ * rate and the expert load distribution to be watched.  The loss is the
+ * standard balancing loss
+ *   L = alpha * E * sum_e f_e P_e,  f_e = counts[e] / (T k),
+ *   P_e = (1/T) sum_t probs[t, e],  alpha = cfg->aux_coeff
+ *   aux[0] = L (0 when alpha = 0), aux[1] = drop rate 1 - offsets[E] / (T k)
+ * The expert load distribution is counts itself.  probs [T,E] float,
+ * counts [E] and offsets [E+1] int32 as written by moe_permute,
+ * aux [2] float, all device.  fp32 sums in a fixed order (deterministic).
+ * Workspace as above. */
+MOE_API int moe_router_aux(const moe_cfg* cfg, const float* probs, const int32_t* counts,
+                           const int32_t* offsets, float* aux, void* ws, size_t ws_bytes,
+                           moe_stream_t stream);
+
 /* --------------------------------------------------------------- backward
  * The backward pass retraces the forward steps in reverse order ("The step
  * timeline").  The
@@ -204,7 +225,9 @@ MOE_API int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp,
 
 /* B1 router backward (the router is a shared parameter with an ordinary
  * gradient -- "Sharded by expert, replicated everywhere else"):
- *   dp[t, idx[t,j]] = dgate[t,j] for kept j, else 0
+ *   dp[t, e] = a_e + (dgate[t,j] if e = idx[t,j] for a kept j)
+ *       with a_e = alpha * E * counts[e] / (T k T), the gradient of the
+ *       load-balancing loss (alpha = cfg->aux_coeff; a_e = 0 when alpha = 0)
  *   dz  = probs * (dp - sum_e probs * dp)
  *   db  = sum_t dz                       [E] float
  *   dWr = x^T dz                         [d,E] s
@@ -212,7 +235,8 @@ MOE_API int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp,
  * (the unpermute-sum of B2 is fused in).  Workspace as above. */
 MOE_API int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr,
                   const float* probs, const int32_t* idx,
-                  const int32_t* row_of, const float* dgate, const void* dXp,
+                  const int32_t* row_of, const int32_t* counts /* [E]; may be NULL
+                  when cfg->aux_coeff == 0 */, const float* dgate, const void* dXp,
                   void* dX, void* dWr, float* db, void* ws, size_t ws_bytes,
                   moe_stream_t stream);
 
@@ -241,6 +265,8 @@ typedef struct moe_ctx {
   void* A;          /* [Rmax,f] s */
   void* H;          /* [Rmax,f] s */
   void* Y;          /* [Rmax,d] s */
+  float* aux;       /* [2] float or NULL: routing diagnostics written by
+                       moe_layer_fwd, as by moe_router_aux */
 } moe_ctx;
 
 typedef struct moe_grads {
@@ -291,7 +317,8 @@ typedef enum {
   MOE_KERNEL_ROUTE_PREP = 17,    /* router weight transpose / stacking */
   MOE_KERNEL_PERMUTE_COPY = 18,  /* x -> x_perm row copy */
   MOE_KERNEL_ROUTE_LOGITS = 19,  /* fast router logits x Wr (GEMM) */
-  MOE_KERNEL_COUNT_ = 20
+  MOE_KERNEL_ROUTE_AUX = 20,     /* load-balancing loss and drop rate */
+  MOE_KERNEL_COUNT_ = 21
 } moe_kernel_id;
 
 MOE_API int moe_prof_arm(int kernel_id, int max_launches);

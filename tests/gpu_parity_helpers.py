@@ -73,7 +73,7 @@ def to_int(t) -> np.ndarray:
 def cfg_of(M, w, route_margin=0.0):
     cap = O.capacity(w.T, w.k, w.E, w.cf)
     return M.make_cfg(w.T, w.d, w.E, w.k, w.f, w.dtype, capacity=cap,
-                      route_margin=route_margin)
+                      route_margin=route_margin, aux_coeff=w.aux_coeff)
 
 
 def red_tol(ref, dtype):
@@ -120,13 +120,23 @@ def assert_close(name, got, ref, tol):
 
 
 def run_layer(M, w, inp, route_margin=0.0, bwd=True):
-    """Forward (+ backward) of the layer on the GPU through moe_layer_fwd/bwd."""
+    """Forward (+ backward) of the layer on the GPU through moe_layer_fwd/bwd,
+    with the routing diagnostics on.  res["aux1"] is the balancing loss at
+    coefficient 1 (and the drop rate) from the standalone moe_router_aux on
+    the same routing, so that its sums are checked in every case."""
+    import copy
+
     import torch
     cfg = cfg_of(M, w, route_margin)
     d = {k: to_dev(v) for k, v in inp.items()}
-    layer = M.MoeLayer(cfg, d["Wr"], d["b"], d["W1"], d["W2"])
+    layer = M.MoeLayer(cfg, d["Wr"], d["b"], d["W1"], d["W2"], diagnostics=True)
     out = layer.forward(d["x"])
     res = dict(out=out, **layer.saved)
+    c1 = copy.copy(cfg)
+    c1.aux_coeff = 1.0
+    res["aux1"] = torch.full((2,), -1.0, dtype=torch.float32, device="cuda")
+    M.moe_router_aux(c1, layer.saved["probs"], layer.saved["counts"], layer.saved["offsets"],
+                     res["aux1"], layer.ws)
     if bwd:
         dX, g = layer.backward(d["x"], d["dOut"])
         res.update(dX=dX, **g)
@@ -176,6 +186,10 @@ def check_layer_full(res, fw, bw, w, check_bwd=True):
     assert_close("H", to_f64(res["H"])[:R], fw["H"], tol)
     assert_close("Y", to_f64(res["Y"])[:R], fw["Y"], tol)
     assert_close("out", to_f64(res["out"]), fw["out"], tol)
+    if res.get("aux") is not None:
+        check_aux("aux", res["aux"], res["probs"], fw, w, w.aux_coeff)
+    if res.get("aux1") is not None:
+        check_aux("aux1", res["aux1"], res["probs"], fw, w, 1.0)
     if check_bwd:
         assert_close("dX", to_f64(res["dX"]), bw["dX"], tol)
         dz = bw["dz"]
@@ -189,8 +203,28 @@ def check_layer_full(res, fw, bw, w, check_bwd=True):
     return R
 
 
-def make_case(T, d, E, k, f, dtype, cf, bias="zero", seed=0, **kw):
-    w = W.custom(T, d, E, k, f, dtype=dtype, cf=cf, bias=bias, name=f"T{T}d{d}E{E}k{k}f{f}")
+def check_aux(name, aux, probs, fw, w, coeff):
+    """Balancing loss and drop rate against the oracle.
+
+    Loss: the oracle's fp64 value on its own probabilities, within what the
+    probability tolerance (1e-5 relative, 1e-6 absolute per element) allows:
+    L = coeff E sum_e f_e P_e with sum_e f_e = 1 moves by at most
+    1e-5 L + 1e-6 coeff E.  Against the oracle's formula on the GPU's own
+    probabilities the only error left is the kernel's summation: fp32
+    partial sums over 64 tokens (relative error <= 63 * 2^-24) summed in
+    fp64, then one rounding to fp32 -- 4e-6 relative.
+    Drop rate: exact integers, one rounding to fp32 (<= 2^-24 < 1e-7)."""
+    a = to_f64(aux)
+    ref = O.aux_loss(fw["probs"], fw["counts"], w.k, coeff)
+    assert abs(a[0] - ref) <= 1e-5 * abs(ref) + 1e-6 * coeff * w.E, (name, a[0], ref)
+    own = O.aux_loss(to_f64(probs), fw["counts"], w.k, coeff)
+    assert abs(a[0] - own) <= 4e-6 * abs(own) + 1e-30, (name, a[0], own)
+    assert abs(a[1] - O.drop_rate(fw["offsets"], w.T, w.k)) <= 1e-7, (name, a[1])
+
+
+def make_case(T, d, E, k, f, dtype, cf, bias="zero", seed=0, aux_coeff=0.0, **kw):
+    w = W.custom(T, d, E, k, f, dtype=dtype, cf=cf, bias=bias, name=f"T{T}d{d}E{E}k{k}f{f}",
+                 aux_coeff=aux_coeff)
     inp = W.make_inputs(w, seed=seed)
     for key, v in kw.items():
         inp[key] = v

@@ -13,7 +13,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_parity_helpers import (assert_close, check_layer_full, check_routing_exact,
+from gpu_parity_helpers import (assert_close, check_aux, check_layer_full, check_routing_exact,
                                 expert_grad_tols, logit_error, run_layer, say, term_norm,
                                 terms_tol, to_dev, to_f64, to_int)
 
@@ -97,6 +97,9 @@ def test_c4_large(M):
     assert err <= TAU / 2
     assert_close("probs", to_f64(res["probs"]), fw["probs"], "prob")
     assert_close("gate", to_f64(res["gate"]), fw["gate"], "prob")
+    check_aux("aux1", res["aux1"], res["probs"], fw, w, 1.0)
+    say(f"C4 balancing loss (coefficient 1) {float(to_f64(res['aux1'])[0]):.6f}, "
+        f"drop rate {float(to_f64(res['aux1'])[1]):.6f}")
 
     off, src, k = fw["offsets"], fw["src_of"], w.k
     x = fw["x"]

@@ -10,7 +10,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_parity_helpers import (TOL, assert_close, cfg_of, check_layer_full,
+from gpu_parity_helpers import (TOL, assert_close, cfg_of, check_aux, check_layer_full,
                                 check_routing_exact, logit_error, make_case,
                                 run_layer, say, terms_tol, to_dev, to_f64, to_int)
 
@@ -102,10 +102,11 @@ def test_exact_ties_go_to_the_lower_expert(M):
 
 def test_zero_tokens(M):
     import torch
-    w = W.custom(0, 64, 4, 2, 64, dtype="bf16", cf=None)
+    w = W.custom(0, 64, 4, 2, 64, dtype="bf16", cf=None, aux_coeff=0.01)
     cfg = cfg_of(M, w)
     e = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt, device="cuda")
     layer = M.MoeLayer(cfg, e(64, 4), None, e(4, 64, 64), e(4, 64, 64))
+    layer.saved["aux"].fill_(-1.0)
     x = e(0, 64)
     out = layer.forward(x)
     dX, g = layer.backward(x, e(0, 64))
@@ -114,13 +115,60 @@ def test_zero_tokens(M):
     assert to_int(layer.saved["counts"]).tolist() == [0] * 4
     assert to_int(layer.saved["offsets"]).tolist() == [0] * 5
     assert np.all(to_f64(g["dW1"]) == 0) and np.all(to_f64(g["dWr"]) == 0)
+    assert to_f64(layer.saved["aux"]).tolist() == [0.0, 0.0]
+
+
+BALANCE_CASES = [
+    # T, d, E, k, f, dtype, cf, bias, alpha
+    (513, 64, 40, 3, 136, "bf16", 0.75, "zipf", 1.0),  # skewed loads, drops
+    (300, 36, 5, 2, 52, "f32", 0.9, "normal", 0.01),   # the tutorial's coefficient
+    (260, 48, 130, 8, 40, "bf16", None, "normal", 0.1),  # E > 128, dropless
+]
+
+
+@pytest.mark.parametrize("case", BALANCE_CASES,
+                         ids=lambda c: "T{}E{}k{}{}a{}".format(c[0], c[2], c[3], c[5], c[8]))
+def test_layer_with_balancing_loss(M, case):
+    """The layer with the load-balancing loss on: its value, the drop rate
+    and every gradient (the router's now carry the loss's term) against the
+    oracle."""
+    T, d, E, k, f, dt, cf, bias, alpha = case
+    w, inp = make_case(T, d, E, k, f, dt, cf, bias, seed=T + 1, aux_coeff=alpha)
+    say("case", case)
+    res = run_layer(M, w, inp)
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    check_layer_full(res, fw, bw, w)
+    say("  loss", float(to_f64(res["aux"])[0]), "oracle", fw["aux_loss"],
+        "drop", float(to_f64(res["aux"])[1]), "oracle", fw["drop_rate"])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_balancing_gradient_alone(M, dt):
+    """dOut = 0: the whole router gradient is the balancing loss's, so a
+    dropped or mis-scaled term cannot hide under the task gradient.  The
+    router outputs are compared at the tolerance of their dtype after scaling
+    by the output's largest magnitude; the expert gradients are exactly 0."""
+    w, inp = make_case(700, 128, 16, 4, 96, dt, 1.0, "normal", seed=11, aux_coeff=1.0)
+    inp["dOut"] = np.zeros_like(inp["dOut"])
+    res = run_layer(M, w, inp)
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    check_aux("aux", res["aux"], res["probs"], fw, w, 1.0)
+    rtol, atol = TOL[dt]
+    for name in ("dX", "dWr", "db"):
+        ref = bw[name]
+        scale = float(np.abs(ref).max())
+        assert scale > 0, name
+        assert_close(name, to_f64(res[name]), ref, (rtol, atol * scale))
+    assert np.all(to_f64(res["dW1"]) == 0) and np.all(to_f64(res["dW2"]) == 0)
 
 
 def test_step_entry_points_equal_the_layer_entry_points(M):
     """moe_route .. moe_route_bwd called one by one give bitwise the layer's
     results (same kernels, same order)."""
     import torch
-    w, inp = make_case(700, 128, 8, 2, 160, "bf16", 1.0, "normal", seed=7)
+    w, inp = make_case(700, 128, 8, 2, 160, "bf16", 1.0, "normal", seed=7, aux_coeff=0.05)
     res = run_layer(M, w, inp)
     cfg, d, L = res["_cfg"], res["_dev"], res["_layer"]
     T, E, k = w.T, w.E, w.k
@@ -132,6 +180,8 @@ def test_step_entry_points_equal_the_layer_entry_points(M):
     counts, offsets = z(E, dt=torch.int32), z(E + 1, dt=torch.int32)
     row_of, src_of, xp = z(T, k, dt=torch.int32), z(Rmax, dt=torch.int32), z(Rmax, w.d)
     M.moe_permute(cfg, d["x"], idx, counts, offsets, row_of, src_of, xp, ws)
+    aux = z(2, dt=torch.float32)
+    M.moe_router_aux(cfg, probs, counts, offsets, aux, ws)
     A, H, Y = z(Rmax, w.f), z(Rmax, w.f), z(Rmax, w.d)
     M.moe_grouped_ffn(cfg, xp, offsets, d["W1"], d["W2"], A, H, Y, ws)
     out = z(T, w.d)
@@ -143,12 +193,14 @@ def test_step_entry_points_equal_the_layer_entry_points(M):
     dXe = z(T, w.d, dt=torch.float32)
     M.moe_unpermute_bwd(cfg, dXp, row_of, dXe)
     dX, dWr, db = z(T, w.d), torch.zeros_like(d["Wr"]), z(E, dt=torch.float32)
-    M.moe_route_bwd(cfg, d["x"], d["Wr"], probs, idx, row_of, dg, dXp, dX, dWr, db, ws)
+    M.moe_route_bwd(cfg, d["x"], d["Wr"], probs, idx, row_of, counts, dg, dXp, dX, dWr, db,
+                    ws)
     torch.cuda.synchronize()
     R = int(to_int(offsets)[-1])
     for name, a, b in [("probs", probs, res["probs"]), ("idx", idx, res["idx"]),
                        ("gate", gate, res["gate"]), ("offsets", offsets, res["offsets"]),
                        ("row_of", row_of, res["row_of"]), ("out", out, res["out"]),
+                       ("aux", aux, res["aux"]),
                        ("dX", dX, res["dX"]), ("dWr", dWr, res["dWr"]), ("db", db, res["db"]),
                        ("dW1", dW1, res["dW1"]), ("dW2", dW2, res["dW2"])]:
         assert torch.equal(a, b), name
@@ -169,11 +221,11 @@ def test_step_entry_points_equal_the_layer_entry_points(M):
 
 def test_runs_are_bitwise_deterministic(M):
     import torch
-    w, inp = make_case(1500, 256, 16, 2, 384, "bf16", 1.0, "normal", seed=8)
+    w, inp = make_case(1500, 256, 16, 2, 384, "bf16", 1.0, "normal", seed=8, aux_coeff=0.01)
     a = run_layer(M, w, inp)
     b = run_layer(M, w, inp)
     for key in ("probs", "idx", "gate", "counts", "offsets", "row_of", "out", "dX",
-                "dWr", "db", "dW1", "dW2"):
+                "dWr", "db", "dW1", "dW2", "aux", "aux1"):
         assert torch.equal(a[key], b[key]), key
     R = int(to_int(a["offsets"])[-1])
     for key in ("src_of", "x_perm", "A", "H", "Y"):

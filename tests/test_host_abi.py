@@ -147,9 +147,40 @@ def test_status_strings():
 
 
 def test_cfg_struct_layout_matches_header():
-    # int64 T; 5 x int32; int64 capacity (8-aligned); float; uint32 -> 48 bytes
-    assert ctypes.sizeof(B.MoeCfg) == 48
+    # int64 T; 5 x int32; int64 capacity (8-aligned); float; uint32; float
+    # aux_coeff -> 52 bytes, padded to 56 for the int64 members
+    assert ctypes.sizeof(B.MoeCfg) == 56
     assert B.MoeCfg.capacity.offset == 32 and B.MoeCfg.flags.offset == 44
+    assert B.MoeCfg.aux_coeff.offset == 48
+    # MoeCtx: eleven tensors, then the optional diagnostics output
+    assert B.MoeCtx.aux.offset == 11 * ctypes.sizeof(ctypes.c_void_p)
+
+
+@pytest.mark.parametrize("coeff", [-0.01, float("nan"), float("inf")])
+def test_invalid_balancing_coefficient_is_rejected(coeff):
+    c = M.make_cfg(16, 64, 8, 2, 64, "bf16", aux_coeff=coeff)
+    assert M.moe_check_cfg(c) == B.MOE_ERR_ARG
+    assert M.moe_workspace_bytes(c) == 0
+
+
+def test_balancing_entry_points_validate_arguments():
+    c = M.make_cfg(16, 64, 8, 2, 64, "bf16", aux_coeff=0.01)
+    assert M.moe_check_cfg(c) == B.MOE_OK
+    ws = M.moe_workspace_bytes(c)
+    aux = B.lib.moe_router_aux
+    assert aux(ctypes.byref(c), None, _A, _A, _A, _A, ws, None) == B.MOE_ERR_ARG
+    assert aux(ctypes.byref(c), _A, None, _A, _A, _A, ws, None) == B.MOE_ERR_ARG
+    assert aux(ctypes.byref(c), _A, _A, None, _A, _A, ws, None) == B.MOE_ERR_ARG
+    assert aux(ctypes.byref(c), _A, _A, _A, None, _A, ws, None) == B.MOE_ERR_ARG
+    assert aux(ctypes.byref(c), _A, _A, _A, _A + 2, _A, ws, None) == B.MOE_ERR_ALIGN
+    assert aux(ctypes.byref(c), _A, _A, _A, _A, _A, 10, None) == B.MOE_ERR_WORKSPACE
+    # the router backward needs counts only when the loss is on
+    rb = lambda cfg, counts: B.lib.moe_route_bwd(
+        ctypes.byref(cfg), _A, _A, _A, _A, _A, counts, _A, _A, _A, _A, None, _A, 10, None)
+    assert rb(c, None) == B.MOE_ERR_ARG
+    assert rb(c, _A) == B.MOE_ERR_WORKSPACE
+    c.aux_coeff = 0.0
+    assert rb(c, None) == B.MOE_ERR_WORKSPACE
 
 
 def test_binding_has_no_oracle_dependency(repo_root):
