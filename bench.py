@@ -14,6 +14,7 @@ This build runs on one GPU: --gpus above 1 exits with a message.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -49,6 +50,12 @@ def parse():
                     help="kernel timed for the roofline (default: GEMM_DH, the dA = "
                          "(dYp W2^T) * gelu'(A) GEMM, the longest per launch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--aux-coeff", type=float, default=0.0,
+                    help="coefficient of the load-balancing loss (default 0: the bare "
+                         "layer); > 0 also computes the loss and drop rate every step")
+    ap.add_argument("--recompute", action="store_true",
+                    help="selective recomputation: A and H are not saved and the "
+                         "backward recomputes them (one extra grouped GEMM)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="before the warmup, run one plain device-to-device copy of BYTES "
                          "(calibration of the HBM byte counters)")
@@ -191,6 +198,8 @@ def main():
 
     import workloads as W
     w = W.get(a.config)
+    if a.aux_coeff:
+        w = dataclasses.replace(w, aux_coeff=a.aux_coeff)
     if a.summarize_counters:
         return summarize_counters(a, w)
     import expert_router_gemm_softmax_amd as M
@@ -204,7 +213,8 @@ def main():
         cap = None
     else:
         cap = M.moe_capacity(w.T, w.k, w.E, w.cf)
-    cfg = M.make_cfg(w.T, w.d, w.E, w.k, w.f, w.dtype, capacity=cap)
+    cfg = M.make_cfg(w.T, w.d, w.E, w.k, w.f, w.dtype, capacity=cap,
+                     aux_coeff=a.aux_coeff, recompute=a.recompute)
     sdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
     if w.kind == "layer":
@@ -224,6 +234,8 @@ def main():
         ws = torch.empty(M.moe_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
         e = lambda *s, dt=sdt: torch.empty(*s, dtype=dt, device="cuda")
         A, H, Y = e(Rmax, w.f), e(Rmax, w.f), e(Rmax, w.d)
+        if a.recompute:
+            A = H = None
         out, dYp, dXp = e(w.T, w.d), e(Rmax, w.d), e(Rmax, w.d)
         dg = e(w.T, 1, dt=torch.float32)
         dW1, dW2 = torch.empty_like(d["W1"]), torch.empty_like(d["W2"])
@@ -270,9 +282,21 @@ def main():
     # algorithmic work of the timed kernel per launch
     flops = {"GEMM_UP": 2.0 * R * w.d * w.f, "GEMM_DOWN": 2.0 * R * w.d * w.f,
              "GEMM_DH": 2.0 * R * w.d * w.f, "GEMM_DX": 2.0 * R * w.d * w.f,
-             "GEMM_DW1": 2.0 * R * w.d * w.f, "GEMM_DW2": 2.0 * R * w.d * w.f}
+             "GEMM_DW1": 2.0 * R * w.d * w.f, "GEMM_DW2": 2.0 * R * w.d * w.f,
+             "GEMM_RECOMPUTE": 2.0 * R * w.d * w.f}
+    s_b = 2 if w.dtype == "bf16" else 4
+    Tk = w.T * w.k
+    hbm_bytes = {"COMBINE": R * w.d * s_b + w.T * w.d * s_b + 8 * Tk,
+                 "COMBINE_BWD": w.T * w.d * s_b + 2 * R * w.d * s_b + 12 * Tk,
+                 "PERMUTE_COPY": 2 * R * w.d * s_b,
+                 "ROUTE_AUX": 4 * w.T * w.E + 8 * w.E + 4}
     avg_s = (k_ms / 1e3) / max(k_n, 1)
-    if kernel in flops:
+    if kernel in hbm_bytes and avg_s > 0:
+        achieved = hbm_bytes[kernel] / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": kernel, "avg_ms": round(avg_s * 1e3, 5)}
+    elif kernel in flops:
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
         achieved = flops[kernel] / avg_s / 1e12 if avg_s > 0 else 0.0
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
@@ -295,7 +319,8 @@ def main():
         "config": {"workload": f"{w.name}: T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} "
                                f"cf={w.cf} bias={w.bias}",
                    "tokens": w.T, "d": w.d, "experts": w.E, "top_k": w.k, "ffn": w.f,
-                   "capacity": cap, "kept_rows": R, "parallelism": "single GPU"},
+                   "capacity": cap, "kept_rows": R, "parallelism": "single GPU",
+                   "aux_coeff": a.aux_coeff, "recompute": a.recompute},
         "roofline": roof,
         "gpu_event_ms_per_step": round(gpu_ms / a.steps, 4),
     }

@@ -27,12 +27,14 @@ MOE_ERR_UNIMPLEMENTED = -7
 MOE_FP32 = 0
 MOE_BF16 = 1
 MOE_NO_CAPACITY = -1
+MOE_FLAG_RECOMPUTE = 1
 
 KERNELS = dict(ROUTE=0, PERMUTE_COUNT=1, PERMUTE_SCAN=2, PERMUTE_SCATTER=3,
                GEMM_UP=4, GEMM_DOWN=5, COMBINE=6, COMBINE_BWD=7, GEMM_DH=8,
                GEMM_DX=9, GEMM_DW2=10, GEMM_DW1=11, UNPERMUTE_BWD=12,
                ROUTE_BWD_DZ=13, ROUTE_BWD_DX=14, ROUTE_BWD_DW=15, SCHEDULE=16,
-               ROUTE_PREP=17, PERMUTE_COPY=18, ROUTE_LOGITS=19, ROUTE_AUX=20)
+               ROUTE_PREP=17, PERMUTE_COPY=18, ROUTE_LOGITS=19, ROUTE_AUX=20,
+               GEMM_RECOMPUTE=21)
 
 
 class MoeLibraryError(ImportError):
@@ -169,13 +171,15 @@ def _stream(stream):
 
 
 def make_cfg(T, d, E, k, f, dtype="bf16", capacity=None, route_margin=0.0,
-             aux_coeff=0.0) -> MoeCfg:
+             aux_coeff=0.0, recompute=False) -> MoeCfg:
     """capacity: None = no limit, else an int >= 0; aux_coeff: weight of the
-    load-balancing loss (0 = none)."""
+    load-balancing loss (0 = none); recompute: keep A and H out of the saved
+    state and recompute them in backward (MOE_FLAG_RECOMPUTE)."""
     dt = {"bf16": MOE_BF16, "f32": MOE_FP32, MOE_BF16: MOE_BF16, MOE_FP32: MOE_FP32}[dtype]
     return MoeCfg(T=int(T), d=int(d), E=int(E), k=int(k), f=int(f), dtype=dt,
                   capacity=MOE_NO_CAPACITY if capacity is None else int(capacity),
-                  route_margin=float(route_margin), flags=0, aux_coeff=float(aux_coeff))
+                  route_margin=float(route_margin),
+                  flags=MOE_FLAG_RECOMPUTE if recompute else 0, aux_coeff=float(aux_coeff))
 
 
 def moe_capacity(T, k, E, cf) -> int:

@@ -61,7 +61,7 @@ int check_cfg(const moe_cfg* c) {
   if (c->k < 1 || c->k > 32 || c->E < c->k || c->E > 256) return MOE_ERR_ARG;
   if (c->d < 1 || c->f < 1) return MOE_ERR_ARG;
   if (c->capacity < MOE_NO_CAPACITY) return MOE_ERR_ARG;
-  if (c->flags != 0) return MOE_ERR_ARG;
+  if ((c->flags & ~MOE_FLAG_RECOMPUTE) != 0) return MOE_ERR_ARG;
   if (c->T * c->k > 0x7fffffffLL) return MOE_ERR_SHAPE;
   if (!(c->route_margin == c->route_margin)) return MOE_ERR_ARG;  // NaN
   if (!(c->aux_coeff >= 0.0f && c->aux_coeff <= FLT_MAX)) return MOE_ERR_ARG;  // NaN, <0, inf
@@ -109,6 +109,10 @@ Sizes sizes(const moe_cfg& c) {
 }
 
 inline hipStream_t S(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+// A and H are caller buffers unless the recomputation mode keeps them in
+// the workspace
+inline bool saves_ah(const moe_cfg& c) { return (c.flags & MOE_FLAG_RECOMPUTE) == 0; }
 
 }  // namespace
 }  // namespace moe
@@ -196,8 +200,10 @@ int moe_grouped_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offse
   MOE_TRY(need(offsets, z.E1, 4));
   MOE_TRY(need(W1, z.Edf, 16));
   MOE_TRY(need(W2, z.Edf, 16));
-  MOE_TRY(need(A, z.Rf, 16));
-  MOE_TRY(need(H, z.Rf, 16));
+  if (saves_ah(c)) {
+    MOE_TRY(need(A, z.Rf, 16));
+    MOE_TRY(need(H, z.Rf, 16));
+  }
   MOE_TRY(need(Y, z.Rd, 16));
   MOE_TRY(need_ws(c, ws, ws_bytes));
   clear_stale_error();
@@ -244,8 +250,10 @@ int moe_grouped_ffn_bwd(const moe_cfg* cfg, const void* x_perm, const int32_t* o
   MOE_TRY(need(offsets, z.E1, 4));
   MOE_TRY(need(W1, z.Edf, 16));
   MOE_TRY(need(W2, z.Edf, 16));
-  MOE_TRY(need(A, z.Rf, 16));
-  MOE_TRY(need(H, z.Rf, 16));
+  if (saves_ah(c)) {
+    MOE_TRY(need(A, z.Rf, 16));
+    MOE_TRY(need(H, z.Rf, 16));
+  }
   MOE_TRY(need(dYp, z.Rd, 16));
   MOE_TRY(need(dXp, z.Rd, 16));
   MOE_TRY(need(dW1, z.Edf, 16));
@@ -318,8 +326,10 @@ static int check_ctx(const moe_cfg& c, const moe_ctx* x) {
   MOE_TRY(need(x->row_of, z.Tk, 4));
   MOE_TRY(need(x->src_of, z.Rmax * 4, 4));
   MOE_TRY(need(x->x_perm, z.Rd, 16));
-  MOE_TRY(need(x->A, z.Rf, 16));
-  MOE_TRY(need(x->H, z.Rf, 16));
+  if (saves_ah(c)) {
+    MOE_TRY(need(x->A, z.Rf, 16));
+    MOE_TRY(need(x->H, z.Rf, 16));
+  }
   MOE_TRY(need(x->Y, z.Rd, 16));
   if (x->aux) MOE_TRY(need(x->aux, 2 * sizeof(float), 4));
   return MOE_OK;

@@ -153,7 +153,7 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 //   dxe      [T, d] f32         unpermute-sum of dXp (router backward)
 struct WsLayout {
   size_t wrT, zf, wl_count, wl_tok, wl_n, wl_e, gpart, perm_blk, tiles, aux_part, dz, dzb, wrp,
-      dwr_part, db_part, dgate, dYp, dA, dXp, dxe, total;
+      dwr_part, db_part, dgate, dYp, dA, dXp, dxe, rA, rH, total;
   int nblk_perm;
   int nblk_aux;
   int nblk_dz;
@@ -229,6 +229,10 @@ inline WsLayout ws_layout(const moe_cfg& c) {
   L.dA = take((size_t)Rmax * c.f * s);
   L.dXp = take((size_t)Rmax * c.d * s);
   L.dxe = take((size_t)c.T * c.d * 4);
+  // A and H of the recomputation mode (kept in the workspace, not saved)
+  const bool rec = (c.flags & MOE_FLAG_RECOMPUTE) != 0;
+  L.rA = take(rec ? (size_t)Rmax * c.f * s : 0);
+  L.rH = take(rec ? (size_t)Rmax * c.f * s : 0);
   L.total = off;
   return L;
 }

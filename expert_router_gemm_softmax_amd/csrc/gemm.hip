@@ -197,7 +197,7 @@ __device__ __forceinline__ void epi_write8(const GemmArgs& g, int64_t o, float (
     st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
   } else if constexpr (EPI == EPI_GELU) {
     const u32x4 ab = St<uint16_t>::pack(v8);
-    st16(static_cast<uint16_t*>(g.C) + o, ab);
+    if (g.C != nullptr) st16(static_cast<uint16_t*>(g.C) + o, ab);  // NULL: H only
     float a8[8];
     St<uint16_t>::unpack(ab, a8);
 #pragma unroll
@@ -631,7 +631,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       const int64_t o = cbase + (int64_t)row * g.ldc + col;
       if constexpr (EPI == EPI_STORE || EPI == EPI_F32) C[o] = acc[i][j];
       else if constexpr (EPI == EPI_ADDF32) C[o] = acc[i][j] + Aux[o];
-      else if constexpr (EPI == EPI_GELU) { C[o] = acc[i][j]; C2[o] = gelu_tanh(acc[i][j]); }
+      else if constexpr (EPI == EPI_GELU) {
+        if (C != nullptr) C[o] = acc[i][j];
+        C2[o] = gelu_tanh(acc[i][j]);
+      }
       else C[o] = acc[i][j] * gelu_tanh_grad(Aux[o]);
     }
   }
@@ -795,6 +798,11 @@ int launch_ffn_fwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
   int32_t* tiles = ws_ptr<int32_t>(ws, L.tiles);
   int rc = schedule(c, offsets, tiles, s);
   if (rc != MOE_OK) return rc;
+  const bool rec = (c.flags & MOE_FLAG_RECOMPUTE) != 0;
+  if (rec) {
+    A = nullptr;  // not kept
+    H = ws_ptr<void>(ws, L.rH);
+  }
   GemmArgs g{};
   g.offsets = offsets;
   g.tiles = tiles;
@@ -829,6 +837,20 @@ int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
   if (rows_max(c) > 0) {
     rc = schedule(c, offsets, tiles, s);
     if (rc != MOE_OK) return rc;
+    if (c.flags & MOE_FLAG_RECOMPUTE) {
+      // recompute A and H exactly as the forward does (same kernel, inputs
+      // and tile schedule: bitwise the forward's values)
+      void* rA = ws_ptr<void>(ws, L.rA);
+      void* rH = ws_ptr<void>(ws, L.rH);
+      g.A = x_perm; g.B = W1; g.C = rA; g.C2 = rH;
+      g.N = c.f; g.K = c.d; g.lda = c.d; g.ldb = c.f; g.ldc = c.f;
+      g.b_estride = (int64_t)c.d * c.f;
+      rc = run_gemm<MODE_ROW, false, EPI_GELU>(MOE_KERNEL_GEMM_RECOMPUTE, c, g, s);
+      if (rc != MOE_OK) return rc;
+      g.C2 = nullptr;
+      A = rA;
+      H = rH;
+    }
     // dA = (dYp W2^T) * gelu'(A): B = W2[e] as [N=f][K=d]
     g.A = dYp; g.B = W2; g.C = dA; g.Aux = A;
     g.N = c.f; g.K = c.d; g.lda = c.d; g.ldb = c.d; g.ldc = c.f;

@@ -17,7 +17,9 @@ class MoeLayer:
     With diagnostics (the default when cfg.aux_coeff > 0) every forward also
     writes saved["aux"] = [load-balancing loss, drop rate]; the expert loads
     are saved["counts"].  The backward adds the loss's gradient whenever
-    cfg.aux_coeff > 0.
+    cfg.aux_coeff > 0.  Under MOE_FLAG_RECOMPUTE (make_cfg(recompute=True))
+    A and H are not saved (saved["A"] = saved["H"] = None): the forward keeps
+    them in the workspace and the backward recomputes them.
     """
 
     def __init__(self, cfg: B.MoeCfg, Wr, b, W1, W2, device="cuda", diagnostics=None):
@@ -36,6 +38,8 @@ class MoeLayer:
             offsets=e(E + 1, dt=torch.int32), row_of=e(T, k, dt=torch.int32),
             src_of=e(self.Rmax, dt=torch.int32), x_perm=e(self.Rmax, d),
             A=e(self.Rmax, f), H=e(self.Rmax, f), Y=e(self.Rmax, d))
+        if cfg.flags & B.MOE_FLAG_RECOMPUTE:
+            self.saved["A"] = self.saved["H"] = None
         if diagnostics is None:
             diagnostics = cfg.aux_coeff > 0
         self.saved["aux"] = e(2, dt=torch.float32) if diagnostics else None

@@ -66,6 +66,18 @@ typedef enum { MOE_FP32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 #define MOE_NO_CAPACITY (-1)
 
+/* moe_cfg.flags bits.
+ * MOE_FLAG_RECOMPUTE: selective recomputation ("GPU expert parallel",
+ * section "Recomputation re-runs the dispatch unless you save the
+ * permutation": keep the routing map, drop the MLP hidden states).  The
+ * forward keeps A and H only in the workspace (A is not stored at all) and
+ * the backward recomputes them from x_perm with the same kernel, one extra
+ * grouped GEMM; the A and H arguments of moe_grouped_ffn,
+ * moe_grouped_ffn_bwd and moe_ctx are then ignored and may be NULL.
+ * Results are bitwise those of the default mode; the saved state shrinks
+ * by 2 Rmax f s bytes and the workspace grows by as much. */
+#define MOE_FLAG_RECOMPUTE 1u
+
 /* hipStream_t, passed opaquely so that this header needs no HIP headers. */
 typedef void* moe_stream_t;
 
@@ -80,7 +92,7 @@ typedef struct moe_cfg {
   int64_t capacity;   /* per-expert capacity C >= 0, or MOE_NO_CAPACITY */
   float route_margin; /* router certification margin (logit units); <= 0
                          selects the default 1e-3.  See moe_route. */
-  uint32_t flags;     /* must be 0 */
+  uint32_t flags;     /* MOE_FLAG_* bits; others must be 0 */
   float aux_coeff;    /* coefficient alpha >= 0 of the auxiliary
                          load-balancing loss (0 = none); see moe_router_aux.
                          When > 0, moe_route_bwd and moe_layer_bwd add its
@@ -157,7 +169,8 @@ MOE_API int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx,
  *   H = gelu_tanh(A)      [Rmax,f] s   (from the stored A)
  *   Y = H W2[e]           [Rmax,d] s
  * W1 [E,d,f] s, W2 [E,f,d] s.  offsets lives on the device and is never
- * read back by the host.  Workspace as above. */
+ * read back by the host.  Under MOE_FLAG_RECOMPUTE, A and H are ignored
+ * (H lives in the workspace).  Workspace as above. */
 MOE_API int moe_grouped_ffn(const moe_cfg* cfg, const void* x_perm,
                     const int32_t* offsets, const void* W1, const void* W2,
                     void* A, void* H, void* Y, void* ws, size_t ws_bytes,
@@ -201,7 +214,9 @@ MOE_API int moe_combine_bwd(const moe_cfg* cfg, const void* dOut, const void* Y,
                     const int32_t* row_of, const float* gate, void* dYp,
                     float* dgate, moe_stream_t stream);
 
-/* B4+B3 grouped expert FFN backward; per expert e over its rows:
+/* B4+B3 grouped expert FFN backward; per expert e over its rows (under
+ * MOE_FLAG_RECOMPUTE, A and H are first recomputed from x_perm into the
+ * workspace, and the A and H arguments are ignored):
  *   dH  = dYp W2[e]^T               (fp32, not stored)
  *   dA  = RN_s(dH * gelu_tanh'(A))  (stored in the workspace)
  *   dXp = dA W1[e]^T                [Rmax,d] s
@@ -252,7 +267,7 @@ typedef struct moe_weights {
 /* Saved forward state, all caller-owned device buffers.  The small integer
  * routing map is kept and reused by backward instead of routing again
  * (section "Recomputation re-runs the dispatch unless you save the
- * permutation"). */
+ * permutation").  A and H may be NULL under MOE_FLAG_RECOMPUTE. */
 typedef struct moe_ctx {
   float* probs;     /* [T,E] float */
   int32_t* idx;     /* [T,k] */
@@ -318,7 +333,8 @@ typedef enum {
   MOE_KERNEL_PERMUTE_COPY = 18,  /* x -> x_perm row copy */
   MOE_KERNEL_ROUTE_LOGITS = 19,  /* fast router logits x Wr (GEMM) */
   MOE_KERNEL_ROUTE_AUX = 20,     /* load-balancing loss and drop rate */
-  MOE_KERNEL_COUNT_ = 21
+  MOE_KERNEL_GEMM_RECOMPUTE = 21, /* A, H recomputed in backward (MOE_FLAG_RECOMPUTE) */
+  MOE_KERNEL_COUNT_ = 22
 } moe_kernel_id;
 
 MOE_API int moe_prof_arm(int kernel_id, int max_launches);

@@ -164,12 +164,14 @@ def test_balancing_gradient_alone(M, dt):
     assert np.all(to_f64(res["dW1"]) == 0) and np.all(to_f64(res["dW2"]) == 0)
 
 
-def test_step_entry_points_equal_the_layer_entry_points(M):
+@pytest.mark.parametrize("recompute", [False, True], ids=["save", "recompute"])
+def test_step_entry_points_equal_the_layer_entry_points(M, recompute):
     """moe_route .. moe_route_bwd called one by one give bitwise the layer's
-    results (same kernels, same order)."""
+    results (same kernels, same order); in the recomputation mode with no A
+    and H buffers at all."""
     import torch
     w, inp = make_case(700, 128, 8, 2, 160, "bf16", 1.0, "normal", seed=7, aux_coeff=0.05)
-    res = run_layer(M, w, inp)
+    res = run_layer(M, w, inp, recompute=recompute)
     cfg, d, L = res["_cfg"], res["_dev"], res["_layer"]
     T, E, k = w.T, w.E, w.k
     Rmax = M.moe_rows_max(cfg)
@@ -183,6 +185,8 @@ def test_step_entry_points_equal_the_layer_entry_points(M):
     aux = z(2, dt=torch.float32)
     M.moe_router_aux(cfg, probs, counts, offsets, aux, ws)
     A, H, Y = z(Rmax, w.f), z(Rmax, w.f), z(Rmax, w.d)
+    if recompute:
+        A = H = None
     M.moe_grouped_ffn(cfg, xp, offsets, d["W1"], d["W2"], A, H, Y, ws)
     out = z(T, w.d)
     M.moe_combine(cfg, Y, row_of, gate, out)
@@ -206,6 +210,9 @@ def test_step_entry_points_equal_the_layer_entry_points(M):
         assert torch.equal(a, b), name
     for name, a, b in [("x_perm", xp, res["x_perm"]), ("A", A, res["A"]),
                        ("Y", Y, res["Y"]), ("src_of", src_of, res["src_of"])]:
+        if a is None:
+            assert b is None, name
+            continue
         assert torch.equal(a[:R], b[:R]), name
     # unpermute-sum against the oracle definition on the GPU's own dXp
     fw = O.layer_fwd(inp, w)
@@ -217,6 +224,50 @@ def test_step_entry_points_equal_the_layer_entry_points(M):
         m = fw["row_of"][:, j] >= 0
         gn[m, j] = np.sqrt(((dOut[m] * fw["Y"][fw["row_of"][m, j]]) ** 2).sum(axis=1))
     assert_close("dgate", to_f64(dg), bw["dgate"], terms_tol(gn, "bf16"))
+
+
+RECOMPUTE_CASES = [
+    # T, d, E, k, f, dtype, cf, bias, alpha
+    (1000, 264, 6, 2, 200, "bf16", 1.1, "zero", 0.0),   # ragged K and N tails, drops
+    (300, 36, 5, 2, 52, "f32", 0.9, "normal", 0.01),    # fp32, balancing loss on
+    (260, 48, 130, 8, 40, "bf16", None, "normal", 0.0),  # many experts, empty ones
+]
+
+SAME_IN_BOTH_MODES = ("probs", "idx", "gate", "counts", "offsets", "row_of", "out", "dX",
+                      "dWr", "db", "dW1", "dW2", "aux", "aux1")
+
+
+@pytest.mark.parametrize("case", RECOMPUTE_CASES,
+                         ids=lambda c: "T{}E{}k{}{}".format(c[0], c[2], c[3], c[5]))
+def test_recompute_mode_is_bitwise_the_save_mode(M, case):
+    """Selective recomputation (A and H not saved, recomputed in backward)
+    changes memory, not results: every output is bitwise that of the save
+    mode, and so within the oracle's tolerances."""
+    import torch
+    T, d, E, k, f, dt, cf, bias, alpha = case
+    w, inp = make_case(T, d, E, k, f, dt, cf, bias, seed=T + 2, aux_coeff=alpha)
+    a = run_layer(M, w, inp)
+    b = run_layer(M, w, inp, recompute=True)
+    assert b["A"] is None and b["H"] is None
+    for key in SAME_IN_BOTH_MODES:
+        assert torch.equal(a[key], b[key]), key
+    R = int(to_int(a["offsets"])[-1])
+    for key in ("src_of", "x_perm", "Y"):
+        assert torch.equal(a[key][:R], b[key][:R]), key
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    check_layer_full(b, fw, bw, w)
+
+
+@pytest.mark.parametrize("name", ["C1", "C2"])
+def test_recompute_mode_named_workloads_bitwise(M, name):
+    import torch
+    w = W.get(name)
+    inp = W.make_inputs(w, seed=0)
+    a = run_layer(M, w, inp)
+    b = run_layer(M, w, inp, recompute=True)
+    for key in SAME_IN_BOTH_MODES:
+        assert torch.equal(a[key], b[key]), key
 
 
 def test_runs_are_bitwise_deterministic(M):

@@ -103,8 +103,10 @@ def test_bad_dtype_and_flags():
     c.dtype = 7
     assert M.moe_check_cfg(c) == B.MOE_ERR_DTYPE
     c = M.make_cfg(16, 64, 8, 2, 64, "bf16")
-    c.flags = 1
+    c.flags = 2
     assert M.moe_check_cfg(c) == B.MOE_ERR_ARG
+    c.flags = B.MOE_FLAG_RECOMPUTE
+    assert M.moe_check_cfg(c) == B.MOE_OK
     c = M.make_cfg(16, 12, 8, 2, 64, "f32")   # 48-byte rows: aligned for fp32
     assert M.moe_check_cfg(c) == B.MOE_OK
 
@@ -154,6 +156,26 @@ def test_cfg_struct_layout_matches_header():
     assert B.MoeCfg.aux_coeff.offset == 48
     # MoeCtx: eleven tensors, then the optional diagnostics output
     assert B.MoeCtx.aux.offset == 11 * ctypes.sizeof(ctypes.c_void_p)
+
+
+def test_recompute_mode_moves_a_and_h_into_the_workspace():
+    base = M.make_cfg(1000, 64, 8, 2, 96, "bf16", capacity=300)
+    rec = M.make_cfg(1000, 64, 8, 2, 96, "bf16", capacity=300, recompute=True)
+    Rmax = M.moe_rows_max(base)
+    grow = M.moe_workspace_bytes(rec) - M.moe_workspace_bytes(base)
+    # two [Rmax, f] bf16 regions, each rounded up to 256 bytes
+    assert 2 * Rmax * 96 * 2 <= grow <= 2 * Rmax * 96 * 2 + 512
+    ws = M.moe_workspace_bytes(rec)
+    # A and H may be NULL under the flag (validation then stops at ws_bytes)
+    ffn = lambda cfg, A, H: B.lib.moe_grouped_ffn(ctypes.byref(cfg), _A, _A, _A, _A, A, H,
+                                                  _A, _A, 10, None)
+    assert ffn(base, None, None) == B.MOE_ERR_ARG
+    assert ffn(rec, None, None) == B.MOE_ERR_WORKSPACE
+    bwd = lambda cfg: B.lib.moe_grouped_ffn_bwd(ctypes.byref(cfg), _A, _A, _A, _A, None, None,
+                                                _A, _A, _A, _A, _A, 10, None)
+    assert bwd(base) == B.MOE_ERR_ARG
+    assert bwd(rec) == B.MOE_ERR_WORKSPACE
+    assert ws > 0
 
 
 @pytest.mark.parametrize("coeff", [-0.01, float("nan"), float("inf")])
