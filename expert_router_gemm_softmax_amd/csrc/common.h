@@ -165,7 +165,7 @@ constexpr int kPermTokens = 256;  // tokens per permute block
 // per CU (256) of up to 256 x 256
 constexpr size_t kGemmPartFloats = (size_t)256 * 256 * 256;
 constexpr int kDzTokens = 16;     // tokens per router-backward dz block
-constexpr int kAuxTokens = 64;    // tokens per block of the balancing-loss column sums
+constexpr int kAuxTokens = 32;    // tokens per block of the balancing-loss column sums
 
 inline int64_t rows_max(const moe_cfg& c) {
   const int64_t tk = c.T * c.k;

@@ -10,10 +10,11 @@
 // The expert loads are counts itself.
 //
 // Two kernels: per-block column sums of probs over kAuxTokens tokens (one
-// thread per expert, rows read coalesced across experts), then one block
-// that sums the partials in block order, forms the loss with a fixed tree
-// over experts (fp64) and writes aux[0] = L, aux[1] = drop rate.  The sums
-// have a fixed order, so the result is deterministic.
+// thread per expert, rows read coalesced across experts, all loads in
+// flight), then one block that sums the partials per expert in fp64 (one
+// wave per expert, lane-strided), forms the loss with a fixed tree over
+// experts and writes aux[0] = L, aux[1] = drop rate.  Every sum has a fixed
+// order, so the result is deterministic.
 #include "common.h"
 
 namespace moe {
@@ -27,40 +28,40 @@ __global__ __launch_bounds__(256) void route_aux_part_kernel(const float* __rest
   const int64_t t0 = (int64_t)blockIdx.x * kAuxTokens;
   const int n = (int)(T_ - t0 < kAuxTokens ? T_ - t0 : kAuxTokens);
   const float* p = probs + t0 * E + e;
+  // every row's load in flight at once, then the sum in token order
+  float v[kAuxTokens];
+#pragma unroll
+  for (int q = 0; q < kAuxTokens; ++q) v[q] = q < n ? p[(int64_t)q * E] : 0.0f;
   float s = 0.0f;
-  int t = 0;
-  // eight rows' loads in flight per step; summed in token order
-  for (; t + 8 <= n; t += 8) {
-    float v[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = p[(int64_t)(t + q) * E];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) s += v[q];
-  }
-  for (; t < n; ++t) s += p[(int64_t)t * E];
+  for (int q = 0; q < kAuxTokens; ++q) s += v[q];
   part[(int64_t)e * gridDim.x + blockIdx.x] = s;
 }
 
-__global__ __launch_bounds__(256) void route_aux_final_kernel(
+// One block of 1024 threads: wave w sums the partials of experts w, w+16,
+// ... (lane-strided in fp64, then the fixed wave tree), then a fixed tree
+// over experts forms the loss.
+__global__ __launch_bounds__(1024) void route_aux_final_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, float* __restrict__ aux, int nblk, int64_t T_,
     int E, int k, float coeff) {
   __shared__ double red[256];
-  const int e = threadIdx.x;
-  double term = 0.0;
-  if (e < E) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x < 256) red[threadIdx.x] = 0.0;
+  __syncthreads();
+  for (int e = w; e < E; e += 16) {
     const float* pe = part + (int64_t)e * nblk;
     double s = 0.0;
-    for (int b = 0; b < nblk; ++b) s += (double)pe[b];
-    term = (double)counts[e] * s;  // counts_e * T P_e
+    for (int b = lane; b < nblk; b += kWave) s += (double)pe[b];
+    s = wave_sum_d(s);
+    if (lane == 0) red[e] = (double)counts[e] * s;  // counts_e * T P_e
   }
-  red[e] = term;
   __syncthreads();
   for (int h = 128; h > 0; h >>= 1) {
-    if (e < h) red[e] += red[e + h];
+    if (threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
     __syncthreads();
   }
-  if (e == 0) {
+  if (threadIdx.x == 0) {
     const double tk = (double)T_ * (double)k;
     aux[0] = (float)((double)coeff * (double)E * red[0] / (tk * (double)T_));
     aux[1] = (float)(1.0 - (double)offsets[E] / tk);
@@ -87,7 +88,7 @@ int launch_route_aux(const moe_cfg& c, const float* probs, const int32_t* counts
   MOE_LAUNCH_NP(MOE_KERNEL_ROUTE_AUX,
                 route_aux_part_kernel<<<L.nblk_aux, 256, 0, s>>>(probs, part, c.T, c.E));
   MOE_LAUNCH_NP(MOE_KERNEL_ROUTE_AUX,
-                route_aux_final_kernel<<<1, 256, 0, s>>>(part, counts, offsets, aux,
+                route_aux_final_kernel<<<1, 1024, 0, s>>>(part, counts, offsets, aux,
                                                          L.nblk_aux, c.T, c.E, c.k,
                                                          c.aux_coeff));
   prof_end(MOE_KERNEL_ROUTE_AUX, s);

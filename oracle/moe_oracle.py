@@ -54,6 +54,14 @@ Readings taken where the pages are silent (numbered as in the design doc; R8
      mean router probability of expert e over the tokens.  f is piecewise
      constant, so the gradient flows through P only and joins dgate before
      the softmax backward.  Drop rate = 1 - R / (T k).
+  R17 gate renormalisation (an option; the pages fix no gate normalisation):
+     g[t,j] = p[t,idx_j] / sum_i p[t,idx_i] over the k selected experts,
+     before the capacity drop; a drop does not renormalise again (R6).
+  R18 capacity priority (an option; the pages do not say which assignments
+     of a full expert go first): 'slot' walks the assignments slot-major,
+     every token's first choice before any second choice, (j, t) in
+     lexicographic order, instead of token-major (t, j).  Rows of an expert
+     are laid out in that walk order.
 
 Every floating-point result here is fp64 arithmetic on exactly converted
 inputs followed by one rounding at the storage point; ``exact=True`` turns
@@ -152,26 +160,32 @@ def capacity(T: int, k: int, E: int, cf: Optional[float]) -> Optional[int]:
     return math.ceil(Fraction(str(cf)) * T * k / E)
 
 
-def assign(idx: np.ndarray, E: int, C: Optional[int]):
-    """Capacity drop and the permutation map (R5, R7).
+def assign(idx: np.ndarray, E: int, C: Optional[int], priority: str = "token"):
+    """Capacity drop and the permutation map (R5, R7, R18).
 
-    Walk the T*k assignments in token order; pos = how many earlier tokens
-    chose the same expert; kept iff pos < C.  Returns
+    Walk the T*k assignments in token-major order (t, j), or slot-major
+    (j, t) for priority 'slot'; pos = how many earlier assignments in the
+    walk chose the same expert; kept iff pos < C.  Returns
       counts[E]   routed assignments per expert (before the drop),
       offsets[E+1] exclusive scan of the kept counts (offsets[E] = R),
       row_of[T,k] row of (t,j) in the permuted buffer, or -1 if dropped,
       src_of[R]   t*k + j of the assignment stored in each row.
     """
     T, k = idx.shape
+    if priority == "token":
+        walk = ((t, j) for t in range(T) for j in range(k))
+    elif priority == "slot":
+        walk = ((t, j) for j in range(k) for t in range(T))
+    else:
+        raise ValueError(priority)
     counts = np.zeros(E, dtype=np.int64)
     pos = np.full((T, k), -1, dtype=np.int64)
-    for t in range(T):
-        for j in range(k):
-            e = int(idx[t, j])
-            p = counts[e]
-            counts[e] = p + 1
-            if C is None or p < C:
-                pos[t, j] = p
+    for t, j in walk:
+        e = int(idx[t, j])
+        p = counts[e]
+        counts[e] = p + 1
+        if C is None or p < C:
+            pos[t, j] = p
     kept = counts if C is None else np.minimum(counts, C)
     offsets = np.zeros(E + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(kept)
@@ -269,19 +283,41 @@ def unpermute_bwd(dXp, row_of) -> np.ndarray:
     return acc
 
 
-def router_dz(probs, idx, row_of, dg, aux=None) -> np.ndarray:
+def renorm_gates(probs, idx) -> np.ndarray:
+    """Gates renormalised over the selected experts (R17):
+    g[t,j] = p[t,idx_j] / sum_i p[t,idx_i] (fp64; the caller rounds)."""
+    sel = np.take_along_axis(np.asarray(probs, np.float64),
+                             np.asarray(idx).astype(np.int64), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def router_dz(probs, idx, row_of, dg, aux=None, renorm: bool = False) -> np.ndarray:
     """Softmax backward: dp[t, idx[t,j]] = dgate[t,j] for kept j (else 0),
     plus the load-balancing gradient aux[e] (aux_dp) when given;
-    dz = p * (dp - sum_e p dp)."""
+    dz = p * (dp - sum_e p dp).  With renormalised gates (R17) the gate
+    gradient first goes through g_j = p_j / S, S = sum_i p_i over the
+    selected experts: dL/dp_j = (dgate_j - sum_i g_i dgate_i) / S for every
+    selected j, dropped ones included (their own dgate is 0)."""
     probs = np.asarray(probs, np.float64)
     T, E = probs.shape
     dp = np.zeros((T, E), dtype=np.float64)
     if aux is not None:
         dp += np.asarray(aux, np.float64)[None, :]
     row_of = np.asarray(row_of)
-    for j in range(row_of.shape[1]):
-        m = row_of[:, j] >= 0
-        dp[np.nonzero(m)[0], np.asarray(idx)[m, j]] += np.asarray(dg)[m, j]
+    idx64 = np.asarray(idx).astype(np.int64)
+    dg = np.asarray(dg, np.float64)
+    if renorm:
+        sel = np.take_along_axis(probs, idx64, axis=1)
+        S = sel.sum(axis=1, keepdims=True)
+        g = sel / S
+        dsel = (dg - (g * dg).sum(axis=1, keepdims=True)) / S
+        rows = np.arange(T)
+        for j in range(idx64.shape[1]):
+            dp[rows, idx64[:, j]] += dsel[:, j]
+    else:
+        for j in range(row_of.shape[1]):
+            m = row_of[:, j] >= 0
+            dp[np.nonzero(m)[0], idx64[m, j]] += dg[m, j]
     s = (probs * dp).sum(axis=1, keepdims=True)
     return probs * (dp - s)
 
@@ -328,9 +364,12 @@ def route(inp: Dict[str, np.ndarray], w, exact: bool = False):
     z = router_logits(x, to_f64(inp["Wr"]), to_f64(inp["b"]), round32=not exact)
     probs = r32(softmax(z))
     idx = topk_select(z, w.k)
-    gate = np.take_along_axis(probs, idx.astype(np.int64), axis=1)
+    if w.renorm:
+        gate = r32(renorm_gates(probs, idx))
+    else:
+        gate = np.take_along_axis(probs, idx.astype(np.int64), axis=1)
     C = capacity(w.T, w.k, w.E, w.cf)
-    counts, offsets, row_of, src_of = assign(idx, w.E, C)
+    counts, offsets, row_of, src_of = assign(idx, w.E, C, w.priority)
     return dict(x=x, z=z, probs=probs, idx=idx, gate=gate, C=C, counts=counts,
                 offsets=offsets, row_of=row_of, src_of=src_of)
 
@@ -394,7 +433,7 @@ def layer_bwd(inp: Dict[str, np.ndarray], w, fw: Dict[str, np.ndarray],
     if w.kind == "layer":
         dXe = r32(unpermute_bwd(dXp, fw["row_of"]))
         aux = aux_dp(fw["counts"], w.T, w.k, w.aux_coeff) if w.aux_coeff > 0 else None
-        dz = router_dz(fw["probs"], fw["idx"], fw["row_of"], dg, aux)
+        dz = router_dz(fw["probs"], fw["idx"], fw["row_of"], dg, aux, w.renorm)
         dX, dWr, db = route_bwd(fw["x"], to_f64(inp["Wr"]), dz, dXe, rnd, r32)
         bw.update(dXe=dXe, dz=dz, dX=dX, dWr=dWr, db=db)
     return bw

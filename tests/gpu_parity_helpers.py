@@ -212,8 +212,8 @@ def check_aux(name, aux, probs, fw, w, coeff):
     L = coeff E sum_e f_e P_e with sum_e f_e = 1 moves by at most
     1e-5 L + 1e-6 coeff E.  Against the oracle's formula on the GPU's own
     probabilities the only error left is the kernel's summation: fp32
-    partial sums over 64 tokens (relative error <= 63 * 2^-24) summed in
-    fp64, then one rounding to fp32 -- 4e-6 relative.
+    partial sums over at most 64 tokens (relative error <= 63 * 2^-24)
+    summed in fp64, then one rounding to fp32 -- 4e-6 relative.
     Drop rate: exact integers, one rounding to fp32 (<= 2^-24 < 1e-7)."""
     a = to_f64(aux)
     ref = O.aux_loss(fw["probs"], fw["counts"], w.k, coeff)

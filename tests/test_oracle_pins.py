@@ -152,13 +152,20 @@ def test_capacity_closed_forms():
     assert O.capacity(10, 2, 4, 0.0) == 0
 
 
-def _brute_force_maps(idx, E, C):
-    """pos of (t,j) = number of (t',j') with t' < t and the same expert,
-    by direct pairwise comparison (no running counters)."""
+def _brute_force_maps(idx, E, C, priority="token"):
+    """pos of (t,j) = number of (t',j') before it with the same expert, by
+    direct pairwise comparison (no running counters).  'token': before
+    means t' < t (a token's experts are distinct); 'slot': j' < j, or
+    j' = j and t' < t."""
     T, k = idx.shape
     flat_e = idx.reshape(-1)
     flat_t = np.repeat(np.arange(T), k)
-    pos = np.array([np.sum((flat_e == flat_e[a]) & (flat_t < flat_t[a]))
+    flat_j = np.tile(np.arange(k), T)
+    if priority == "token":
+        before = lambda a: flat_t < flat_t[a]
+    else:
+        before = lambda a: (flat_j < flat_j[a]) | ((flat_j == flat_j[a]) & (flat_t < flat_t[a]))
+    pos = np.array([np.sum((flat_e == flat_e[a]) & before(a))
                     for a in range(T * k)]).reshape(T, k)
     counts = np.bincount(flat_e, minlength=E)
     kept_mask = pos < (C if C is not None else T * k + 1)
@@ -193,6 +200,67 @@ def test_assign_matches_pairwise_brute_force_and_invariants(T, E, k, C):
         toks = src_of[offsets[e]:offsets[e + 1]] // k
         assert np.all(np.diff(toks) > 0)
         assert np.all(idx.reshape(-1)[src_of[offsets[e]:offsets[e + 1]]] == e)
+
+
+@pytest.mark.parametrize("T,E,k,C", [(64, 8, 2, 12), (40, 5, 3, None), (30, 6, 2, 0),
+                                     (1, 3, 2, 1), (33, 16, 8, 5), (80, 4, 3, 30)])
+def test_slot_priority_matches_pairwise_brute_force(T, E, k, C):
+    rng = np.random.default_rng(T * 7 + k)
+    z = rng.standard_normal((T, E)) + np.linspace(2, 0, E)
+    idx = O.topk_select(z, k)
+    counts, offsets, row_of, src_of = O.assign(idx, E, C, "slot")
+    bc, bo, br = _brute_force_maps(idx, E, C, "slot")
+    np.testing.assert_array_equal(counts, bc)
+    np.testing.assert_array_equal(offsets, bo)
+    np.testing.assert_array_equal(row_of, br)
+    cap = C if C is not None else T * k
+    np.testing.assert_array_equal(np.diff(offsets), np.minimum(counts, cap))
+    for e in range(E):   # rows of an expert in slot-major order (j, then t)
+        a = src_of[offsets[e]:offsets[e + 1]]
+        key = (a % k) * T + a // k
+        assert np.all(np.diff(key) > 0)
+
+
+def test_slot_priority_hand_example():
+    # token 0 picks (0, 1), token 1 picks (1, 0); C = 1.  Token-major keeps
+    # both choices of token 0; slot-major keeps both first choices.
+    idx = np.array([[0, 1], [1, 0]])
+    _, off_t, row_t, _ = O.assign(idx, 2, 1, "token")
+    _, off_s, row_s, _ = O.assign(idx, 2, 1, "slot")
+    assert row_t.tolist() == [[0, 1], [-1, -1]]
+    assert row_s.tolist() == [[0, -1], [1, -1]]
+    assert off_t.tolist() == off_s.tolist() == [0, 1, 2]
+
+
+def test_slot_priority_with_one_expert_per_token_is_token_priority():
+    rng = np.random.default_rng(5)
+    idx = O.topk_select(rng.standard_normal((50, 6)), 1)
+    for C in (None, 3, 0):
+        a = O.assign(idx, 6, C, "token")
+        b = O.assign(idx, 6, C, "slot")
+        for u, v in zip(a, b):
+            np.testing.assert_array_equal(u, v)
+
+
+def test_renormalised_gates_closed_forms():
+    rng = np.random.default_rng(6)
+    z = rng.standard_normal((20, 7))
+    p = O.softmax(z)
+    for k in (1, 2, 4):
+        idx = O.topk_select(z, k)
+        g = O.renorm_gates(p, idx)
+        np.testing.assert_allclose(g.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+        if k == 1:
+            np.testing.assert_array_equal(g, 1.0)
+        # only ratios of the selected probabilities matter
+        np.testing.assert_allclose(O.renorm_gates(3.0 * p, idx), g, rtol=1e-15)
+        # ordered like the selection (z descending)
+        assert np.all(np.diff(g, axis=1) <= 0)
+    # all experts selected: the probabilities themselves
+    idx = O.topk_select(z, 7)
+    np.testing.assert_allclose(O.renorm_gates(p, idx),
+                               np.take_along_axis(p, idx.astype(np.int64), axis=1),
+                               rtol=1e-14)
 
 
 def test_permute_then_inverse_permute_is_identity_on_kept_tokens():
@@ -308,14 +376,20 @@ def _min_topk_gap(z, k):
     return np.min(zs[:, :kk - 1] - zs[:, 1:kk]) if kk > 1 else np.inf
 
 
-@pytest.mark.parametrize("T,d,E,k,f,cf,aux", [(10, 4, 3, 2, 5, None, 0.0),
-                                              (12, 5, 4, 2, 6, 0.75, 0.0),
-                                              (7, 3, 4, 1, 4, 1.0, 0.0),
-                                              (6, 4, 5, 3, 3, None, 0.0),
-                                              (12, 5, 4, 2, 6, 0.75, 0.3),
-                                              (9, 4, 5, 1, 3, None, 2.0)])
-def test_backward_matches_central_finite_differences(T, d, E, k, f, cf, aux):
-    w = W.custom(T, d, E, k, f, cf=cf, aux_coeff=aux)
+@pytest.mark.parametrize("T,d,E,k,f,cf,aux,renorm,prio", [
+    (10, 4, 3, 2, 5, None, 0.0, False, "token"),
+    (12, 5, 4, 2, 6, 0.75, 0.0, False, "token"),
+    (7, 3, 4, 1, 4, 1.0, 0.0, False, "token"),
+    (6, 4, 5, 3, 3, None, 0.0, False, "token"),
+    (12, 5, 4, 2, 6, 0.75, 0.3, False, "token"),
+    (9, 4, 5, 1, 3, None, 2.0, False, "token"),
+    (12, 5, 4, 2, 6, 0.75, 0.0, True, "token"),    # renormalised gates with drops
+    (6, 4, 5, 3, 3, None, 0.3, True, "token"),     # renormalised, balancing loss
+    (12, 5, 4, 2, 6, 0.75, 0.0, False, "slot"),    # slot-major priority with drops
+    (10, 4, 4, 3, 5, 0.8, 0.0, True, "slot"),
+])
+def test_backward_matches_central_finite_differences(T, d, E, k, f, cf, aux, renorm, prio):
+    w = W.custom(T, d, E, k, f, cf=cf, aux_coeff=aux, renorm=renorm, priority=prio)
     seed = 0
     while True:      # pick a seed whose routing margins exceed the step by far
         inp = _exact_inputs(T, d, E, k, f, seed=seed)
@@ -344,12 +418,13 @@ def test_backward_matches_central_finite_differences(T, d, E, k, f, cf, aux):
                                    err_msg=name)
 
 
-def test_backward_matches_torch_autograd_in_fp64():
+@pytest.mark.parametrize("renorm", [False, True])
+def test_backward_matches_torch_autograd_in_fp64(renorm):
     """Independent library cross-check: the same layer written with torch
     autograd (routing and drops taken from the oracle, then held fixed)."""
     torch = pytest.importorskip("torch")
     T, d, E, k, f = 16, 6, 5, 2, 7
-    w = W.custom(T, d, E, k, f, cf=1.0)
+    w = W.custom(T, d, E, k, f, cf=1.0, renorm=renorm)
     inp = _exact_inputs(T, d, E, k, f, seed=11)
     fw = O.layer_fwd(inp, w, exact=True)
     bw = O.layer_bwd(inp, w, fw, exact=True)
@@ -358,12 +433,14 @@ def test_backward_matches_torch_autograd_in_fp64():
     p = torch.softmax(tt["x"] @ tt["Wr"] + tt["b"], dim=1)
     out = torch.zeros(T, d, dtype=torch.float64)
     for t in range(T):
+        sel = p[t, torch.as_tensor(fw["idx"][t].astype(np.int64))]
+        gates = sel / sel.sum() if renorm else sel
         for j in range(k):
             if fw["row_of"][t, j] < 0:
                 continue
             e = int(fw["idx"][t, j])
             hdn = torch.nn.functional.gelu(tt["x"][t] @ tt["W1"][e], approximate="tanh")
-            out[t] = out[t] + p[t, e] * (hdn @ tt["W2"][e])
+            out[t] = out[t] + gates[j] * (hdn @ tt["W2"][e])
     (out * torch.tensor(inp["dOut"])).sum().backward()
     np.testing.assert_allclose(fw["out"], out.detach().numpy(), rtol=1e-12, atol=1e-15)
     for n, g in (("x", "dX"), ("Wr", "dWr"), ("b", "db"), ("W1", "dW1"), ("W2", "dW2")):
