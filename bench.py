@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--aux-coeff", type=float, default=0.0,
                     help="coefficient of the load-balancing loss (default 0: the bare "
                          "layer); > 0 also computes the loss and drop rate every step")
+    ap.add_argument("--renorm", action="store_true",
+                    help="gates renormalised over the selected experts")
+    ap.add_argument("--priority", choices=("token", "slot"), default="token",
+                    help="capacity priority: token-major (default) or slot-major")
     ap.add_argument("--recompute", action="store_true",
                     help="selective recomputation: A and H are not saved and the "
                          "backward recomputes them (one extra grouped GEMM)")
@@ -198,8 +202,8 @@ def main():
 
     import workloads as W
     w = W.get(a.config)
-    if a.aux_coeff:
-        w = dataclasses.replace(w, aux_coeff=a.aux_coeff)
+    if a.aux_coeff or a.renorm or a.priority != "token":
+        w = dataclasses.replace(w, aux_coeff=a.aux_coeff, renorm=a.renorm, priority=a.priority)
     if a.summarize_counters:
         return summarize_counters(a, w)
     import expert_router_gemm_softmax_amd as M
@@ -214,7 +218,8 @@ def main():
     else:
         cap = M.moe_capacity(w.T, w.k, w.E, w.cf)
     cfg = M.make_cfg(w.T, w.d, w.E, w.k, w.f, w.dtype, capacity=cap,
-                     aux_coeff=a.aux_coeff, recompute=a.recompute)
+                     aux_coeff=a.aux_coeff, recompute=a.recompute, renorm=a.renorm,
+                     priority=a.priority)
     sdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
     if w.kind == "layer":
@@ -320,7 +325,8 @@ def main():
                                f"cf={w.cf} bias={w.bias}",
                    "tokens": w.T, "d": w.d, "experts": w.E, "top_k": w.k, "ffn": w.f,
                    "capacity": cap, "kept_rows": R, "parallelism": "single GPU",
-                   "aux_coeff": a.aux_coeff, "recompute": a.recompute},
+                   "aux_coeff": a.aux_coeff, "recompute": a.recompute,
+                   "renorm": a.renorm, "priority": a.priority},
         "roofline": roof,
         "gpu_event_ms_per_step": round(gpu_ms / a.steps, 4),
     }

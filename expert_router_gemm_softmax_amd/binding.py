@@ -28,6 +28,8 @@ MOE_FP32 = 0
 MOE_BF16 = 1
 MOE_NO_CAPACITY = -1
 MOE_FLAG_RECOMPUTE = 1
+MOE_FLAG_RENORM = 2
+MOE_FLAG_SLOT_PRIORITY = 4
 
 KERNELS = dict(ROUTE=0, PERMUTE_COUNT=1, PERMUTE_SCAN=2, PERMUTE_SCATTER=3,
                GEMM_UP=4, GEMM_DOWN=5, COMBINE=6, COMBINE_BWD=7, GEMM_DH=8,
@@ -171,15 +173,22 @@ def _stream(stream):
 
 
 def make_cfg(T, d, E, k, f, dtype="bf16", capacity=None, route_margin=0.0,
-             aux_coeff=0.0, recompute=False) -> MoeCfg:
+             aux_coeff=0.0, recompute=False, renorm=False, priority="token") -> MoeCfg:
     """capacity: None = no limit, else an int >= 0; aux_coeff: weight of the
     load-balancing loss (0 = none); recompute: keep A and H out of the saved
-    state and recompute them in backward (MOE_FLAG_RECOMPUTE)."""
+    state and recompute them in backward (MOE_FLAG_RECOMPUTE); renorm: gates
+    renormalised over the selected experts (MOE_FLAG_RENORM); priority:
+    'token' or 'slot' capacity walk (MOE_FLAG_SLOT_PRIORITY)."""
+    if priority not in ("token", "slot"):
+        raise ValueError(f"priority must be 'token' or 'slot', not {priority!r}")
     dt = {"bf16": MOE_BF16, "f32": MOE_FP32, MOE_BF16: MOE_BF16, MOE_FP32: MOE_FP32}[dtype]
     return MoeCfg(T=int(T), d=int(d), E=int(E), k=int(k), f=int(f), dtype=dt,
                   capacity=MOE_NO_CAPACITY if capacity is None else int(capacity),
                   route_margin=float(route_margin),
-                  flags=MOE_FLAG_RECOMPUTE if recompute else 0, aux_coeff=float(aux_coeff))
+                  flags=((MOE_FLAG_RECOMPUTE if recompute else 0)
+                         | (MOE_FLAG_RENORM if renorm else 0)
+                         | (MOE_FLAG_SLOT_PRIORITY if priority == "slot" else 0)),
+                  aux_coeff=float(aux_coeff))
 
 
 def moe_capacity(T, k, E, cf) -> int:

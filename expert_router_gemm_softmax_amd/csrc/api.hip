@@ -61,7 +61,8 @@ int check_cfg(const moe_cfg* c) {
   if (c->k < 1 || c->k > 32 || c->E < c->k || c->E > 256) return MOE_ERR_ARG;
   if (c->d < 1 || c->f < 1) return MOE_ERR_ARG;
   if (c->capacity < MOE_NO_CAPACITY) return MOE_ERR_ARG;
-  if ((c->flags & ~MOE_FLAG_RECOMPUTE) != 0) return MOE_ERR_ARG;
+  if ((c->flags & ~(MOE_FLAG_RECOMPUTE | MOE_FLAG_RENORM | MOE_FLAG_SLOT_PRIORITY)) != 0)
+    return MOE_ERR_ARG;
   if (c->T * c->k > 0x7fffffffLL) return MOE_ERR_SHAPE;
   if (!(c->route_margin == c->route_margin)) return MOE_ERR_ARG;  // NaN
   if (!(c->aux_coeff >= 0.0f && c->aux_coeff <= FLT_MAX)) return MOE_ERR_ARG;  // NaN, <0, inf

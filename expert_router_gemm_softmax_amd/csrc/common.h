@@ -189,7 +189,8 @@ inline WsLayout ws_layout(const moe_cfg& c) {
   const size_t s = elem_bytes(c);
   const int64_t Rmax = rows_max(c);
   const int64_t T1 = c.T > 0 ? c.T : 1;
-  L.nblk_perm = (int)ceil_div(T1, kPermTokens);
+  // permute blocks: over T tokens, or k T virtual tokens for slot priority
+  L.nblk_perm = (int)ceil_div((c.flags & MOE_FLAG_SLOT_PRIORITY) ? T1 * c.k : T1, kPermTokens);
   L.nblk_dz = (int)ceil_div(T1, kDzTokens);
   L.nblk_aux = (int)ceil_div(T1, kAuxTokens);
   // dWr = x^T dz as a k-ragged GEMM over uniform token chunks: enough chunks

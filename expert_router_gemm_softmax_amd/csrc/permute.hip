@@ -1,6 +1,9 @@
 // Permute with capacity drop (F2): per-expert histogram, exclusive scan of
 // the kept counts, stable scatter in token order, and the row copy
-// x -> x_perm.  Routed tokens are laid out contiguously per expert ("GPU
+// x -> x_perm.  Under MOE_FLAG_SLOT_PRIORITY the walk is slot-major, (j, t)
+// in lexicographic order: the same kernels then run over k*T virtual tokens
+// v = j T + t with one assignment each, so ranks, drops and row order all
+// follow the slot-major walk.  Routed tokens are laid out contiguously per expert ("GPU
 // expert parallel", section "The step timeline"); assignments beyond the
 // capacity are dropped (distributed-training tutorial, "The Capacity
 // Factor"), the later tokens first.
@@ -14,18 +17,33 @@ namespace moe {
 namespace {
 
 constexpr int kPW = kPermTokens / kWave;  // waves per permute block
+
+// The walk: virtual token v, its slot jv < kv; returns the flat assignment
+// index t * k + j.  Token-major: v = t, kv = k.  Slot-major: v = j T + t, kv = 1.
+struct Walk {
+  int64_t T, Tv;
+  int k, kv;
+  bool slot;
+  __device__ __forceinline__ int64_t flat(int64_t v, int jv) const {
+    if (slot) {
+      const int64_t j = v / T;
+      return (v - j * T) * k + j;
+    }
+    return v * k + jv;
+  }
+};
 static_assert(kPermTokens == 256, "the scatter kernel's offset scan is a 256-thread scan");
 
 // per-block expert histogram: blk[b][e] = #assignments of block b to e
 __global__ __launch_bounds__(kPermTokens) void permute_count_kernel(
-    const int32_t* __restrict__ idx, int32_t* __restrict__ blk, int64_t T_, int E, int k) {
+    const int32_t* __restrict__ idx, int32_t* __restrict__ blk, Walk wk, int E) {
   extern __shared__ int32_t hist[];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  const int64_t t = (int64_t)blockIdx.x * kPermTokens + threadIdx.x;
-  if (t < T_)
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j];
+  const int64_t v = (int64_t)blockIdx.x * kPermTokens + threadIdx.x;
+  if (v < wk.Tv)
+    for (int j = 0; j < wk.kv; ++j) {
+      const int e = idx[wk.flat(v, j)];
       if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
     }
   __syncthreads();
@@ -67,17 +85,15 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
 __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ blk,
     const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ row_of, int32_t* __restrict__ src_of, int64_t T_, int E, int k,
-    int64_t cap) {
+    int32_t* __restrict__ row_of, int32_t* __restrict__ src_of, Walk wk, int E, int64_t cap) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);  // [kPW][E]
   int32_t* wbase = reinterpret_cast<int32_t*>(mask + kPW * E);            // [kPW][E]
   int32_t* s_off = wbase + kPW * E;                                       // [E]
   __shared__ int s_wave[4];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t t0 = (int64_t)blockIdx.x * kPermTokens;
-  const int64_t t = t0 + threadIdx.x;
-  const bool valid = t < T_;
+  const int64_t v = (int64_t)blockIdx.x * kPermTokens + threadIdx.x;
+  const bool valid = v < wk.Tv;
 
   // offsets = exclusive scan of min(counts, C) (E <= 256, one per thread);
   // block 0 publishes them
@@ -100,8 +116,8 @@ __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
   for (int i = threadIdx.x; i < kPW * E; i += blockDim.x) mask[i] = 0ull;
   __syncthreads();
   if (valid)
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j];
+    for (int j = 0; j < wk.kv; ++j) {
+      const int e = idx[wk.flat(v, j)];
       if ((unsigned)e < (unsigned)E) atomicOr(&mask[w * E + e], 1ull << lane);
     }
   __syncthreads();
@@ -115,10 +131,11 @@ __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
   __syncthreads();
   if (valid) {
     const unsigned long long lt = (1ull << lane) - 1ull;
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j];
+    for (int j = 0; j < wk.kv; ++j) {
+      const int64_t a = wk.flat(v, j);
+      const int e = idx[a];
       if ((unsigned)e >= (unsigned)E) {  // outside the contract: treat as dropped
-        row_of[t * k + j] = -1;
+        row_of[a] = -1;
         continue;
       }
       const int64_t pos = (int64_t)blk[(int64_t)blockIdx.x * E + e] + wbase[w * E + e] +
@@ -126,9 +143,9 @@ __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
       int32_t row = -1;
       if (cap < 0 || pos < cap) {
         row = (int32_t)(s_off[e] + pos);
-        src_of[row] = (int32_t)(t * k + j);
+        src_of[row] = (int32_t)a;
       }
-      row_of[t * k + j] = row;
+      row_of[a] = row;
     }
   }
 }
@@ -174,18 +191,23 @@ int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
                    int32_t* src_of, void* x_perm, void* ws, hipStream_t s) {
   const WsLayout L = ws_layout(c);
   int32_t* blk = ws_ptr<int32_t>(ws, L.perm_blk);
-  const int nblk = c.T > 0 ? (int)ceil_div(c.T, kPermTokens) : 0;
+  Walk wk;
+  wk.T = c.T;
+  wk.k = c.k;
+  wk.slot = (c.flags & MOE_FLAG_SLOT_PRIORITY) != 0;
+  wk.Tv = wk.slot ? c.T * c.k : c.T;
+  wk.kv = wk.slot ? 1 : c.k;
+  const int nblk = c.T > 0 ? (int)ceil_div(wk.Tv, kPermTokens) : 0;  // L.nblk_perm
   if (nblk > 0)
     MOE_LAUNCH(MOE_KERNEL_PERMUTE_COUNT, s,
-               permute_count_kernel<<<nblk, kPermTokens, c.E * 4, s>>>(idx, blk, c.T,
-                                                                      c.E, c.k));
+               permute_count_kernel<<<nblk, kPermTokens, c.E * 4, s>>>(idx, blk, wk, c.E));
   MOE_LAUNCH(MOE_KERNEL_PERMUTE_SCAN, s,
              permute_scan_kernel<<<c.E, 256, 0, s>>>(blk, counts, offsets, nblk, c.E));
   if (nblk > 0) {
     const size_t sm = (size_t)kPW * c.E * 8 + (size_t)kPW * c.E * 4 + (size_t)c.E * 4;
     MOE_LAUNCH(MOE_KERNEL_PERMUTE_SCATTER, s,
                permute_scatter_kernel<<<nblk, kPermTokens, sm, s>>>(
-                   idx, blk, counts, offsets, row_of, src_of, c.T, c.E, c.k, c.capacity));
+                   idx, blk, counts, offsets, row_of, src_of, wk, c.E, c.capacity));
     const int g = (int)std::min<int64_t>(ceil_div(c.T, 4), 65536);
     if (c.dtype == MOE_BF16)
       MOE_LAUNCH(MOE_KERNEL_PERMUTE_COPY, s,

@@ -20,6 +20,8 @@
 // (lanes across experts): softmax statistics, top-(k+1), coalesced writes of
 // probabilities, experts and gates, and the worklist of uncertain tokens;
 // the rescoring kernel then certifies those tokens in fp64, one per wave.
+// Gates are the chosen probabilities, or (MOE_FLAG_RENORM) those divided by
+// their sum taken in selection order; both kernels form them the same way.
 #include "gemm.h"
 
 #include <float.h>
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(256) void route_kernel(
     const float* __restrict__ zf, const float* __restrict__ bias, float* __restrict__ probs,
     int32_t* __restrict__ idx_out, float* __restrict__ gate_out, int* __restrict__ wl_count,
     int* __restrict__ wl_tok, int* __restrict__ wl_n, int* __restrict__ wl_e, int64_t T_,
-    int E, int Epad, int k, float tau) {
+    int E, int Epad, int k, float tau, bool renorm) {
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * 4;
   float bz[NS];
@@ -117,6 +119,7 @@ __global__ __launch_bounds__(256) void route_kernel(
     uint32_t taken = 0;
     float vsel_prev = 0.0f, vk = -INFINITY;
     bool flag = false;
+    float psel = 0.0f, S = 0.0f;  // lane j: probability of the j-th choice
     for (int j = 0; j < nsel; ++j) {
       float v = -INFINITY;
       int e = 0x7fffffff;
@@ -133,17 +136,20 @@ __global__ __launch_bounds__(256) void route_kernel(
       if (j > 0 && vsel_prev - v < tau) flag = true;
       vsel_prev = v;
       if (j < k) {
-        // the owner lane writes the expert and its probability
-        if ((e & 63) == lane) {
-          idx_out[t * k + j] = e;
+        // the owner lane writes the expert; its probability goes to lane j
+        float pe = 0.0f;
 #pragma unroll
-          for (int i = 0; i < NS; ++i)
-            if (i == (e >> 6)) gate_out[t * k + j] = ps[i];
-        }
+        for (int i = 0; i < NS; ++i)
+          if (i == (e >> 6)) pe = ps[i];
+        pe = __shfl(pe, e & 63, kWave);
+        S += pe;
+        if (lane == j) psel = pe;
+        if ((e & 63) == lane) idx_out[t * k + j] = e;
       } else {
         vk = v;
       }
     }
+    if (lane < k) gate_out[t * k + lane] = renorm ? psel / S : psel;
     if (flag) {  // uniform over the wave
       const float thr = E > k ? vk - tau : -INFINITY;
       int slot = 0;
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
     const int* __restrict__ wl_count, const int* __restrict__ wl_tok,
     const int* __restrict__ wl_n, const int* __restrict__ wl_e, const T* __restrict__ x, const T* __restrict__ wrT, const float* __restrict__ bias,
     const float* __restrict__ probs, int32_t* __restrict__ idx_out,
-    float* __restrict__ gate_out, int d, int E, int Epad, int k) {
+    float* __restrict__ gate_out, int d, int E, int Epad, int k, bool renorm) {
   constexpr int V = St<T>::kVec;
   constexpr int CPL = 4;  // 16-byte chunks per lane per pass
   const int lane = threadIdx.x & 63;
@@ -247,6 +253,7 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
       ce[i] = u < n ? cand[u] : 0x7fffffff;
     }
     uint32_t taken = 0;
+    float psel = 0.0f, S = 0.0f;  // lane j: probability of the j-th choice
     for (int j = 0; j < k; ++j) {
       float v = -INFINITY;
       int e = 0x7fffffff;
@@ -257,15 +264,18 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
           e = ce[i];
         }
       wave_argmax(v, e);
-      // the lane holding the winner marks it and writes the expert and gate
+      // the lane holding the winner marks it and writes the expert
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (lane + kWave * i < n && ce[i] == e && !((taken >> i) & 1u)) {
           taken |= 1u << i;
           idx_out[t * k + j] = e;
-          gate_out[t * k + j] = probs[t * E + e];
         }
+      const float pe = e < E ? probs[t * E + e] : 0.0f;  // e < E: n >= k candidates
+      S += pe;
+      if (lane == j) psel = pe;
     }
+    if (lane < k) gate_out[t * k + lane] = renorm ? psel / S : psel;
   }
 }
 
@@ -274,6 +284,7 @@ int launch_route_t(const moe_cfg& c, const T* x, const T* Wr, const float* b, fl
                    int32_t* idx, float* gate, T* wrT, float* zf, const RouteWorklist& wl,
                    hipStream_t s) {
   const int Epad = route_epad(c.E);
+  const bool renorm = (c.flags & MOE_FLAG_RENORM) != 0;
   int rc = launch_transpose_wr(c, Wr, wrT, wl.count, s);
   if (rc != MOE_OK) return rc;
   // zf = x wrT^T: one group of T rows, N = Epad, K = d
@@ -297,20 +308,23 @@ int launch_route_t(const moe_cfg& c, const T* x, const T* Wr, const float* b, fl
   if (Epad <= 64)
     MOE_LAUNCH(MOE_KERNEL_ROUTE, s,
                route_kernel<1><<<grid, 256, 0, s>>>(zf, b, probs, idx, gate, wl.count, wl.tok,
-                                                    wl.n, wl.e, c.T, c.E, Epad, c.k, tau));
+                                                    wl.n, wl.e, c.T, c.E, Epad, c.k, tau,
+                                                    renorm));
   else if (Epad <= 128)
     MOE_LAUNCH(MOE_KERNEL_ROUTE, s,
                route_kernel<2><<<grid, 256, 0, s>>>(zf, b, probs, idx, gate, wl.count, wl.tok,
-                                                    wl.n, wl.e, c.T, c.E, Epad, c.k, tau));
+                                                    wl.n, wl.e, c.T, c.E, Epad, c.k, tau,
+                                                    renorm));
   else
     MOE_LAUNCH(MOE_KERNEL_ROUTE, s,
                route_kernel<4><<<grid, 256, 0, s>>>(zf, b, probs, idx, gate, wl.count, wl.tok,
-                                                    wl.n, wl.e, c.T, c.E, Epad, c.k, tau));
+                                                    wl.n, wl.e, c.T, c.E, Epad, c.k, tau,
+                                                    renorm));
   const int rgrid = (int)std::min<int64_t>(ceil_div(c.T, 4), 2048);
   MOE_LAUNCH(MOE_KERNEL_ROUTE, s,
              route_rescore_kernel<T><<<rgrid, 256, 0, s>>>(
                  wl.count, wl.tok, wl.n, wl.e, x, wrT, b, probs, idx, gate, c.d, c.E,
-                 Epad, c.k));
+                 Epad, c.k, renorm));
   return MOE_OK;
 }
 

@@ -49,10 +49,20 @@ __global__ __launch_bounds__(1024) void route_aux_final_kernel(
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (threadIdx.x < 256) red[threadIdx.x] = 0.0;
   __syncthreads();
+  constexpr int U = 16;  // loads in flight per lane
   for (int e = w; e < E; e += 16) {
     const float* pe = part + (int64_t)e * nblk;
     double s = 0.0;
-    for (int b = lane; b < nblk; b += kWave) s += (double)pe[b];
+    for (int b0 = 0; b0 < nblk; b0 += kWave * U) {
+      float v[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int b = b0 + q * kWave + lane;
+        v[q] = b < nblk ? pe[b] : 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) s += (double)v[q];
+    }
     s = wave_sum_d(s);
     if (lane == 0) red[e] = (double)counts[e] * s;  // counts_e * T P_e
   }

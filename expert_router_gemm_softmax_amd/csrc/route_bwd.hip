@@ -4,6 +4,8 @@
 // index, top-k and capacity steps are piecewise constant and pass no
 // gradient.
 //   dp[t, e] = a_e + dgate[t,j] if e = idx[t,j] for a kept j, else a_e
+//   (with renormalised gates g_j = p_j / S the gate term of a selected j is
+//   (dgate_j - sum_i g_i dgate_i) / S instead, dropped j included)
 //   dz = p * (dp - sum_e p dp)
 // where a_e = alpha E counts[e] / (T k T) is the gradient of the
 // load-balancing loss (zero when its coefficient alpha is zero).
@@ -29,7 +31,8 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
     const float* __restrict__ probs, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ row_of, const int32_t* __restrict__ counts,
     const float* __restrict__ dgate, float* __restrict__ dz, uint16_t* __restrict__ dzb,
-    float* __restrict__ db_part, int64_t T_, int E, int Ep, int k, float aux_scale) {
+    float* __restrict__ db_part, int64_t T_, int E, int Ep, int k, float aux_scale,
+    bool renorm) {
   __shared__ float sdb[4][256];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float dbacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -51,13 +54,37 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
       p[i] = e < E ? probs[t * E + e] : 0.0f;
       dp[i] = a[i];
     }
-    for (int j = 0; j < k; ++j) {
-      if (row_of[t * k + j] < 0) continue;
-      const int e = idx[t * k + j];
-      const float g = dgate[t * k + j];
+    if (renorm) {
+      // gates g_j = p_j / S (S summed in selection order, as the forward);
+      // dL/dp_j = (dgate_j - sum_i g_i dgate_i) / S for every selected j
+      auto psel = [&](int j) {  // an index outside [0, E) counts as probability 0
+        const int e = idx[t * k + j];
+        return (unsigned)e < (unsigned)E ? probs[t * E + e] : 0.0f;
+      };
+      float S = 0.0f;
+      for (int j = 0; j < k; ++j) S += psel(j);
+      float G = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const float dg = row_of[t * k + j] < 0 ? 0.0f : dgate[t * k + j];
+        G += psel(j) / S * dg;
+      }
+      for (int j = 0; j < k; ++j) {
+        const int e = idx[t * k + j];
+        const float dg = row_of[t * k + j] < 0 ? 0.0f : dgate[t * k + j];
+        const float g = (dg - G) / S;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (e == lane + 64 * i) dp[i] += g;
+        for (int i = 0; i < 4; ++i)
+          if (e == lane + 64 * i) dp[i] += g;
+      }
+    } else {
+      for (int j = 0; j < k; ++j) {
+        if (row_of[t * k + j] < 0) continue;
+        const int e = idx[t * k + j];
+        const float g = dgate[t * k + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (e == lane + 64 * i) dp[i] += g;
+      }
     }
     float sp = 0.0f;
 #pragma unroll
@@ -166,7 +193,8 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
     MOE_LAUNCH(MOE_KERNEL_ROUTE_BWD_DZ, s,
                route_bwd_dz_kernel<BF><<<nblk, 256, 0, s>>>(probs, idx, row_of, counts, dgate,
                                                            dz, dzb, dbp, c.T, c.E, Ep, c.k,
-                                                           aux_scale));
+                                                           aux_scale,
+                                                           (c.flags & MOE_FLAG_RENORM) != 0));
   if constexpr (BF) {
     const int64_t n = (int64_t)c.d * 2 * Ep;
     MOE_LAUNCH(MOE_KERNEL_ROUTE_PREP, s,

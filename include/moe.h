@@ -77,6 +77,19 @@ typedef enum { MOE_FP32 = 0, MOE_BF16 = 1 } moe_dtype;
  * Results are bitwise those of the default mode; the saved state shrinks
  * by 2 Rmax f s bytes and the workspace grows by as much. */
 #define MOE_FLAG_RECOMPUTE 1u
+/* MOE_FLAG_RENORM: gates renormalised over the k selected experts,
+ * gate[t,j] = p[t,idx_j] / sum_i p[t,idx_i] (sum in selection order, fp32),
+ * before the capacity drop; the router backward differentiates through the
+ * normalisation.  Without it the gates are the probabilities themselves.
+ * The pages fix neither; top-k routing is used both ways. */
+#define MOE_FLAG_RENORM 2u
+/* MOE_FLAG_SLOT_PRIORITY: the capacity walk is slot-major -- every token's
+ * first choice before any token's second choice, (j, t) in lexicographic
+ * order -- instead of token-major (t, j); the rows of an expert in x_perm
+ * follow the same order.  Which assignments of a full expert go first is
+ * not fixed by the pages ("The Capacity Factor" only says the excess is
+ * dropped). */
+#define MOE_FLAG_SLOT_PRIORITY 4u
 
 /* hipStream_t, passed opaquely so that this header needs no HIP headers. */
 typedef void* moe_stream_t;
@@ -133,7 +146,8 @@ MOE_API const char* moe_last_error(void);
  *   probs [T,E] float  softmax over all E of z = x Wr + b
  *   idx   [T,k] int32  the k experts in order (z descending, expert index
  *                      ascending on equal z)
- *   gate  [T,k] float  probs[t, idx[t,j]] (not renormalised)
+ *   gate  [T,k] float  probs[t, idx[t,j]] (renormalised over the k under
+ *                      MOE_FLAG_RENORM)
  * Decisions are made on the canonical logit RN_fp32(sum in fp64 + b): the
  * fast fp32 logits are used where the top-(k+1) gaps exceed
  * cfg->route_margin, and every logit that can change the decision is
@@ -148,7 +162,8 @@ MOE_API int moe_route(const moe_cfg* cfg, const void* x, const void* Wr,
  * contiguous buffer per expert ("The step timeline"); assignments beyond an
  * expert's capacity are dropped ("The Capacity Factor").  Assignments are kept in
  * token order: (t,j) is kept iff fewer than C earlier tokens chose expert
- * idx[t,j].
+ * idx[t,j] (under MOE_FLAG_SLOT_PRIORITY: fewer than C earlier assignments
+ * in slot-major order (j, t)); the rows of an expert follow that order.
  *   idx [T,k] int32 (each row k distinct experts in [0,E))
  *   counts  [E]   int32  routed assignments per expert, before the drop
  *   offsets [E+1] int32  exclusive scan of min(counts, C); offsets[E] = R
@@ -242,7 +257,11 @@ MOE_API int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp,
  * gradient -- "Sharded by expert, replicated everywhere else"):
  *   dp[t, e] = a_e + (dgate[t,j] if e = idx[t,j] for a kept j)
  *       with a_e = alpha * E * counts[e] / (T k T), the gradient of the
- *       load-balancing loss (alpha = cfg->aux_coeff; a_e = 0 when alpha = 0)
+ *       load-balancing loss (alpha = cfg->aux_coeff; a_e = 0 when alpha = 0);
+ *       under MOE_FLAG_RENORM the gate term is instead
+ *       (dgate[t,j] - sum_i g_i dgate[t,i]) / S for every selected j, with
+ *       S = sum_i probs[t, idx[t,i]] and g_i = probs[t, idx[t,i]] / S
+ *       (dgate of a dropped assignment counts as 0)
  *   dz  = probs * (dp - sum_e probs * dp)
  *   db  = sum_t dz                       [E] float
  *   dWr = x^T dz                         [d,E] s

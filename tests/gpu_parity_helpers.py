@@ -73,7 +73,8 @@ def to_int(t) -> np.ndarray:
 def cfg_of(M, w, route_margin=0.0, recompute=False):
     cap = O.capacity(w.T, w.k, w.E, w.cf)
     return M.make_cfg(w.T, w.d, w.E, w.k, w.f, w.dtype, capacity=cap,
-                      route_margin=route_margin, aux_coeff=w.aux_coeff, recompute=recompute)
+                      route_margin=route_margin, aux_coeff=w.aux_coeff, recompute=recompute,
+                      renorm=w.renorm, priority=w.priority)
 
 
 def red_tol(ref, dtype):
@@ -171,16 +172,27 @@ def logit_error(res, fw):
     return float(np.max(np.where(ok, np.abs(dg - dz), 0.0)))
 
 
+def check_gate_formula(res, fw, w):
+    """gate is bitwise the probability of the chosen expert, or with
+    renormalisation p_j / S with S the fp32 sum in selection order and one
+    correctly rounded fp32 division -- recomputed from the GPU's own probs."""
+    p = to_f64(res["probs"]).astype(np.float32)
+    sel = np.take_along_axis(p, fw["idx"].astype(np.int64), axis=1)
+    if w.renorm:
+        S = np.zeros(sel.shape[0], np.float32)
+        for j in range(sel.shape[1]):
+            S = (S + sel[:, j]).astype(np.float32)
+        sel = (sel / S[:, None]).astype(np.float32)
+    np.testing.assert_array_equal(to_f64(res["gate"]), sel.astype(np.float64), err_msg="gate")
+
+
 def check_layer_full(res, fw, bw, w, check_bwd=True):
     """Every output of the layer against the full oracle."""
     tol = w.dtype
     R = check_routing_exact(res, fw, w)
     assert_close("probs", to_f64(res["probs"]), fw["probs"], "prob")
     assert_close("gate", to_f64(res["gate"]), fw["gate"], "prob")
-    # gate is bitwise the probability of the chosen expert
-    p = to_f64(res["probs"])
-    np.testing.assert_array_equal(
-        to_f64(res["gate"]), np.take_along_axis(p, fw["idx"].astype(np.int64), axis=1))
+    check_gate_formula(res, fw, w)
     np.testing.assert_array_equal(to_f64(res["x_perm"])[:R], fw["x_perm"], err_msg="x_perm")
     if res.get("A") is not None:  # None in the recomputation mode
         assert_close("A", to_f64(res["A"])[:R], fw["A"], tol)
@@ -223,9 +235,10 @@ def check_aux(name, aux, probs, fw, w, coeff):
     assert abs(a[1] - O.drop_rate(fw["offsets"], w.T, w.k)) <= 1e-7, (name, a[1])
 
 
-def make_case(T, d, E, k, f, dtype, cf, bias="zero", seed=0, aux_coeff=0.0, **kw):
+def make_case(T, d, E, k, f, dtype, cf, bias="zero", seed=0, aux_coeff=0.0, renorm=False,
+              priority="token", **kw):
     w = W.custom(T, d, E, k, f, dtype=dtype, cf=cf, bias=bias, name=f"T{T}d{d}E{E}k{k}f{f}",
-                 aux_coeff=aux_coeff)
+                 aux_coeff=aux_coeff, renorm=renorm, priority=priority)
     inp = W.make_inputs(w, seed=seed)
     for key, v in kw.items():
         inp[key] = v

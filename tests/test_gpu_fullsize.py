@@ -13,7 +13,8 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_parity_helpers import (assert_close, check_aux, check_layer_full, check_routing_exact,
+from gpu_parity_helpers import (assert_close, check_aux, check_gate_formula,
+                                check_layer_full, check_routing_exact,
                                 expert_grad_tols, logit_error, run_layer, say, term_norm,
                                 terms_tol, to_dev, to_f64, to_int)
 
@@ -80,6 +81,21 @@ def test_c3_epshare_full(M):
     t1, t2 = expert_grad_tols(fw, bw, "bf16")
     assert_close("dW1", to_f64(dW1), bw["dW1"], t1)
     assert_close("dW2", to_f64(dW2), bw["dW2"], t2)
+
+
+def test_c4_routing_variants(M):
+    """C4 with renormalised gates and slot-major capacity priority: the
+    routing maps bit-exact and the gates bitwise their formula (forward)."""
+    w = W.get("C4").replace(renorm=True, priority="slot")
+    inp = W.make_inputs(w, seed=0)
+    res = run_layer(M, w, inp, bwd=False)
+    fw = O.route(inp, w)
+    R = check_routing_exact(res, fw, w)
+    check_gate_formula(res, fw, w)
+    assert_close("gate", to_f64(res["gate"]), fw["gate"], "prob")
+    tok = O.assign(fw["idx"], w.E, fw["C"], "token")[2]
+    say(f"C4 slot-major: R={R}, {int(np.sum((tok >= 0) != (fw['row_of'] >= 0)))} "
+        f"assignments kept differently from token-major")
 
 
 def test_c4_large(M):

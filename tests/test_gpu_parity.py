@@ -164,6 +164,38 @@ def test_balancing_gradient_alone(M, dt):
     assert np.all(to_f64(res["dW1"]) == 0) and np.all(to_f64(res["dW2"]) == 0)
 
 
+VARIANT_CASES = [
+    # T, d, E, k, f, dtype, cf, bias, renorm, priority
+    (513, 64, 40, 3, 136, "bf16", 0.75, "zipf", True, "slot"),   # both, skew, drops
+    (1000, 264, 6, 2, 200, "bf16", 1.1, "zero", True, "token"),  # renormalised top-2
+    (300, 36, 5, 2, 52, "f32", 0.9, "normal", False, "slot"),    # fp32, slot-major
+    (260, 48, 130, 8, 40, "bf16", None, "normal", True, "token"),  # E > 128, k = 8
+    (100, 64, 40, 32, 64, "bf16", 1.0, "normal", True, "slot"),  # k = 32
+    (777, 128, 16, 4, 96, "bf16", 0.6, "normal", False, "slot"),  # many drops
+]
+
+
+@pytest.mark.parametrize("case", VARIANT_CASES,
+                         ids=lambda c: "T{}E{}k{}{}{}{}".format(c[0], c[2], c[3], c[5],
+                                                                "-renorm" if c[8] else "",
+                                                                "-" + c[9]))
+def test_routing_variants_match_oracle(M, case):
+    """Renormalised gates and slot-major capacity priority: routing maps
+    bit-exact, gates bitwise their formula, every output within tolerance."""
+    T, d, E, k, f, dt, cf, bias, renorm, prio = case
+    w, inp = make_case(T, d, E, k, f, dt, cf, bias, seed=T + 3, renorm=renorm, priority=prio)
+    say("case", case)
+    res = run_layer(M, w, inp)
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    R = check_layer_full(res, fw, bw, w)
+    if prio == "slot" and cf is not None:
+        # the variant changes which assignments are kept
+        tok = O.assign(fw["idx"], E, fw["C"], "token")[2]
+        say("  R =", R, "kept sets differ from token-major:",
+            bool(np.any((tok >= 0) != (fw["row_of"] >= 0))))
+
+
 @pytest.mark.parametrize("recompute", [False, True], ids=["save", "recompute"])
 def test_step_entry_points_equal_the_layer_entry_points(M, recompute):
     """moe_route .. moe_route_bwd called one by one give bitwise the layer's

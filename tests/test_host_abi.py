@@ -103,10 +103,25 @@ def test_bad_dtype_and_flags():
     c.dtype = 7
     assert M.moe_check_cfg(c) == B.MOE_ERR_DTYPE
     c = M.make_cfg(16, 64, 8, 2, 64, "bf16")
-    c.flags = 2
-    assert M.moe_check_cfg(c) == B.MOE_ERR_ARG
-    c.flags = B.MOE_FLAG_RECOMPUTE
-    assert M.moe_check_cfg(c) == B.MOE_OK
+    for bad in (8, 16, 1 << 31):
+        c.flags = bad
+        assert M.moe_check_cfg(c) == B.MOE_ERR_ARG
+    for ok in (B.MOE_FLAG_RECOMPUTE, B.MOE_FLAG_RENORM, B.MOE_FLAG_SLOT_PRIORITY, 7):
+        c.flags = ok
+        assert M.moe_check_cfg(c) == B.MOE_OK
+    c = M.make_cfg(16, 64, 8, 2, 64, "bf16", recompute=True, renorm=True, priority="slot")
+    assert c.flags == 7
+    with pytest.raises(ValueError):
+        M.make_cfg(16, 64, 8, 2, 64, "bf16", priority="expert")
+
+
+def test_slot_priority_sizes_the_permute_workspace_for_k_t_virtual_tokens():
+    tok = M.make_cfg(100000, 64, 64, 8, 64, "bf16")
+    slot = M.make_cfg(100000, 64, 64, 8, 64, "bf16", priority="slot")
+    # per-block expert counts: ceil(k T / 256) blocks instead of ceil(T / 256)
+    extra = (-(-8 * 100000 // 256) - (-(-100000 // 256))) * 64 * 4
+    grow = M.moe_workspace_bytes(slot) - M.moe_workspace_bytes(tok)
+    assert extra <= grow <= extra + 256
     c = M.make_cfg(16, 12, 8, 2, 64, "f32")   # 48-byte rows: aligned for fp32
     assert M.moe_check_cfg(c) == B.MOE_OK
 
