@@ -62,6 +62,11 @@ Readings taken where the pages are silent (numbered as in the design doc; R8
      every token's first choice before any second choice, (j, t) in
      lexicographic order, instead of token-major (t, j).  Rows of an expert
      are laid out in that walk order.
+  R19 fallback path of a dropped assignment (an option; the pages only say
+     that excess tokens are dropped or take a fallback path): 'identity'
+     sends the token past the expert unchanged, so the dropped assignment
+     contributes gate[t,j] * x[t] to out[t]; backward, it adds
+     gate[t,j] * dOut[t] to dX[t] and dgate[t,j] = <dOut[t], x[t]>.
 
 Every floating-point result here is fp64 arithmetic on exactly converted
 inputs followed by one rounding at the storage point; ``exact=True`` turns
@@ -244,22 +249,27 @@ def expert_ffn_bwd(xe, W1e, W2e, Ae, He, dYe, rnd):
 
 
 # ------------------------------------------------------------ F5: combine
-def combine(Y, row_of, gate, rnd) -> np.ndarray:
+def combine(Y, row_of, gate, rnd, x=None) -> np.ndarray:
     """out[t] = sum over kept j (ascending) of gate[t,j] * Y[row_of[t,j]];
-    the inverse permutation back to token order (R6)."""
+    the inverse permutation back to token order (R6).  With the identity
+    fallback (x given, R19) a dropped j adds gate[t,j] * x[t] instead."""
     row_of = np.asarray(row_of)
     T, k = row_of.shape
+    g = np.asarray(gate, np.float64)
     acc = np.zeros((T, Y.shape[1]), dtype=np.float64)
     for j in range(k):
         m = row_of[:, j] >= 0
-        acc[m] += np.asarray(gate, np.float64)[m, j, None] * Y[row_of[m, j]]
+        acc[m] += g[m, j, None] * Y[row_of[m, j]]
+        if x is not None:
+            acc[~m] += g[~m, j, None] * np.asarray(x, np.float64)[~m]
     return rnd(acc)
 
 
 # ------------------------------------------------------------ backward
-def combine_bwd(dOut, Y, row_of, gate, R: int, rnd, r32):
+def combine_bwd(dOut, Y, row_of, gate, R: int, rnd, r32, x=None):
     """dYp[row_of[t,j]] = gate[t,j] * dOut[t];  dgate[t,j] = <dOut[t], Y[row]>
-    for kept assignments, 0 for dropped ones."""
+    for kept assignments; for dropped ones 0, or <dOut[t], x[t]> with the
+    identity fallback (x given, R19)."""
     row_of = np.asarray(row_of)
     T, k = row_of.shape
     dYp = np.zeros((R, dOut.shape[1]), dtype=np.float64)
@@ -269,17 +279,23 @@ def combine_bwd(dOut, Y, row_of, gate, R: int, rnd, r32):
         rows = row_of[m, j]
         dYp[rows] = np.asarray(gate, np.float64)[m, j, None] * dOut[m]
         dg[m, j] = np.einsum("td,td->t", dOut[m], Y[rows])
+        if x is not None:
+            dg[~m, j] = np.einsum("td,td->t", dOut[~m], np.asarray(x, np.float64)[~m])
     return rnd(dYp), r32(dg)
 
 
-def unpermute_bwd(dXp, row_of) -> np.ndarray:
-    """dXe[t] = sum over kept j of dXp[row_of[t,j]] (fp64, caller rounds)."""
+def unpermute_bwd(dXp, row_of, gate=None, dOut=None) -> np.ndarray:
+    """dXe[t] = sum over kept j of dXp[row_of[t,j]] (fp64, caller rounds);
+    with the identity fallback (gate and dOut given, R19) a dropped j adds
+    gate[t,j] * dOut[t]."""
     row_of = np.asarray(row_of)
     T, k = row_of.shape
     acc = np.zeros((T, dXp.shape[1]), dtype=np.float64)
     for j in range(k):
         m = row_of[:, j] >= 0
         acc[m] += dXp[row_of[m, j]]
+        if gate is not None:
+            acc[~m] += np.asarray(gate, np.float64)[~m, j, None] * np.asarray(dOut)[~m]
     return acc
 
 
@@ -315,9 +331,10 @@ def router_dz(probs, idx, row_of, dg, aux=None, renorm: bool = False) -> np.ndar
         for j in range(idx64.shape[1]):
             dp[rows, idx64[:, j]] += dsel[:, j]
     else:
+        # dgate of a dropped assignment is 0 unless a fallback path carries it
+        rows = np.arange(T)
         for j in range(row_of.shape[1]):
-            m = row_of[:, j] >= 0
-            dp[np.nonzero(m)[0], idx64[m, j]] += dg[m, j]
+            dp[rows, idx64[:, j]] += dg[:, j]
     s = (probs * dp).sum(axis=1, keepdims=True)
     return probs * (dp - s)
 
@@ -383,6 +400,8 @@ def layer_fwd(inp: Dict[str, np.ndarray], w, exact: bool = False,
     offsets given); per-expert FFN -> gate-scaled inverse permutation.
     """
     rnd = rounder(w.dtype, exact)
+    if w.fallback not in ("none", "identity"):
+        raise ValueError(w.fallback)
     if w.kind == "layer":
         fw = route(inp, w, exact)
         fw["x_perm"] = permute(fw["x"], fw["src_of"], w.k)
@@ -403,7 +422,8 @@ def layer_fwd(inp: Dict[str, np.ndarray], w, exact: bool = False,
         A[lo:hi], H[lo:hi], Y[lo:hi] = expert_ffn_fwd(
             fw["x_perm"][lo:hi], to_f64(inp["W1"][e]), to_f64(inp["W2"][e]), rnd)
     fw.update(A=A, H=H, Y=Y, R=R)
-    fw["out"] = combine(Y, fw["row_of"], fw["gate"], rnd)
+    fb = w.kind == "layer" and w.fallback == "identity"
+    fw["out"] = combine(Y, fw["row_of"], fw["gate"], rnd, fw["x"] if fb else None)
     if w.kind == "layer":
         fw["aux_loss"] = aux_loss(fw["probs"], fw["counts"], w.k, w.aux_coeff)
         fw["drop_rate"] = drop_rate(fw["offsets"], w.T, w.k)
@@ -418,7 +438,9 @@ def layer_bwd(inp: Dict[str, np.ndarray], w, fw: Dict[str, np.ndarray],
     r32 = rounder("f32", exact)
     dOut = to_f64(inp["dOut"])
     R = fw["R"]
-    dYp, dg = combine_bwd(dOut, fw["Y"], fw["row_of"], fw["gate"], R, rnd, r32)
+    fb = w.kind == "layer" and w.fallback == "identity"
+    dYp, dg = combine_bwd(dOut, fw["Y"], fw["row_of"], fw["gate"], R, rnd, r32,
+                          fw["x"] if fb else None)
     off = fw["offsets"]
     dXp = np.zeros((R, w.d))
     dA = np.zeros((R, w.f))
@@ -431,7 +453,8 @@ def layer_bwd(inp: Dict[str, np.ndarray], w, fw: Dict[str, np.ndarray],
             fw["A"][lo:hi], fw["H"][lo:hi], dYp[lo:hi], rnd)
     bw = dict(dYp=dYp, dgate=dg, dXp=dXp, dA=dA, dW1=dW1, dW2=dW2)
     if w.kind == "layer":
-        dXe = r32(unpermute_bwd(dXp, fw["row_of"]))
+        dXe = r32(unpermute_bwd(dXp, fw["row_of"], fw["gate"] if fb else None,
+                                dOut if fb else None))
         aux = aux_dp(fw["counts"], w.T, w.k, w.aux_coeff) if w.aux_coeff > 0 else None
         dz = router_dz(fw["probs"], fw["idx"], fw["row_of"], dg, aux, w.renorm)
         dX, dWr, db = route_bwd(fw["x"], to_f64(inp["Wr"]), dz, dXe, rnd, r32)

@@ -242,6 +242,28 @@ def test_slot_priority_with_one_expert_per_token_is_token_priority():
             np.testing.assert_array_equal(u, v)
 
 
+def test_identity_fallback_closed_forms():
+    """With every assignment dropped the identity fallback returns
+    (sum_j gate_j) x: exactly x when k = E (the probabilities sum to 1) or
+    when the gates are renormalised; without drops it changes nothing."""
+    T, d, E, f = 9, 5, 4, 6
+    inp = _exact_inputs(T, d, E, 2, f, seed=21)
+    for k, renorm in ((E, False), (2, True)):
+        w = W.custom(T, d, E, k, f, cf=0.0, renorm=renorm, fallback="identity")
+        fw = O.layer_fwd(inp, w, exact=True)
+        assert fw["R"] == 0
+        np.testing.assert_allclose(fw["out"], inp["x"], rtol=1e-14, atol=1e-15)
+        bw = O.layer_bwd(inp, w, fw, exact=True)
+        # no expert ran: the expert weights get no gradient
+        assert np.all(bw["dW1"] == 0) and np.all(bw["dW2"] == 0)
+    w0 = W.custom(T, d, E, 2, f, cf=None)
+    w1 = W.custom(T, d, E, 2, f, cf=None, fallback="identity")
+    np.testing.assert_array_equal(O.layer_fwd(inp, w0, exact=True)["out"],
+                                  O.layer_fwd(inp, w1, exact=True)["out"])
+    with pytest.raises(ValueError):
+        O.layer_fwd(inp, W.custom(T, d, E, 2, f, cf=None, fallback="skip"), exact=True)
+
+
 def test_renormalised_gates_closed_forms():
     rng = np.random.default_rng(6)
     z = rng.standard_normal((20, 7))
@@ -376,20 +398,24 @@ def _min_topk_gap(z, k):
     return np.min(zs[:, :kk - 1] - zs[:, 1:kk]) if kk > 1 else np.inf
 
 
-@pytest.mark.parametrize("T,d,E,k,f,cf,aux,renorm,prio", [
-    (10, 4, 3, 2, 5, None, 0.0, False, "token"),
-    (12, 5, 4, 2, 6, 0.75, 0.0, False, "token"),
-    (7, 3, 4, 1, 4, 1.0, 0.0, False, "token"),
-    (6, 4, 5, 3, 3, None, 0.0, False, "token"),
-    (12, 5, 4, 2, 6, 0.75, 0.3, False, "token"),
-    (9, 4, 5, 1, 3, None, 2.0, False, "token"),
-    (12, 5, 4, 2, 6, 0.75, 0.0, True, "token"),    # renormalised gates with drops
-    (6, 4, 5, 3, 3, None, 0.3, True, "token"),     # renormalised, balancing loss
-    (12, 5, 4, 2, 6, 0.75, 0.0, False, "slot"),    # slot-major priority with drops
-    (10, 4, 4, 3, 5, 0.8, 0.0, True, "slot"),
+@pytest.mark.parametrize("T,d,E,k,f,cf,aux,renorm,prio,fb", [
+    (10, 4, 3, 2, 5, None, 0.0, False, "token", "none"),
+    (12, 5, 4, 2, 6, 0.75, 0.0, False, "token", "none"),
+    (7, 3, 4, 1, 4, 1.0, 0.0, False, "token", "none"),
+    (6, 4, 5, 3, 3, None, 0.0, False, "token", "none"),
+    (12, 5, 4, 2, 6, 0.75, 0.3, False, "token", "none"),
+    (9, 4, 5, 1, 3, None, 2.0, False, "token", "none"),
+    (12, 5, 4, 2, 6, 0.75, 0.0, True, "token", "none"),   # renormalised gates, drops
+    (6, 4, 5, 3, 3, None, 0.3, True, "token", "none"),    # renormalised, balancing loss
+    (12, 5, 4, 2, 6, 0.75, 0.0, False, "slot", "none"),   # slot-major priority, drops
+    (10, 4, 4, 3, 5, 0.8, 0.0, True, "slot", "none"),
+    (12, 5, 4, 2, 6, 0.75, 0.0, False, "token", "identity"),  # identity fallback
+    (10, 4, 4, 3, 5, 0.8, 0.2, True, "slot", "identity"),     # everything at once
 ])
-def test_backward_matches_central_finite_differences(T, d, E, k, f, cf, aux, renorm, prio):
-    w = W.custom(T, d, E, k, f, cf=cf, aux_coeff=aux, renorm=renorm, priority=prio)
+def test_backward_matches_central_finite_differences(T, d, E, k, f, cf, aux, renorm, prio,
+                                                     fb):
+    w = W.custom(T, d, E, k, f, cf=cf, aux_coeff=aux, renorm=renorm, priority=prio,
+                 fallback=fb)
     seed = 0
     while True:      # pick a seed whose routing margins exceed the step by far
         inp = _exact_inputs(T, d, E, k, f, seed=seed)
@@ -418,13 +444,14 @@ def test_backward_matches_central_finite_differences(T, d, E, k, f, cf, aux, ren
                                    err_msg=name)
 
 
-@pytest.mark.parametrize("renorm", [False, True])
-def test_backward_matches_torch_autograd_in_fp64(renorm):
+@pytest.mark.parametrize("renorm,fb", [(False, "none"), (True, "none"),
+                                       (False, "identity"), (True, "identity")])
+def test_backward_matches_torch_autograd_in_fp64(renorm, fb):
     """Independent library cross-check: the same layer written with torch
     autograd (routing and drops taken from the oracle, then held fixed)."""
     torch = pytest.importorskip("torch")
     T, d, E, k, f = 16, 6, 5, 2, 7
-    w = W.custom(T, d, E, k, f, cf=1.0, renorm=renorm)
+    w = W.custom(T, d, E, k, f, cf=1.0, renorm=renorm, fallback=fb)
     inp = _exact_inputs(T, d, E, k, f, seed=11)
     fw = O.layer_fwd(inp, w, exact=True)
     bw = O.layer_bwd(inp, w, fw, exact=True)
@@ -437,6 +464,8 @@ def test_backward_matches_torch_autograd_in_fp64(renorm):
         gates = sel / sel.sum() if renorm else sel
         for j in range(k):
             if fw["row_of"][t, j] < 0:
+                if fb == "identity":     # the token passes the expert unchanged
+                    out[t] = out[t] + gates[j] * tt["x"][t]
                 continue
             e = int(fw["idx"][t, j])
             hdn = torch.nn.functional.gelu(tt["x"][t] @ tt["W1"][e], approximate="tanh")

@@ -58,6 +58,7 @@ class Workload:
     aux_coeff: float = 0.0  # load-balancing loss coefficient (0 = none)
     renorm: bool = False    # gates renormalised over the selected k experts
     priority: str = "token"  # capacity priority: 'token' (token-major) | 'slot'
+    fallback: str = "none"   # dropped assignments: 'none' | 'identity' (pass-through)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -88,10 +89,10 @@ def get(name: str) -> Workload:
 
 def custom(T, d, E, k, f, dtype="f32", cf=None, bias="zero",
            kind="layer", name="custom", w_std=0.02, aux_coeff=0.0, renorm=False,
-           priority="token") -> Workload:
+           priority="token", fallback="none") -> Workload:
     return Workload(name, T=T, d=d, E=E, k=k, f=f, dtype=dtype, cf=cf,
                     bias=bias, kind=kind, w_std=w_std, aux_coeff=aux_coeff,
-                    renorm=renorm, priority=priority)
+                    renorm=renorm, priority=priority, fallback=fallback)
 
 
 # ---------------------------------------------------------------- storage
