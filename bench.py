@@ -57,6 +57,8 @@ def parse():
                     help="gates renormalised over the selected experts")
     ap.add_argument("--priority", choices=("token", "slot"), default="token",
                     help="capacity priority: token-major (default) or slot-major")
+    ap.add_argument("--fallback", choices=("none", "identity"), default="none",
+                    help="dropped assignments: dropped (default) or the identity fallback")
     ap.add_argument("--recompute", action="store_true",
                     help="selective recomputation: A and H are not saved and the "
                          "backward recomputes them (one extra grouped GEMM)")
@@ -202,8 +204,9 @@ def main():
 
     import workloads as W
     w = W.get(a.config)
-    if a.aux_coeff or a.renorm or a.priority != "token":
-        w = dataclasses.replace(w, aux_coeff=a.aux_coeff, renorm=a.renorm, priority=a.priority)
+    if a.aux_coeff or a.renorm or a.priority != "token" or a.fallback != "none":
+        w = dataclasses.replace(w, aux_coeff=a.aux_coeff, renorm=a.renorm, priority=a.priority,
+                                fallback=a.fallback)
     if a.summarize_counters:
         return summarize_counters(a, w)
     import expert_router_gemm_softmax_amd as M
@@ -219,7 +222,7 @@ def main():
         cap = M.moe_capacity(w.T, w.k, w.E, w.cf)
     cfg = M.make_cfg(w.T, w.d, w.E, w.k, w.f, w.dtype, capacity=cap,
                      aux_coeff=a.aux_coeff, recompute=a.recompute, renorm=a.renorm,
-                     priority=a.priority)
+                     priority=a.priority, fallback=a.fallback)
     sdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
     if w.kind == "layer":
@@ -326,7 +329,7 @@ def main():
                    "tokens": w.T, "d": w.d, "experts": w.E, "top_k": w.k, "ffn": w.f,
                    "capacity": cap, "kept_rows": R, "parallelism": "single GPU",
                    "aux_coeff": a.aux_coeff, "recompute": a.recompute,
-                   "renorm": a.renorm, "priority": a.priority},
+                   "renorm": a.renorm, "priority": a.priority, "fallback": a.fallback},
         "roofline": roof,
         "gpu_event_ms_per_step": round(gpu_ms / a.steps, 4),
     }

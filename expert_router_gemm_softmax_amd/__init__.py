@@ -6,7 +6,8 @@ backward, as hand-written HIP kernels behind the C-ABI of include/moe.h.
 The Python side only marshals arguments; importing fails loudly when
 libmoe.so has not been built.
 """
-from .binding import (KERNELS, MOE_BF16, MOE_FLAG_RECOMPUTE, MOE_FLAG_RENORM,
+from .binding import (KERNELS, MOE_BF16, MOE_FLAG_DROP_IDENTITY, MOE_FLAG_RECOMPUTE,
+                      MOE_FLAG_RENORM,
                       MOE_FLAG_SLOT_PRIORITY, MOE_FP32, MOE_NO_CAPACITY,
                       MoeCfg, MoeCtx,
                       MoeError, MoeGrads, MoeLibraryError, MoeWeights, LIB_PATH,

@@ -30,6 +30,7 @@ MOE_NO_CAPACITY = -1
 MOE_FLAG_RECOMPUTE = 1
 MOE_FLAG_RENORM = 2
 MOE_FLAG_SLOT_PRIORITY = 4
+MOE_FLAG_DROP_IDENTITY = 8
 
 KERNELS = dict(ROUTE=0, PERMUTE_COUNT=1, PERMUTE_SCAN=2, PERMUTE_SCATTER=3,
                GEMM_UP=4, GEMM_DOWN=5, COMBINE=6, COMBINE_BWD=7, GEMM_DH=8,
@@ -86,12 +87,12 @@ _SIGS = {
     "moe_route": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_permute": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_grouped_ffn": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
-    "moe_combine": (c_int, [_CFG, _P, _P, _P, _P, _P]),
-    "moe_combine_bwd": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_combine": (c_int, [_CFG, _P, _P, _P, _P, _P, _P]),
+    "moe_combine_bwd": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_ffn_bwd": (c_int, [_CFG] + [_P] * 11 + [c_size_t, _P]),
-    "moe_unpermute_bwd": (c_int, [_CFG, _P, _P, _P, _P]),
+    "moe_unpermute_bwd": (c_int, [_CFG, _P, _P, _P, _P, _P, _P]),
     "moe_router_aux": (c_int, [_CFG, _P, _P, _P, _P, _P, c_size_t, _P]),
-    "moe_route_bwd": (c_int, [_CFG] + [_P] * 12 + [c_size_t, _P]),
+    "moe_route_bwd": (c_int, [_CFG] + [_P] * 14 + [c_size_t, _P]),
     "moe_layer_fwd": (c_int, [_CFG, POINTER(MoeWeights), _P, _P, POINTER(MoeCtx), _P,
                               c_size_t, _P]),
     "moe_layer_bwd": (c_int, [_CFG, POINTER(MoeWeights), _P, _P, POINTER(MoeCtx), _P,
@@ -173,21 +174,26 @@ def _stream(stream):
 
 
 def make_cfg(T, d, E, k, f, dtype="bf16", capacity=None, route_margin=0.0,
-             aux_coeff=0.0, recompute=False, renorm=False, priority="token") -> MoeCfg:
+             aux_coeff=0.0, recompute=False, renorm=False, priority="token",
+             fallback="none") -> MoeCfg:
     """capacity: None = no limit, else an int >= 0; aux_coeff: weight of the
     load-balancing loss (0 = none); recompute: keep A and H out of the saved
     state and recompute them in backward (MOE_FLAG_RECOMPUTE); renorm: gates
     renormalised over the selected experts (MOE_FLAG_RENORM); priority:
-    'token' or 'slot' capacity walk (MOE_FLAG_SLOT_PRIORITY)."""
+    'token' or 'slot' capacity walk (MOE_FLAG_SLOT_PRIORITY); fallback: 'none'
+    or 'identity' for dropped assignments (MOE_FLAG_DROP_IDENTITY)."""
     if priority not in ("token", "slot"):
         raise ValueError(f"priority must be 'token' or 'slot', not {priority!r}")
+    if fallback not in ("none", "identity"):
+        raise ValueError(f"fallback must be 'none' or 'identity', not {fallback!r}")
     dt = {"bf16": MOE_BF16, "f32": MOE_FP32, MOE_BF16: MOE_BF16, MOE_FP32: MOE_FP32}[dtype]
     return MoeCfg(T=int(T), d=int(d), E=int(E), k=int(k), f=int(f), dtype=dt,
                   capacity=MOE_NO_CAPACITY if capacity is None else int(capacity),
                   route_margin=float(route_margin),
                   flags=((MOE_FLAG_RECOMPUTE if recompute else 0)
                          | (MOE_FLAG_RENORM if renorm else 0)
-                         | (MOE_FLAG_SLOT_PRIORITY if priority == "slot" else 0)),
+                         | (MOE_FLAG_SLOT_PRIORITY if priority == "slot" else 0)
+                         | (MOE_FLAG_DROP_IDENTITY if fallback == "identity" else 0)),
                   aux_coeff=float(aux_coeff))
 
 
@@ -226,14 +232,16 @@ def moe_grouped_ffn(cfg, x_perm, offsets, W1, W2, A, H, Y, ws, stream=None):
         _ptr(Y), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def moe_combine(cfg, Y, row_of, gate, out, stream=None):
+def moe_combine(cfg, Y, row_of, gate, out, x=None, stream=None):
+    """x: only read under the identity fallback (MOE_FLAG_DROP_IDENTITY)."""
     _check("moe_combine", lib.moe_combine(
-        byref(cfg), _ptr(Y), _ptr(row_of), _ptr(gate), _ptr(out), _stream(stream)))
+        byref(cfg), _ptr(Y), _ptr(row_of), _ptr(gate), _ptr(x), _ptr(out), _stream(stream)))
 
 
-def moe_combine_bwd(cfg, dOut, Y, row_of, gate, dYp, dgate, stream=None):
+def moe_combine_bwd(cfg, dOut, Y, row_of, gate, dYp, dgate, x=None, stream=None):
+    """x: only read under the identity fallback (MOE_FLAG_DROP_IDENTITY)."""
     _check("moe_combine_bwd", lib.moe_combine_bwd(
-        byref(cfg), _ptr(dOut), _ptr(Y), _ptr(row_of), _ptr(gate), _ptr(dYp),
+        byref(cfg), _ptr(dOut), _ptr(Y), _ptr(row_of), _ptr(gate), _ptr(x), _ptr(dYp),
         _ptr(dgate), _stream(stream)))
 
 
@@ -245,9 +253,11 @@ def moe_grouped_ffn_bwd(cfg, x_perm, offsets, W1, W2, A, H, dYp, dXp, dW1, dW2, 
         _stream(stream)))
 
 
-def moe_unpermute_bwd(cfg, dXp, row_of, dXe, stream=None):
+def moe_unpermute_bwd(cfg, dXp, row_of, dXe, gate=None, dOut=None, stream=None):
+    """gate, dOut: only read under the identity fallback."""
     _check("moe_unpermute_bwd", lib.moe_unpermute_bwd(
-        byref(cfg), _ptr(dXp), _ptr(row_of), _ptr(dXe), _stream(stream)))
+        byref(cfg), _ptr(dXp), _ptr(row_of), _ptr(gate), _ptr(dOut), _ptr(dXe),
+        _stream(stream)))
 
 
 def moe_router_aux(cfg, probs, counts, offsets, aux, ws, stream=None):
@@ -257,12 +267,13 @@ def moe_router_aux(cfg, probs, counts, offsets, aux, ws, stream=None):
 
 
 def moe_route_bwd(cfg, x, Wr, probs, idx, row_of, counts, dgate, dXp, dX, dWr, db, ws,
-                  stream=None):
-    """counts may be None when cfg.aux_coeff is 0."""
+                  gate=None, dOut=None, stream=None):
+    """counts may be None when cfg.aux_coeff is 0; gate and dOut are only
+    read under the identity fallback."""
     _check("moe_route_bwd", lib.moe_route_bwd(
         byref(cfg), _ptr(x), _ptr(Wr), _ptr(probs), _ptr(idx), _ptr(row_of), _ptr(counts),
-        _ptr(dgate), _ptr(dXp), _ptr(dX), _ptr(dWr), _ptr(db), _ptr(ws), _nbytes(ws),
-        _stream(stream)))
+        _ptr(gate), _ptr(dOut), _ptr(dgate), _ptr(dXp), _ptr(dX), _ptr(dWr), _ptr(db),
+        _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_layer_fwd(cfg, weights: MoeWeights, x, out, ctx: MoeCtx, ws, stream=None):

@@ -61,7 +61,8 @@ int check_cfg(const moe_cfg* c) {
   if (c->k < 1 || c->k > 32 || c->E < c->k || c->E > 256) return MOE_ERR_ARG;
   if (c->d < 1 || c->f < 1) return MOE_ERR_ARG;
   if (c->capacity < MOE_NO_CAPACITY) return MOE_ERR_ARG;
-  if ((c->flags & ~(MOE_FLAG_RECOMPUTE | MOE_FLAG_RENORM | MOE_FLAG_SLOT_PRIORITY)) != 0)
+  if ((c->flags & ~(MOE_FLAG_RECOMPUTE | MOE_FLAG_RENORM | MOE_FLAG_SLOT_PRIORITY |
+                    MOE_FLAG_DROP_IDENTITY)) != 0)
     return MOE_ERR_ARG;
   if (c->T * c->k > 0x7fffffffLL) return MOE_ERR_SHAPE;
   if (!(c->route_margin == c->route_margin)) return MOE_ERR_ARG;  // NaN
@@ -114,6 +115,8 @@ inline hipStream_t S(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); 
 // A and H are caller buffers unless the recomputation mode keeps them in
 // the workspace
 inline bool saves_ah(const moe_cfg& c) { return (c.flags & MOE_FLAG_RECOMPUTE) == 0; }
+// the identity fallback of dropped assignments reads x, gate and dOut
+inline bool fallback(const moe_cfg& c) { return (c.flags & MOE_FLAG_DROP_IDENTITY) != 0; }
 
 }  // namespace
 }  // namespace moe
@@ -212,21 +215,22 @@ int moe_grouped_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offse
 }
 
 int moe_combine(const moe_cfg* cfg, const void* Y, const int32_t* row_of, const float* gate,
-                void* out, moe_stream_t stream) {
+                const void* x, void* out, moe_stream_t stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_cfg& c = *cfg;
   const Sizes z = sizes(c);
   MOE_TRY(need(Y, z.Rd, 16));
   MOE_TRY(need(row_of, z.Tk, 4));
   MOE_TRY(need(gate, z.Tk, 4));
+  if (fallback(c)) MOE_TRY(need(x, z.Td, 16));
   MOE_TRY(need(out, z.Td, 16));
   clear_stale_error();
-  return launch_combine(c, Y, row_of, gate, out, S(stream));
+  return launch_combine(c, Y, row_of, gate, x, out, S(stream));
 }
 
 int moe_combine_bwd(const moe_cfg* cfg, const void* dOut, const void* Y,
-                    const int32_t* row_of, const float* gate, void* dYp, float* dgate,
-                    moe_stream_t stream) {
+                    const int32_t* row_of, const float* gate, const void* x, void* dYp,
+                    float* dgate, moe_stream_t stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_cfg& c = *cfg;
   const Sizes z = sizes(c);
@@ -234,10 +238,11 @@ int moe_combine_bwd(const moe_cfg* cfg, const void* dOut, const void* Y,
   MOE_TRY(need(Y, z.Rd, 16));
   MOE_TRY(need(row_of, z.Tk, 4));
   MOE_TRY(need(gate, z.Tk, 4));
+  if (fallback(c)) MOE_TRY(need(x, z.Td, 16));
   MOE_TRY(need(dYp, z.Rd, 16));
   MOE_TRY(need(dgate, z.Tk, 4));
   clear_stale_error();
-  return launch_combine_bwd(c, dOut, Y, row_of, gate, dYp, dgate, S(stream));
+  return launch_combine_bwd(c, dOut, Y, row_of, gate, x, dYp, dgate, S(stream));
 }
 
 int moe_grouped_ffn_bwd(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
@@ -266,15 +271,19 @@ int moe_grouped_ffn_bwd(const moe_cfg* cfg, const void* x_perm, const int32_t* o
 }
 
 int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp, const int32_t* row_of,
-                      float* dXe, moe_stream_t stream) {
+                      const float* gate, const void* dOut, float* dXe, moe_stream_t stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_cfg& c = *cfg;
   const Sizes z = sizes(c);
   MOE_TRY(need(dXp, z.Rd, 16));
   MOE_TRY(need(row_of, z.Tk, 4));
+  if (fallback(c)) {
+    MOE_TRY(need(gate, z.Tk, 4));
+    MOE_TRY(need(dOut, z.Td, 16));
+  }
   MOE_TRY(need(dXe, (size_t)c.T * c.d * 4, 16));
   clear_stale_error();
-  return launch_unpermute_bwd(c, dXp, row_of, dXe, S(stream));
+  return launch_unpermute_bwd(c, dXp, row_of, gate, dOut, dXe, S(stream));
 }
 
 int moe_router_aux(const moe_cfg* cfg, const float* probs, const int32_t* counts,
@@ -294,8 +303,9 @@ int moe_router_aux(const moe_cfg* cfg, const float* probs, const int32_t* counts
 
 int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr, const float* probs,
                   const int32_t* idx, const int32_t* row_of, const int32_t* counts,
-                  const float* dgate, const void* dXp, void* dX, void* dWr, float* db,
-                  void* ws, size_t ws_bytes, moe_stream_t stream) {
+                  const float* gate, const void* dOut, const float* dgate, const void* dXp,
+                  void* dX, void* dWr, float* db, void* ws, size_t ws_bytes,
+                  moe_stream_t stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_cfg& c = *cfg;
   const Sizes z = sizes(c);
@@ -305,6 +315,10 @@ int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr, const float
   MOE_TRY(need(idx, z.Tk, 4));
   MOE_TRY(need(row_of, z.Tk, 4));
   if (c.aux_coeff > 0.0f) MOE_TRY(need(counts, (size_t)c.E * 4, 4));
+  if (fallback(c)) {
+    MOE_TRY(need(gate, z.Tk, 4));
+    MOE_TRY(need(dOut, z.Td, 16));
+  }
   MOE_TRY(need(dgate, z.Tk, 4));
   MOE_TRY(need(dXp, z.Rd, 16));
   MOE_TRY(need(dX, z.Td, 16));
@@ -312,8 +326,8 @@ int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr, const float
   if (db) MOE_TRY(need(db, (size_t)c.E * 4, 4));
   MOE_TRY(need_ws(c, ws, ws_bytes));
   clear_stale_error();
-  return launch_route_bwd(c, x, Wr, probs, idx, row_of, counts, dgate, dXp, dX, dWr, db, ws,
-                          S(stream));
+  return launch_route_bwd(c, x, Wr, probs, idx, row_of, counts, gate, dOut, dgate, dXp, dX,
+                          dWr, db, ws, S(stream));
 }
 
 static int check_ctx(const moe_cfg& c, const moe_ctx* x) {
@@ -366,7 +380,7 @@ int moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const void* x, void*
     MOE_TRY(launch_route_aux(c, ctx->probs, ctx->counts, ctx->offsets, ctx->aux, ws, s));
   MOE_TRY(launch_ffn_fwd(c, ctx->x_perm, ctx->offsets, w->W1, w->W2, ctx->A, ctx->H, ctx->Y,
                          ws, s));
-  return launch_combine(c, ctx->Y, ctx->row_of, ctx->gate, out, s);
+  return launch_combine(c, ctx->Y, ctx->row_of, ctx->gate, x, out, s);
 }
 
 int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* x, const void* dOut,
@@ -392,11 +406,11 @@ int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* x, const
   void* dYp = ws_ptr<void>(ws, L.dYp);
   void* dXp = ws_ptr<void>(ws, L.dXp);
   clear_stale_error();
-  MOE_TRY(launch_combine_bwd(c, dOut, ctx->Y, ctx->row_of, ctx->gate, dYp, dgate, s));
+  MOE_TRY(launch_combine_bwd(c, dOut, ctx->Y, ctx->row_of, ctx->gate, x, dYp, dgate, s));
   MOE_TRY(launch_ffn_bwd(c, ctx->x_perm, ctx->offsets, w->W1, w->W2, ctx->A, ctx->H, dYp,
                          dXp, g->dW1, g->dW2, ws, s));
-  return launch_route_bwd(c, x, w->Wr, ctx->probs, ctx->idx, ctx->row_of, ctx->counts, dgate,
-                          dXp, dX, g->dWr, g->db, ws, s);
+  return launch_route_bwd(c, x, w->Wr, ctx->probs, ctx->idx, ctx->row_of, ctx->counts,
+                          ctx->gate, dOut, dgate, dXp, dX, g->dWr, g->db, ws, s);
 }
 
 const char* moe_last_error(void) { return g_last_error; }

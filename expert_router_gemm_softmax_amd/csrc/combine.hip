@@ -29,11 +29,14 @@ __device__ __forceinline__ void load_pass(const T* __restrict__ src, int64_t r, 
 
 // out[t] = sum over kept j (ascending) of g_j * src[row_of[t,j]], with
 // g_j = gate[t,j] (combine) or 1 (gradient unpermute-sum, fp32 output).
-// One wave per token; two assignments' rows are in flight at once.
+// With a fallback row source fb (the identity fallback: x for the combine,
+// dOut for the unpermute-sum) a dropped j adds gate[t,j] * fb[t] in its
+// place.  One wave per token; two assignments' rows are in flight at once.
 template <typename T, typename OutT, bool GATED>
 __global__ __launch_bounds__(256) void gather_sum_kernel(
     const T* __restrict__ src, const int32_t* __restrict__ row_of,
-    const float* __restrict__ gate, OutT* __restrict__ out, int64_t T_, int d, int k) {
+    const float* __restrict__ gate, const T* __restrict__ fb, OutT* __restrict__ out,
+    int64_t T_, int d, int k) {
   constexpr int V = St<T>::kVec;
   const int lane = threadIdx.x & 63;
   const int nch = d / V;
@@ -48,15 +51,19 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(
         for (int q = 0; q < V; ++q) acc[s][q] = 0.0f;
       for (int j = 0; j < k; j += 2) {
         const int32_t r0 = rows[j];
-        const int32_t r1 = j + 1 < k ? rows[j + 1] : -1;
+        const int32_t r1 = j + 1 < k ? rows[j + 1] : -2;  // -2: no assignment
+        const bool u0 = r0 >= 0 || (fb && r0 == -1);
+        const bool u1 = r1 >= 0 || (fb && r1 == -1);
         u32x4 y0[kCPL], y1[kCPL];
-        load_pass(src, r0, d, g0, nch, lane, y0);
-        load_pass(src, r1, d, g0, nch, lane, y1);
+        load_pass(r0 >= 0 ? src : fb, u0 ? (r0 >= 0 ? (int64_t)r0 : t) : -1, d, g0, nch, lane,
+                  y0);
+        load_pass(r1 >= 0 ? src : fb, u1 ? (r1 >= 0 ? (int64_t)r1 : t) : -1, d, g0, nch, lane,
+                  y1);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int32_t r = h ? r1 : r0;
-          if (r < 0) continue;
-          const float g = GATED ? gate[t * k + j + h] : 1.0f;
+          if (!(h ? u1 : u0)) continue;
+          const float g = (GATED || r < 0) ? gate[t * k + j + h] : 1.0f;
 #pragma unroll
           for (int s = 0; s < kCPL; ++s) {
             if (g0 + s * kWave + lane >= nch) continue;
@@ -88,11 +95,12 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(
 // dYp[row] = gate * dOut[t];  dgate[t,j] = <dOut[t], Y[row]> (0 if dropped).
 // One wave per token: each pass holds dOut's chunks in registers while the
 // k rows of Y stream past, two at a time; lane j keeps dgate[t,j].
+// With the identity fallback (x given) a dropped j gets <dOut[t], x[t]>.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const T* __restrict__ dOut, const T* __restrict__ Y, const int32_t* __restrict__ row_of,
-    const float* __restrict__ gate, T* __restrict__ dYp, float* __restrict__ dgate,
-    int64_t T_, int d, int k) {
+    const float* __restrict__ gate, const T* __restrict__ x, T* __restrict__ dYp,
+    float* __restrict__ dgate, int64_t T_, int d, int k) {
   constexpr int V = St<T>::kVec;
   const int lane = threadIdx.x & 63;
   const int nch = d / V;
@@ -105,14 +113,16 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
       load_pass(dOut, t, d, g0, nch, lane, gv);
       for (int j = 0; j < k; j += 2) {
         const int32_t r0 = rows[j];
-        const int32_t r1 = j + 1 < k ? rows[j + 1] : -1;
+        const int32_t r1 = j + 1 < k ? rows[j + 1] : -2;  // -2: no assignment
+        const bool u0 = r0 >= 0 || (x && r0 == -1);
+        const bool u1 = r1 >= 0 || (x && r1 == -1);
         u32x4 y0[kBwdCPL], y1[kBwdCPL];
-        load_pass(Y, r0, d, g0, nch, lane, y0);
-        load_pass(Y, r1, d, g0, nch, lane, y1);
+        load_pass(r0 >= 0 ? Y : x, u0 ? (r0 >= 0 ? (int64_t)r0 : t) : -1, d, g0, nch, lane, y0);
+        load_pass(r1 >= 0 ? Y : x, u1 ? (r1 >= 0 ? (int64_t)r1 : t) : -1, d, g0, nch, lane, y1);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int32_t r = h ? r1 : r0;
-          if (r < 0) continue;  // uniform over the wave
+          if (!(h ? u1 : u0)) continue;  // uniform over the wave
           const float gj = gate[t * k + j + h];
           float pp = 0.0f;
 #pragma unroll
@@ -127,14 +137,14 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
               pp += g[q] * y[q];
               o[q] = gj * g[q];
             }
-            st16(dYp + (int64_t)r * d + c * V, St<T>::pack(o));
+            if (r >= 0) st16(dYp + (int64_t)r * d + c * V, St<T>::pack(o));
           }
           pp = wave_sum(pp);
           if (lane == j + h) mine += pp;
         }
       }
     }
-    if (lane < k) dgate[t * k + lane] = rows[lane] >= 0 ? mine : 0.0f;
+    if (lane < k) dgate[t * k + lane] = (rows[lane] >= 0 || x) ? mine : 0.0f;
   }
 }
 
@@ -146,52 +156,61 @@ inline int token_grid(int64_t T_) {
 }  // namespace
 
 int launch_combine(const moe_cfg& c, const void* Y, const int32_t* row_of,
-                   const float* gate, void* out, hipStream_t s) {
+                   const float* gate, const void* x, void* out, hipStream_t s) {
   if (c.T == 0) return MOE_OK;
   const int grid = token_grid(c.T);
+  const void* fb = (c.flags & MOE_FLAG_DROP_IDENTITY) ? x : nullptr;
   if (c.dtype == MOE_BF16)
     MOE_LAUNCH(MOE_KERNEL_COMBINE, s,
                gather_sum_kernel<uint16_t, uint16_t, true><<<grid, 256, 0, s>>>(
                    static_cast<const uint16_t*>(Y), row_of, gate,
-                   static_cast<uint16_t*>(out), c.T, c.d, c.k));
+                   static_cast<const uint16_t*>(fb), static_cast<uint16_t*>(out), c.T, c.d,
+                   c.k));
   else
     MOE_LAUNCH(MOE_KERNEL_COMBINE, s,
                gather_sum_kernel<float, float, true><<<grid, 256, 0, s>>>(
-                   static_cast<const float*>(Y), row_of, gate, static_cast<float*>(out),
-                   c.T, c.d, c.k));
+                   static_cast<const float*>(Y), row_of, gate, static_cast<const float*>(fb),
+                   static_cast<float*>(out), c.T, c.d, c.k));
   return MOE_OK;
 }
 
 int launch_combine_bwd(const moe_cfg& c, const void* dOut, const void* Y,
-                       const int32_t* row_of, const float* gate, void* dYp,
+                       const int32_t* row_of, const float* gate, const void* x, void* dYp,
                        float* dgate, hipStream_t s) {
   if (c.T == 0) return MOE_OK;
   const int grid = token_grid(c.T);
+  const void* fb = (c.flags & MOE_FLAG_DROP_IDENTITY) ? x : nullptr;
   if (c.dtype == MOE_BF16)
     MOE_LAUNCH(MOE_KERNEL_COMBINE_BWD, s,
                combine_bwd_kernel<uint16_t><<<grid, 256, 0, s>>>(
                    static_cast<const uint16_t*>(dOut), static_cast<const uint16_t*>(Y),
-                   row_of, gate, static_cast<uint16_t*>(dYp), dgate, c.T, c.d, c.k));
+                   row_of, gate, static_cast<const uint16_t*>(fb),
+                   static_cast<uint16_t*>(dYp), dgate, c.T, c.d, c.k));
   else
     MOE_LAUNCH(MOE_KERNEL_COMBINE_BWD, s,
                combine_bwd_kernel<float><<<grid, 256, 0, s>>>(
                    static_cast<const float*>(dOut), static_cast<const float*>(Y), row_of,
-                   gate, static_cast<float*>(dYp), dgate, c.T, c.d, c.k));
+                   gate, static_cast<const float*>(fb), static_cast<float*>(dYp), dgate,
+                   c.T, c.d, c.k));
   return MOE_OK;
 }
 
 int launch_unpermute_bwd(const moe_cfg& c, const void* dXp, const int32_t* row_of,
-                         float* dXe, hipStream_t s, int kernel_id) {
+                         const float* gate, const void* dOut, float* dXe, hipStream_t s,
+                         int kernel_id) {
   if (c.T == 0) return MOE_OK;
   const int grid = token_grid(c.T);
+  const void* fb = (c.flags & MOE_FLAG_DROP_IDENTITY) ? dOut : nullptr;
   if (c.dtype == MOE_BF16)
     MOE_LAUNCH(kernel_id, s,
                gather_sum_kernel<uint16_t, float, false><<<grid, 256, 0, s>>>(
-                   static_cast<const uint16_t*>(dXp), row_of, nullptr, dXe, c.T, c.d, c.k));
+                   static_cast<const uint16_t*>(dXp), row_of, gate,
+                   static_cast<const uint16_t*>(fb), dXe, c.T, c.d, c.k));
   else
     MOE_LAUNCH(kernel_id, s,
                gather_sum_kernel<float, float, false><<<grid, 256, 0, s>>>(
-                   static_cast<const float*>(dXp), row_of, nullptr, dXe, c.T, c.d, c.k));
+                   static_cast<const float*>(dXp), row_of, gate, static_cast<const float*>(fb),
+                   dXe, c.T, c.d, c.k));
   return MOE_OK;
 }
 

@@ -289,16 +289,20 @@ int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
                    const void* W1, const void* W2, const void* A, const void* H,
                    const void* dYp, void* dXp, void* dW1, void* dW2, void* ws,
                    hipStream_t s);
+// x, gate and dOut feed the identity fallback of dropped assignments
+// (MOE_FLAG_DROP_IDENTITY) and are unused otherwise.
 int launch_combine(const moe_cfg& c, const void* Y, const int32_t* row_of,
-                   const float* gate, void* out, hipStream_t s);
+                   const float* gate, const void* x, void* out, hipStream_t s);
 int launch_combine_bwd(const moe_cfg& c, const void* dOut, const void* Y,
-                       const int32_t* row_of, const float* gate, void* dYp,
+                       const int32_t* row_of, const float* gate, const void* x, void* dYp,
                        float* dgate, hipStream_t s);
 int launch_unpermute_bwd(const moe_cfg& c, const void* dXp, const int32_t* row_of,
-                         float* dXe, hipStream_t s, int kernel_id = MOE_KERNEL_UNPERMUTE_BWD);
+                         const float* gate, const void* dOut, float* dXe, hipStream_t s,
+                         int kernel_id = MOE_KERNEL_UNPERMUTE_BWD);
 int launch_route_bwd(const moe_cfg& c, const void* x, const void* Wr,
                      const float* probs, const int32_t* idx, const int32_t* row_of,
-                     const int32_t* counts, const float* dgate, const void* dXp, void* dX,
-                     void* dWr, float* db, void* ws, hipStream_t s);
+                     const int32_t* counts, const float* gate, const void* dOut,
+                     const float* dgate, const void* dXp, void* dX, void* dWr, float* db,
+                     void* ws, hipStream_t s);
 
 }  // namespace moe

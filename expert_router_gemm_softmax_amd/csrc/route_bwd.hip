@@ -8,7 +8,9 @@
 //   (dgate_j - sum_i g_i dgate_i) / S instead, dropped j included)
 //   dz = p * (dp - sum_e p dp)
 // where a_e = alpha E counts[e] / (T k T) is the gradient of the
-// load-balancing loss (zero when its coefficient alpha is zero).
+// load-balancing loss (zero when its coefficient alpha is zero); under the
+// identity fallback of dropped assignments their dgate counts as well, and
+// dX gains gate * dOut for each of them (in the unpermute-sum).
 //   dX  = sum_{kept j} dXp[row_of[t,j]] + dz Wr^T
 //   dWr = x^T dz,  db = sum_t dz
 // Both products run on the grouped GEMM kernels.  For bf16 storage dz is
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
     const int32_t* __restrict__ row_of, const int32_t* __restrict__ counts,
     const float* __restrict__ dgate, float* __restrict__ dz, uint16_t* __restrict__ dzb,
     float* __restrict__ db_part, int64_t T_, int E, int Ep, int k, float aux_scale,
-    bool renorm) {
+    bool renorm, bool fallback) {
   __shared__ float sdb[4][256];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float dbacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -65,12 +67,12 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
       for (int j = 0; j < k; ++j) S += psel(j);
       float G = 0.0f;
       for (int j = 0; j < k; ++j) {
-        const float dg = row_of[t * k + j] < 0 ? 0.0f : dgate[t * k + j];
+        const float dg = row_of[t * k + j] < 0 && !fallback ? 0.0f : dgate[t * k + j];
         G += psel(j) / S * dg;
       }
       for (int j = 0; j < k; ++j) {
         const int e = idx[t * k + j];
-        const float dg = row_of[t * k + j] < 0 ? 0.0f : dgate[t * k + j];
+        const float dg = row_of[t * k + j] < 0 && !fallback ? 0.0f : dgate[t * k + j];
         const float g = (dg - G) / S;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
       }
     } else {
       for (int j = 0; j < k; ++j) {
-        if (row_of[t * k + j] < 0) continue;
+        if (row_of[t * k + j] < 0 && !fallback) continue;
         const int e = idx[t * k + j];
         const float g = dgate[t * k + j];
 #pragma unroll
@@ -173,8 +175,8 @@ __global__ __launch_bounds__(256) void route_bwd_reduce_kernel(
 template <typename T>
 int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
                 const int32_t* idx, const int32_t* row_of, const int32_t* counts,
-                const float* dgate, const T* dXp, T* dX, T* dWr, float* db, void* ws,
-                hipStream_t s) {
+                const float* gate, const void* dOut, const float* dgate, const T* dXp, T* dX,
+                T* dWr, float* db, void* ws, hipStream_t s) {
   constexpr bool BF = sizeof(T) == 2;
   const WsLayout L = ws_layout(c);
   const int Ep = bwd_ep(c.E);
@@ -194,7 +196,8 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
                route_bwd_dz_kernel<BF><<<nblk, 256, 0, s>>>(probs, idx, row_of, counts, dgate,
                                                            dz, dzb, dbp, c.T, c.E, Ep, c.k,
                                                            aux_scale,
-                                                           (c.flags & MOE_FLAG_RENORM) != 0));
+                                                           (c.flags & MOE_FLAG_RENORM) != 0,
+                                                           (c.flags & MOE_FLAG_DROP_IDENTITY) != 0));
   if constexpr (BF) {
     const int64_t n = (int64_t)c.d * 2 * Ep;
     MOE_LAUNCH(MOE_KERNEL_ROUTE_PREP, s,
@@ -205,7 +208,7 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
   if (c.T > 0) {
     // dX = [dz_hi | dz_lo] [Wr | Wr]^T + unpermute-sum of dXp (fp32)
     float* dxe = ws_ptr<float>(ws, L.dxe);
-    rc = launch_unpermute_bwd(c, dXp, row_of, dxe, s, MOE_KERNEL_ROUTE_BWD_DX);
+    rc = launch_unpermute_bwd(c, dXp, row_of, gate, dOut, dxe, s, MOE_KERNEL_ROUTE_BWD_DX);
     if (rc != MOE_OK) return rc;
     GemmArgs g{};
     g.E = 1;
@@ -254,17 +257,18 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
 
 int launch_route_bwd(const moe_cfg& c, const void* x, const void* Wr,
                      const float* probs, const int32_t* idx, const int32_t* row_of,
-                     const int32_t* counts, const float* dgate, const void* dXp, void* dX,
-                     void* dWr, float* db, void* ws, hipStream_t s) {
+                     const int32_t* counts, const float* gate, const void* dOut,
+                     const float* dgate, const void* dXp, void* dX, void* dWr, float* db,
+                     void* ws, hipStream_t s) {
   if (c.dtype == MOE_BF16)
     return route_bwd_t<uint16_t>(c, static_cast<const uint16_t*>(x),
                                  static_cast<const uint16_t*>(Wr), probs, idx, row_of, counts,
-                                 dgate,
+                                 gate, dOut, dgate,
                                  static_cast<const uint16_t*>(dXp),
                                  static_cast<uint16_t*>(dX), static_cast<uint16_t*>(dWr), db,
                                  ws, s);
   return route_bwd_t<float>(c, static_cast<const float*>(x), static_cast<const float*>(Wr),
-                            probs, idx, row_of, counts, dgate,
+                            probs, idx, row_of, counts, gate, dOut, dgate,
                             static_cast<const float*>(dXp),
                             static_cast<float*>(dX), static_cast<float*>(dWr), db, ws, s);
 }

@@ -90,6 +90,15 @@ typedef enum { MOE_FP32 = 0, MOE_BF16 = 1 } moe_dtype;
  * not fixed by the pages ("The Capacity Factor" only says the excess is
  * dropped). */
 #define MOE_FLAG_SLOT_PRIORITY 4u
+/* MOE_FLAG_DROP_IDENTITY: a dropped assignment takes the identity fallback
+ * path -- the token passes the expert unchanged -- instead of contributing
+ * nothing: it adds gate[t,j] * x[t] to out[t], and backward gate[t,j] *
+ * dOut[t] to dX[t] with dgate[t,j] = <dOut[t], x[t]>.  "The Capacity
+ * Factor" lets excess tokens take a fallback path without defining it; the
+ * pass-through is the plainest one.  Under it, moe_combine and
+ * moe_combine_bwd need x, and moe_unpermute_bwd and moe_route_bwd need gate
+ * and dOut. */
+#define MOE_FLAG_DROP_IDENTITY 8u
 
 /* hipStream_t, passed opaquely so that this header needs no HIP headers. */
 typedef void* moe_stream_t;
@@ -195,9 +204,11 @@ MOE_API int moe_grouped_ffn(const moe_cfg* cfg, const void* x_perm,
  * token order ("The step timeline"), weighted by the gates:
  *   out[t] = sum over kept j (ascending) of gate[t,j] * Y[row_of[t,j]],
  * fp32 accumulation, one rounding to s; 0 for a token with every
- * assignment dropped.  out [T,d] s. */
+ * assignment dropped.  Under MOE_FLAG_DROP_IDENTITY a dropped j adds
+ * gate[t,j] * x[t] in its place (x [T,d] s; otherwise x is unused and may
+ * be NULL).  out [T,d] s. */
 MOE_API int moe_combine(const moe_cfg* cfg, const void* Y, const int32_t* row_of,
-                const float* gate, void* out, moe_stream_t stream);
+                const float* gate, const void* x, void* out, moe_stream_t stream);
 
 /* Routing diagnostics and the auxiliary load-balancing loss.  The
  * distributed-training tutorial (section "The Capacity Factor") adds a
@@ -223,11 +234,13 @@ MOE_API int moe_router_aux(const moe_cfg* cfg, const float* probs, const int32_t
 
 /* B5 combine backward:
  *   dYp[row_of[t,j]] = RN_s(gate[t,j] * dOut[t])  [Rmax,d] s
- *   dgate[t,j]       = <dOut[t], Y[row_of[t,j]]>  [T,k] float (0 if dropped)
+ *   dgate[t,j]       = <dOut[t], Y[row_of[t,j]]>  [T,k] float (0 if dropped;
+ *                      <dOut[t], x[t]> under MOE_FLAG_DROP_IDENTITY, which
+ *                      needs x [T,d] s -- otherwise x may be NULL)
  */
 MOE_API int moe_combine_bwd(const moe_cfg* cfg, const void* dOut, const void* Y,
-                    const int32_t* row_of, const float* gate, void* dYp,
-                    float* dgate, moe_stream_t stream);
+                    const int32_t* row_of, const float* gate, const void* x,
+                    void* dYp, float* dgate, moe_stream_t stream);
 
 /* B4+B3 grouped expert FFN backward; per expert e over its rows (under
  * MOE_FLAG_RECOMPUTE, A and H are first recomputed from x_perm into the
@@ -249,9 +262,12 @@ MOE_API int moe_grouped_ffn_bwd(const moe_cfg* cfg, const void* x_perm,
                         void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* B2 inverse of the permute for gradients:
- *   dXe[t] = sum over kept j of dXp[row_of[t,j]]   [T,d] float */
+ *   dXe[t] = sum over kept j of dXp[row_of[t,j]]   [T,d] float
+ * plus gate[t,j] * dOut[t] for each dropped j under MOE_FLAG_DROP_IDENTITY
+ * (gate [T,k] float and dOut [T,d] s; otherwise both may be NULL). */
 MOE_API int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp,
-                      const int32_t* row_of, float* dXe, moe_stream_t stream);
+                      const int32_t* row_of, const float* gate, const void* dOut,
+                      float* dXe, moe_stream_t stream);
 
 /* B1 router backward (the router is a shared parameter with an ordinary
  * gradient -- "Sharded by expert, replicated everywhere else"):
@@ -261,18 +277,21 @@ MOE_API int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp,
  *       under MOE_FLAG_RENORM the gate term is instead
  *       (dgate[t,j] - sum_i g_i dgate[t,i]) / S for every selected j, with
  *       S = sum_i probs[t, idx[t,i]] and g_i = probs[t, idx[t,i]] / S
- *       (dgate of a dropped assignment counts as 0)
+ *       (dgate of a dropped assignment counts as 0, except under
+ *       MOE_FLAG_DROP_IDENTITY, where every assignment's dgate counts)
  *   dz  = probs * (dp - sum_e probs * dp)
  *   db  = sum_t dz                       [E] float
  *   dWr = x^T dz                         [d,E] s
  *   dX  = sum_{kept j} dXp[row_of[t,j]] + dz Wr^T   [T,d] s
+ *         (+ gate[t,j] * dOut[t] for each dropped j under
+ *         MOE_FLAG_DROP_IDENTITY; gate and dOut may be NULL otherwise)
  * (the unpermute-sum of B2 is fused in).  Workspace as above. */
 MOE_API int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr,
                   const float* probs, const int32_t* idx,
                   const int32_t* row_of, const int32_t* counts /* [E]; may be NULL
-                  when cfg->aux_coeff == 0 */, const float* dgate, const void* dXp,
-                  void* dX, void* dWr, float* db, void* ws, size_t ws_bytes,
-                  moe_stream_t stream);
+                  when cfg->aux_coeff == 0 */, const float* gate, const void* dOut,
+                  const float* dgate, const void* dXp, void* dX, void* dWr, float* db,
+                  void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------ whole layer */
 

@@ -74,7 +74,7 @@ def cfg_of(M, w, route_margin=0.0, recompute=False):
     cap = O.capacity(w.T, w.k, w.E, w.cf)
     return M.make_cfg(w.T, w.d, w.E, w.k, w.f, w.dtype, capacity=cap,
                       route_margin=route_margin, aux_coeff=w.aux_coeff, recompute=recompute,
-                      renorm=w.renorm, priority=w.priority)
+                      renorm=w.renorm, priority=w.priority, fallback=w.fallback)
 
 
 def red_tol(ref, dtype):
@@ -236,9 +236,9 @@ def check_aux(name, aux, probs, fw, w, coeff):
 
 
 def make_case(T, d, E, k, f, dtype, cf, bias="zero", seed=0, aux_coeff=0.0, renorm=False,
-              priority="token", **kw):
+              priority="token", fallback="none", **kw):
     w = W.custom(T, d, E, k, f, dtype=dtype, cf=cf, bias=bias, name=f"T{T}d{d}E{E}k{k}f{f}",
-                 aux_coeff=aux_coeff, renorm=renorm, priority=priority)
+                 aux_coeff=aux_coeff, renorm=renorm, priority=priority, fallback=fallback)
     inp = W.make_inputs(w, seed=seed)
     for key, v in kw.items():
         inp[key] = v

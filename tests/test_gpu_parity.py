@@ -165,25 +165,28 @@ def test_balancing_gradient_alone(M, dt):
 
 
 VARIANT_CASES = [
-    # T, d, E, k, f, dtype, cf, bias, renorm, priority
-    (513, 64, 40, 3, 136, "bf16", 0.75, "zipf", True, "slot"),   # both, skew, drops
-    (1000, 264, 6, 2, 200, "bf16", 1.1, "zero", True, "token"),  # renormalised top-2
-    (300, 36, 5, 2, 52, "f32", 0.9, "normal", False, "slot"),    # fp32, slot-major
-    (260, 48, 130, 8, 40, "bf16", None, "normal", True, "token"),  # E > 128, k = 8
-    (100, 64, 40, 32, 64, "bf16", 1.0, "normal", True, "slot"),  # k = 32
-    (777, 128, 16, 4, 96, "bf16", 0.6, "normal", False, "slot"),  # many drops
+    # T, d, E, k, f, dtype, cf, bias, renorm, priority, fallback
+    (513, 64, 40, 3, 136, "bf16", 0.75, "zipf", True, "slot", "identity"),  # all three
+    (1000, 264, 6, 2, 200, "bf16", 1.1, "zero", True, "token", "none"),  # renormalised top-2
+    (300, 36, 5, 2, 52, "f32", 0.9, "normal", False, "slot", "identity"),  # fp32
+    (260, 48, 130, 8, 40, "bf16", None, "normal", True, "token", "none"),  # E > 128, k = 8
+    (100, 64, 40, 32, 64, "bf16", 1.0, "normal", True, "slot", "none"),  # k = 32
+    (777, 128, 16, 4, 96, "bf16", 0.6, "normal", False, "token", "identity"),  # many drops
+    (200, 64, 4, 4, 64, "bf16", 0.0, "normal", False, "token", "identity"),  # all dropped
 ]
 
 
 @pytest.mark.parametrize("case", VARIANT_CASES,
-                         ids=lambda c: "T{}E{}k{}{}{}{}".format(c[0], c[2], c[3], c[5],
-                                                                "-renorm" if c[8] else "",
-                                                                "-" + c[9]))
+                         ids=lambda c: "T{}E{}k{}{}{}-{}{}".format(
+                             c[0], c[2], c[3], c[5], "-renorm" if c[8] else "", c[9],
+                             "-identity" if c[10] == "identity" else ""))
 def test_routing_variants_match_oracle(M, case):
-    """Renormalised gates and slot-major capacity priority: routing maps
-    bit-exact, gates bitwise their formula, every output within tolerance."""
-    T, d, E, k, f, dt, cf, bias, renorm, prio = case
-    w, inp = make_case(T, d, E, k, f, dt, cf, bias, seed=T + 3, renorm=renorm, priority=prio)
+    """Renormalised gates, slot-major capacity priority and the identity
+    fallback of dropped assignments: routing maps bit-exact, gates bitwise
+    their formula, every output within tolerance."""
+    T, d, E, k, f, dt, cf, bias, renorm, prio, fb = case
+    w, inp = make_case(T, d, E, k, f, dt, cf, bias, seed=T + 3, renorm=renorm, priority=prio,
+                       fallback=fb)
     say("case", case)
     res = run_layer(M, w, inp)
     fw = O.layer_fwd(inp, w)
@@ -194,15 +197,24 @@ def test_routing_variants_match_oracle(M, case):
         tok = O.assign(fw["idx"], E, fw["C"], "token")[2]
         say("  R =", R, "kept sets differ from token-major:",
             bool(np.any((tok >= 0) != (fw["row_of"] >= 0))))
+    if fb == "identity" and cf == 0.0 and k == E:
+        # every assignment dropped, gates summing to 1: the layer returns x
+        assert R == 0
+        assert_close("out = x", to_f64(res["out"]), O.to_f64(inp["x"]), dt)
 
 
-@pytest.mark.parametrize("recompute", [False, True], ids=["save", "recompute"])
-def test_step_entry_points_equal_the_layer_entry_points(M, recompute):
+@pytest.mark.parametrize("mode", ["save", "recompute", "variants"])
+def test_step_entry_points_equal_the_layer_entry_points(M, mode):
     """moe_route .. moe_route_bwd called one by one give bitwise the layer's
     results (same kernels, same order); in the recomputation mode with no A
-    and H buffers at all."""
+    and H buffers at all; with every routing variant on (renormalised gates,
+    slot priority, identity fallback), whose extra inputs the step entry
+    points then take."""
     import torch
-    w, inp = make_case(700, 128, 8, 2, 160, "bf16", 1.0, "normal", seed=7, aux_coeff=0.05)
+    recompute = mode == "recompute"
+    var = dict(renorm=True, priority="slot", fallback="identity") if mode == "variants" else {}
+    w, inp = make_case(700, 128, 8, 2, 160, "bf16", 1.0, "normal", seed=7, aux_coeff=0.05,
+                       **var)
     res = run_layer(M, w, inp, recompute=recompute)
     cfg, d, L = res["_cfg"], res["_dev"], res["_layer"]
     T, E, k = w.T, w.E, w.k
@@ -221,16 +233,16 @@ def test_step_entry_points_equal_the_layer_entry_points(M, recompute):
         A = H = None
     M.moe_grouped_ffn(cfg, xp, offsets, d["W1"], d["W2"], A, H, Y, ws)
     out = z(T, w.d)
-    M.moe_combine(cfg, Y, row_of, gate, out)
+    M.moe_combine(cfg, Y, row_of, gate, out, x=d["x"])
     dYp, dg = z(Rmax, w.d), z(T, k, dt=torch.float32)
-    M.moe_combine_bwd(cfg, d["dOut"], Y, row_of, gate, dYp, dg)
+    M.moe_combine_bwd(cfg, d["dOut"], Y, row_of, gate, dYp, dg, x=d["x"])
     dXp, dW1, dW2 = z(Rmax, w.d), torch.zeros_like(d["W1"]), torch.zeros_like(d["W2"])
     M.moe_grouped_ffn_bwd(cfg, xp, offsets, d["W1"], d["W2"], A, H, dYp, dXp, dW1, dW2, ws)
     dXe = z(T, w.d, dt=torch.float32)
-    M.moe_unpermute_bwd(cfg, dXp, row_of, dXe)
+    M.moe_unpermute_bwd(cfg, dXp, row_of, dXe, gate=gate, dOut=d["dOut"])
     dX, dWr, db = z(T, w.d), torch.zeros_like(d["Wr"]), z(E, dt=torch.float32)
     M.moe_route_bwd(cfg, d["x"], d["Wr"], probs, idx, row_of, counts, dg, dXp, dX, dWr, db,
-                    ws)
+                    ws, gate=gate, dOut=d["dOut"])
     torch.cuda.synchronize()
     R = int(to_int(offsets)[-1])
     for name, a, b in [("probs", probs, res["probs"]), ("idx", idx, res["idx"]),
@@ -255,6 +267,8 @@ def test_step_entry_points_equal_the_layer_entry_points(M, recompute):
     for j in range(w.k):
         m = fw["row_of"][:, j] >= 0
         gn[m, j] = np.sqrt(((dOut[m] * fw["Y"][fw["row_of"][m, j]]) ** 2).sum(axis=1))
+        if w.fallback == "identity":   # dropped: <dOut, x>
+            gn[~m, j] = np.sqrt(((dOut[~m] * fw["x"][~m]) ** 2).sum(axis=1))
     assert_close("dgate", to_f64(dg), bw["dgate"], terms_tol(gn, "bf16"))
 
 

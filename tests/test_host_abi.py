@@ -103,10 +103,11 @@ def test_bad_dtype_and_flags():
     c.dtype = 7
     assert M.moe_check_cfg(c) == B.MOE_ERR_DTYPE
     c = M.make_cfg(16, 64, 8, 2, 64, "bf16")
-    for bad in (8, 16, 1 << 31):
+    for bad in (16, 32, 1 << 31):
         c.flags = bad
         assert M.moe_check_cfg(c) == B.MOE_ERR_ARG
-    for ok in (B.MOE_FLAG_RECOMPUTE, B.MOE_FLAG_RENORM, B.MOE_FLAG_SLOT_PRIORITY, 7):
+    for ok in (B.MOE_FLAG_RECOMPUTE, B.MOE_FLAG_RENORM, B.MOE_FLAG_SLOT_PRIORITY,
+               B.MOE_FLAG_DROP_IDENTITY, 15):
         c.flags = ok
         assert M.moe_check_cfg(c) == B.MOE_OK
     c = M.make_cfg(16, 64, 8, 2, 64, "bf16", recompute=True, renorm=True, priority="slot")
@@ -149,7 +150,7 @@ def test_entry_points_reject_bad_arguments_before_launch():
     bad = M.make_cfg(16, 64, 8, 2, 64, "bf16")
     bad.k = 9
     assert _call_route(bad) == B.MOE_ERR_ARG
-    assert B.lib.moe_combine(ctypes.byref(c), None, _A, _A, _A, None) == B.MOE_ERR_ARG
+    assert B.lib.moe_combine(ctypes.byref(c), None, _A, _A, None, _A, None) == B.MOE_ERR_ARG
     assert B.lib.moe_permute(ctypes.byref(c), _A, _A, _A, _A, _A, _A, _A, _A, 0,
                              None) == B.MOE_ERR_WORKSPACE
     assert B.lib.moe_layer_fwd(ctypes.byref(c), None, _A, _A, None, _A, 1 << 30,
@@ -193,6 +194,31 @@ def test_recompute_mode_moves_a_and_h_into_the_workspace():
     assert ws > 0
 
 
+def test_identity_fallback_entry_points_need_its_extra_inputs():
+    plain = M.make_cfg(16, 64, 8, 2, 64, "bf16")
+    fb = M.make_cfg(16, 64, 8, 2, 64, "bf16", fallback="identity")
+    assert fb.flags == B.MOE_FLAG_DROP_IDENTITY and M.moe_check_cfg(fb) == B.MOE_OK
+    with pytest.raises(ValueError):
+        M.make_cfg(16, 64, 8, 2, 64, "bf16", fallback="zero")
+    # combine: x only under the flag (a NULL out stops a valid call first)
+    comb = lambda cfg, x: B.lib.moe_combine(ctypes.byref(cfg), _A, _A, _A, x, None, None)
+    assert comb(plain, None) == B.MOE_ERR_ARG and comb(fb, None) == B.MOE_ERR_ARG
+    assert B.lib.moe_combine(ctypes.byref(fb), _A, _A, _A, _A + 2, _A, None) == B.MOE_ERR_ALIGN
+    cb = lambda cfg, x: B.lib.moe_combine_bwd(ctypes.byref(cfg), _A, _A, _A, _A, x, _A, None,
+                                              None)
+    assert cb(plain, None) == B.MOE_ERR_ARG   # dgate NULL
+    assert cb(fb, _A + 2) == B.MOE_ERR_ALIGN
+    ub = lambda cfg, g, dO: B.lib.moe_unpermute_bwd(ctypes.byref(cfg), _A, _A, g, dO, None,
+                                                    None)
+    assert ub(fb, None, _A) == B.MOE_ERR_ARG and ub(fb, _A, None) == B.MOE_ERR_ARG
+    assert ub(plain, None, None) == B.MOE_ERR_ARG  # dXe NULL
+    rb = lambda cfg, g, dO: B.lib.moe_route_bwd(
+        ctypes.byref(cfg), _A, _A, _A, _A, _A, None, g, dO, _A, _A, _A, _A, None, _A, 10, None)
+    assert rb(fb, None, _A) == B.MOE_ERR_ARG and rb(fb, _A, None) == B.MOE_ERR_ARG
+    assert rb(fb, _A, _A) == B.MOE_ERR_WORKSPACE
+    assert rb(plain, None, None) == B.MOE_ERR_WORKSPACE
+
+
 @pytest.mark.parametrize("coeff", [-0.01, float("nan"), float("inf")])
 def test_invalid_balancing_coefficient_is_rejected(coeff):
     c = M.make_cfg(16, 64, 8, 2, 64, "bf16", aux_coeff=coeff)
@@ -213,7 +239,8 @@ def test_balancing_entry_points_validate_arguments():
     assert aux(ctypes.byref(c), _A, _A, _A, _A, _A, 10, None) == B.MOE_ERR_WORKSPACE
     # the router backward needs counts only when the loss is on
     rb = lambda cfg, counts: B.lib.moe_route_bwd(
-        ctypes.byref(cfg), _A, _A, _A, _A, _A, counts, _A, _A, _A, _A, None, _A, 10, None)
+        ctypes.byref(cfg), _A, _A, _A, _A, _A, counts, None, None, _A, _A, _A, _A, None, _A,
+        10, None)
     assert rb(c, None) == B.MOE_ERR_ARG
     assert rb(c, _A) == B.MOE_ERR_WORKSPACE
     c.aux_coeff = 0.0
