@@ -28,10 +28,14 @@ __global__ __launch_bounds__(256) void route_aux_part_kernel(const float* __rest
   const int64_t t0 = (int64_t)blockIdx.x * kAuxTokens;
   const int n = (int)(T_ - t0 < kAuxTokens ? T_ - t0 : kAuxTokens);
   const float* p = probs + t0 * E + e;
-  // every row's load in flight at once, then the sum in token order
+  // every row's load in flight at once (indices clamped into the block's
+  // rows so that no load sits behind a branch), then the sum in token order
   float v[kAuxTokens];
 #pragma unroll
-  for (int q = 0; q < kAuxTokens; ++q) v[q] = q < n ? p[(int64_t)q * E] : 0.0f;
+  for (int q = 0; q < kAuxTokens; ++q) v[q] = p[(int64_t)min(q, n - 1) * E];
+#pragma unroll
+  for (int q = 0; q < kAuxTokens; ++q)
+    if (q >= n) v[q] = 0.0f;
   float s = 0.0f;
 #pragma unroll
   for (int q = 0; q < kAuxTokens; ++q) s += v[q];
@@ -56,10 +60,10 @@ __global__ __launch_bounds__(1024) void route_aux_final_kernel(
     for (int b0 = 0; b0 < nblk; b0 += kWave * U) {
       float v[U];
 #pragma unroll
-      for (int q = 0; q < U; ++q) {
-        const int b = b0 + q * kWave + lane;
-        v[q] = b < nblk ? pe[b] : 0.0f;
-      }
+      for (int q = 0; q < U; ++q) v[q] = pe[min(b0 + q * kWave + lane, nblk - 1)];
+#pragma unroll
+      for (int q = 0; q < U; ++q)
+        if (b0 + q * kWave + lane >= nblk) v[q] = 0.0f;
 #pragma unroll
       for (int q = 0; q < U; ++q) s += (double)v[q];
     }
