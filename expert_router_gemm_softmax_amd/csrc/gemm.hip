@@ -679,6 +679,18 @@ inline int64_t row_mtiles_bound(const moe_cfg& c, int BM) {
   return ceil_div(rows_max(c), BM) + c.E;
 }
 
+// A one-group problem's tile count is known here: whether split_of would
+// split its tail (256 slots), so that a problem without a split launches no
+// fixup kernel.
+inline bool one_group_splits(int M, int BM, int ntn, int K) {
+  const int64_t ntotal = ceil_div(M, BM) * ntn;
+  const int64_t rem = ntotal % 256;
+  if (rem == 0) return false;
+  const int64_t nkt = ceil_div(K, BK_ALL);
+  const int64_t sp = std::min<int64_t>(256 / rem, nkt);
+  return sp >= 3;
+}
+
 template <int MODE, bool B_KC, int EPI>
 int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
   const bool bf = c.dtype == MOE_BF16;
@@ -709,7 +721,8 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
   if constexpr (MODE == MODE_ROW) {
     // split-K tail for the bf16 kernels: whole tiles, then up to one block
     // per CU for the parts
-    if (bf && g.part != nullptr && (BM == 256 || BM == 128) && BN == BM) {
+    if (bf && g.part != nullptr && (BM == 256 || BM == 128) && BN == BM &&
+        (g.offsets || one_group_splits(g.M, BM, g.ntn, g.K))) {
       g.slots = 256;  // CUs
       nblk = grid8(nblk) + g.slots;
     } else {
@@ -736,7 +749,9 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
   if constexpr (MODE == MODE_ROW) {
     if (g.part != nullptr) {
       // the GEMM and its tail fixup are timed as one launch
-      const int fgrid = (int)std::min<int64_t>(ceil_div((int64_t)g.slots * BM * BN / 8, 256), 2048);
+      // grid-stride over the split tiles' 8-column chunks; few blocks, so that
+      // a problem whose tail was not split pays little for the launch
+      const int fgrid = (int)std::min<int64_t>(ceil_div((int64_t)g.slots * BM * BN / 8, 256), 512);
       prof_begin(kid, s);
       if (BM == 256) {
         MOE_LAUNCH_NP(kid, gemm_bf16_kernel<MODE, B_KC, EPI, 256, 256><<<grid, 256, 0, s>>>(g));

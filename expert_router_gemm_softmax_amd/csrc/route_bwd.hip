@@ -25,16 +25,33 @@
 namespace moe {
 namespace {
 
+// wrp[i][e] = wrp[i][Ep + e] = Wr[i][e] (zero for E <= e < Ep): the router
+// weights stacked twice for the [hi | lo] products, a grid-stride share of
+// the copy per block of the dz kernel
+__device__ __forceinline__ void stack_wr(const uint16_t* __restrict__ Wr,
+                                         uint16_t* __restrict__ wrp, int d, int E, int Ep) {
+  const int64_t n = (int64_t)d * 2 * Ep;
+  for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < n;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(o / (2 * Ep));
+    int e = (int)(o - (int64_t)i * 2 * Ep);
+    if (e >= Ep) e -= Ep;
+    wrp[o] = e < E ? Wr[(int64_t)i * E + e] : (uint16_t)0;
+  }
+}
+
 // dz for kDzTokens tokens per block (one wave per token); writes dz (fp32
 // storage) or its bf16 hi/lo split (bf16 storage), and the block's partial
-// sums of dz for db.  counts may be NULL when aux_scale is zero.
+// sums of dz for db; for bf16 storage also the stacked router weights.
+// counts may be NULL when aux_scale is zero.
 template <bool BF>
 __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
     const float* __restrict__ probs, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ row_of, const int32_t* __restrict__ counts,
     const float* __restrict__ dgate, float* __restrict__ dz, uint16_t* __restrict__ dzb,
-    float* __restrict__ db_part, int64_t T_, int E, int Ep, int k, float aux_scale,
-    bool renorm, bool fallback) {
+    float* __restrict__ db_part, const uint16_t* __restrict__ Wr, uint16_t* __restrict__ wrp,
+    int d, int64_t T_, int E, int Ep, int k, float aux_scale, bool renorm, bool fallback) {
+  if constexpr (BF) stack_wr(Wr, wrp, d, E, Ep);
   __shared__ float sdb[4][256];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float dbacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -117,18 +134,6 @@ __global__ __launch_bounds__(256) void route_bwd_dz_kernel(
         (sdb[0][e] + sdb[1][e]) + (sdb[2][e] + sdb[3][e]);
 }
 
-// wrp[i][e] = wrp[i][Ep + e] = Wr[i][e] (zero for E <= e < Ep)
-__global__ void stack_wr_kernel(const uint16_t* __restrict__ Wr, uint16_t* __restrict__ wrp,
-                                int d, int E, int Ep) {
-  const int64_t n = (int64_t)d * 2 * Ep;
-  for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < n;
-       o += (int64_t)gridDim.x * blockDim.x) {
-    const int i = (int)(o / (2 * Ep));
-    int e = (int)(o - (int64_t)i * 2 * Ep);
-    if (e >= Ep) e -= Ep;
-    wrp[o] = e < E ? Wr[(int64_t)i * E + e] : (uint16_t)0;
-  }
-}
 
 // dWr[i][e] = sum over chunks (fixed order) of part[c][i][e] (+ the low half)
 // and db[e] = sum over blocks of db_part[e][b]
@@ -193,17 +198,11 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
           : 0.0f;
   if (nblk > 0)
     MOE_LAUNCH(MOE_KERNEL_ROUTE_BWD_DZ, s,
-               route_bwd_dz_kernel<BF><<<nblk, 256, 0, s>>>(probs, idx, row_of, counts, dgate,
-                                                           dz, dzb, dbp, c.T, c.E, Ep, c.k,
-                                                           aux_scale,
-                                                           (c.flags & MOE_FLAG_RENORM) != 0,
-                                                           (c.flags & MOE_FLAG_DROP_IDENTITY) != 0));
-  if constexpr (BF) {
-    const int64_t n = (int64_t)c.d * 2 * Ep;
-    MOE_LAUNCH(MOE_KERNEL_ROUTE_PREP, s,
-               stack_wr_kernel<<<(int)std::min<int64_t>(ceil_div(n, 256), 4096), 256, 0, s>>>(
-                   reinterpret_cast<const uint16_t*>(Wr), wrp, c.d, c.E, Ep));
-  }
+               route_bwd_dz_kernel<BF><<<nblk, 256, 0, s>>>(
+                   probs, idx, row_of, counts, dgate, dz, dzb, dbp,
+                   BF ? reinterpret_cast<const uint16_t*>(Wr) : nullptr, wrp, c.d, c.T, c.E, Ep,
+                   c.k, aux_scale, (c.flags & MOE_FLAG_RENORM) != 0,
+                   (c.flags & MOE_FLAG_DROP_IDENTITY) != 0));
   int rc;
   if (c.T > 0) {
     // dX = [dz_hi | dz_lo] [Wr | Wr]^T + unpermute-sum of dXp (fp32)
