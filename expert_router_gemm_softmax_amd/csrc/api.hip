@@ -374,12 +374,14 @@ int moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const void* x, void*
   const WsLayout L = ws_layout(c);
   clear_stale_error();
   MOE_TRY(launch_route(c, x, w->Wr, w->b, ctx->probs, ctx->idx, ctx->gate, ws, s));
+  // the permute also writes the grouped GEMMs' tile schedule
+  int32_t* tiles = ws_ptr<int32_t>(ws, L.tiles);
   MOE_TRY(launch_permute(c, x, ctx->idx, ctx->counts, ctx->offsets, ctx->row_of,
-                         ctx->src_of, ctx->x_perm, ws, s));
+                         ctx->src_of, ctx->x_perm, ws, s, tiles));
   if (ctx->aux)
     MOE_TRY(launch_route_aux(c, ctx->probs, ctx->counts, ctx->offsets, ctx->aux, ws, s));
   MOE_TRY(launch_ffn_fwd(c, ctx->x_perm, ctx->offsets, w->W1, w->W2, ctx->A, ctx->H, ctx->Y,
-                         ws, s));
+                         ws, s, /*have_tiles=*/true));
   return launch_combine(c, ctx->Y, ctx->row_of, ctx->gate, x, out, s);
 }
 
@@ -406,9 +408,12 @@ int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* x, const
   void* dYp = ws_ptr<void>(ws, L.dYp);
   void* dXp = ws_ptr<void>(ws, L.dXp);
   clear_stale_error();
-  MOE_TRY(launch_combine_bwd(c, dOut, ctx->Y, ctx->row_of, ctx->gate, x, dYp, dgate, s));
+  // the combine backward also writes the grouped GEMMs' tile schedule
+  int32_t* tiles = ws_ptr<int32_t>(ws, L.tiles);
+  MOE_TRY(launch_combine_bwd(c, dOut, ctx->Y, ctx->row_of, ctx->gate, x, dYp, dgate, s,
+                             ctx->offsets, tiles));
   MOE_TRY(launch_ffn_bwd(c, ctx->x_perm, ctx->offsets, w->W1, w->W2, ctx->A, ctx->H, dYp,
-                         dXp, g->dW1, g->dW2, ws, s));
+                         dXp, g->dW1, g->dW2, ws, s, /*have_tiles=*/true));
   return launch_route_bwd(c, x, w->Wr, ctx->probs, ctx->idx, ctx->row_of, ctx->counts,
                           ctx->gate, dOut, dgate, dXp, dX, g->dWr, g->db, ws, s);
 }

@@ -100,8 +100,14 @@ template <typename T>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const T* __restrict__ dOut, const T* __restrict__ Y, const int32_t* __restrict__ row_of,
     const float* __restrict__ gate, const T* __restrict__ x, T* __restrict__ dYp,
-    float* __restrict__ dgate, int64_t T_, int d, int k) {
+    float* __restrict__ dgate, int64_t T_, int d, int k, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ tiles, int E, int BM) {
   constexpr int V = St<T>::kVec;
+  if (blockIdx.x == 0 && tiles != nullptr) {  // the grouped GEMMs' M-tile prefix
+    __shared__ int s_wave[4];
+    const int e = threadIdx.x;
+    block_tile_prefix(e < E ? offsets[e + 1] - offsets[e] : 0, E, BM, tiles, s_wave);
+  }
   const int lane = threadIdx.x & 63;
   const int nch = d / V;
   for (int64_t t = (int64_t)blockIdx.x * kCW + (threadIdx.x >> 6); t < T_;
@@ -176,8 +182,9 @@ int launch_combine(const moe_cfg& c, const void* Y, const int32_t* row_of,
 
 int launch_combine_bwd(const moe_cfg& c, const void* dOut, const void* Y,
                        const int32_t* row_of, const float* gate, const void* x, void* dYp,
-                       float* dgate, hipStream_t s) {
+                       float* dgate, hipStream_t s, const int32_t* offsets, int32_t* tiles) {
   if (c.T == 0) return MOE_OK;
+  const int BM = ffn_row_tile(c);
   const int grid = token_grid(c.T);
   const void* fb = (c.flags & MOE_FLAG_DROP_IDENTITY) ? x : nullptr;
   if (c.dtype == MOE_BF16)
@@ -185,13 +192,13 @@ int launch_combine_bwd(const moe_cfg& c, const void* dOut, const void* Y,
                combine_bwd_kernel<uint16_t><<<grid, 256, 0, s>>>(
                    static_cast<const uint16_t*>(dOut), static_cast<const uint16_t*>(Y),
                    row_of, gate, static_cast<const uint16_t*>(fb),
-                   static_cast<uint16_t*>(dYp), dgate, c.T, c.d, c.k));
+                   static_cast<uint16_t*>(dYp), dgate, c.T, c.d, c.k, offsets, tiles, c.E, BM));
   else
     MOE_LAUNCH(MOE_KERNEL_COMBINE_BWD, s,
                combine_bwd_kernel<float><<<grid, 256, 0, s>>>(
                    static_cast<const float*>(dOut), static_cast<const float*>(Y), row_of,
                    gate, static_cast<const float*>(fb), static_cast<float*>(dYp), dgate,
-                   c.T, c.d, c.k));
+                   c.T, c.d, c.k, offsets, tiles, c.E, BM));
   return MOE_OK;
 }
 

@@ -128,6 +128,19 @@ __device__ __forceinline__ int block_exclusive_scan_256(int v, int* s_wave, int*
   return base + incl - v;
 }
 
+// The M-tile prefix of the grouped row GEMMs: tiles[e] = sum over e' < e of
+// ceil(m_e' / BM), tiles[E] = the total, with thread e of a 256-thread block
+// holding m = m_e (0 for e >= E; E <= 256).  Every thread of the block calls
+// it (it synchronises).
+__device__ __forceinline__ void block_tile_prefix(int m, int E, int BM, int32_t* tiles,
+                                                  int* s_wave) {
+  const int e = threadIdx.x;
+  int tot;
+  const int ex = block_exclusive_scan_256((m + BM - 1) / BM, s_wave, &tot);
+  if (e < E) tiles[e] = ex;
+  if (e == 0) tiles[E] = tot;
+}
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -279,23 +292,32 @@ int launch_route(const moe_cfg& c, const void* x, const void* Wr, const float* b
                  float* probs, int32_t* idx, float* gate, void* ws, hipStream_t s);
 int launch_route_aux(const moe_cfg& c, const float* probs, const int32_t* counts,
                      const int32_t* offsets, float* aux, void* ws, hipStream_t s);
+// M tile of the grouped row GEMMs (their tile schedule is built for it)
+int ffn_row_tile(const moe_cfg& c);
+// tiles (nullable): also write the grouped GEMMs' M-tile prefix for the kept
+// rows, so that the layer forward needs no schedule kernel
 int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
                    int32_t* counts, int32_t* offsets, int32_t* row_of,
-                   int32_t* src_of, void* x_perm, void* ws, hipStream_t s);
+                   int32_t* src_of, void* x_perm, void* ws, hipStream_t s,
+                   int32_t* tiles = nullptr);
+// have_tiles: the workspace already holds the M-tile prefix for offsets
+// (written by the permute or the combine backward), so no schedule kernel
 int launch_ffn_fwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
                    const void* W1, const void* W2, void* A, void* H, void* Y,
-                   void* ws, hipStream_t s);
+                   void* ws, hipStream_t s, bool have_tiles = false);
 int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
                    const void* W1, const void* W2, const void* A, const void* H,
                    const void* dYp, void* dXp, void* dW1, void* dW2, void* ws,
-                   hipStream_t s);
+                   hipStream_t s, bool have_tiles = false);
 // x, gate and dOut feed the identity fallback of dropped assignments
 // (MOE_FLAG_DROP_IDENTITY) and are unused otherwise.
 int launch_combine(const moe_cfg& c, const void* Y, const int32_t* row_of,
                    const float* gate, const void* x, void* out, hipStream_t s);
+// offsets and tiles (nullable): also write the grouped GEMMs' M-tile prefix
 int launch_combine_bwd(const moe_cfg& c, const void* dOut, const void* Y,
                        const int32_t* row_of, const float* gate, const void* x, void* dYp,
-                       float* dgate, hipStream_t s);
+                       float* dgate, hipStream_t s, const int32_t* offsets = nullptr,
+                       int32_t* tiles = nullptr);
 int launch_unpermute_bwd(const moe_cfg& c, const void* dXp, const int32_t* row_of,
                          const float* gate, const void* dOut, float* dXe, hipStream_t s,
                          int kernel_id = MOE_KERNEL_UNPERMUTE_BWD);

@@ -647,11 +647,7 @@ __global__ __launch_bounds__(256) void gemm_schedule_kernel(const int32_t* __res
                                                             int BM) {
   __shared__ int s_wave[4];
   const int e = threadIdx.x;
-  const int m = e < E ? offsets[e + 1] - offsets[e] : 0;
-  int tot;
-  const int ex = block_exclusive_scan_256((m + BM - 1) / BM, s_wave, &tot);
-  if (e < E) tiles[e] = ex;
-  if (e == 0) tiles[E] = tot;
+  block_tile_prefix(e < E ? offsets[e + 1] - offsets[e] : 0, E, BM, tiles, s_wave);
 }
 
 constexpr int kFM = 64, kFN = 64;    // fp32 block tile
@@ -784,6 +780,8 @@ int launch_gemm_schedule(const moe_cfg& c, const int32_t* offsets, int32_t* tile
   return schedule(c, offsets, tiles, s);
 }
 
+int ffn_row_tile(const moe_cfg& c) { return row_bm(c); }
+
 int launch_gemm(int kid, int mode, bool b_kc, int epi, const moe_cfg& c, GemmArgs g,
                 hipStream_t s) {
   if (mode == MODE_ROW && !b_kc && epi == EPI_GELU)
@@ -807,11 +805,11 @@ int launch_gemm(int kid, int mode, bool b_kc, int epi, const moe_cfg& c, GemmArg
 
 int launch_ffn_fwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
                    const void* W1, const void* W2, void* A, void* H, void* Y, void* ws,
-                   hipStream_t s) {
+                   hipStream_t s, bool have_tiles) {
   if (rows_max(c) == 0) return MOE_OK;
   const WsLayout L = ws_layout(c);
   int32_t* tiles = ws_ptr<int32_t>(ws, L.tiles);
-  int rc = schedule(c, offsets, tiles, s);
+  int rc = have_tiles ? MOE_OK : schedule(c, offsets, tiles, s);
   if (rc != MOE_OK) return rc;
   const bool rec = (c.flags & MOE_FLAG_RECOMPUTE) != 0;
   if (rec) {
@@ -839,7 +837,7 @@ int launch_ffn_fwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
 int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
                    const void* W1, const void* W2, const void* A, const void* H,
                    const void* dYp, void* dXp, void* dW1, void* dW2, void* ws,
-                   hipStream_t s) {
+                   hipStream_t s, bool have_tiles) {
   const WsLayout L = ws_layout(c);
   int32_t* tiles = ws_ptr<int32_t>(ws, L.tiles);
   void* dA = ws_ptr<void>(ws, L.dA);
@@ -850,7 +848,7 @@ int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
   g.E = c.E;
   g.part = ws_ptr<float>(ws, L.gpart);
   if (rows_max(c) > 0) {
-    rc = schedule(c, offsets, tiles, s);
+    rc = have_tiles ? MOE_OK : schedule(c, offsets, tiles, s);
     if (rc != MOE_OK) return rc;
     if (c.flags & MOE_FLAG_RECOMPUTE) {
       // recompute A and H exactly as the forward does (same kernel, inputs

@@ -85,7 +85,8 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
 __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ blk,
     const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ row_of, int32_t* __restrict__ src_of, Walk wk, int E, int64_t cap) {
+    int32_t* __restrict__ row_of, int32_t* __restrict__ src_of, Walk wk, int E, int64_t cap,
+    int32_t* __restrict__ tiles, int BM) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);  // [kPW][E]
   int32_t* wbase = reinterpret_cast<int32_t*>(mask + kPW * E);            // [kPW][E]
@@ -110,6 +111,8 @@ __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
     if (blockIdx.x == 0) {
       if (e < E) offsets[e] = ex;
       if (e == 0) offsets[E] = tot;
+      // and the grouped GEMMs' M-tile prefix of the kept rows (uniform branch)
+      if (tiles != nullptr) block_tile_prefix(kept, E, BM, tiles, s_wave);
     }
   }
 
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(
 
 int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
                    int32_t* counts, int32_t* offsets, int32_t* row_of,
-                   int32_t* src_of, void* x_perm, void* ws, hipStream_t s) {
+                   int32_t* src_of, void* x_perm, void* ws, hipStream_t s, int32_t* tiles) {
   const WsLayout L = ws_layout(c);
   int32_t* blk = ws_ptr<int32_t>(ws, L.perm_blk);
   Walk wk;
@@ -207,7 +210,8 @@ int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
     const size_t sm = (size_t)kPW * c.E * 8 + (size_t)kPW * c.E * 4 + (size_t)c.E * 4;
     MOE_LAUNCH(MOE_KERNEL_PERMUTE_SCATTER, s,
                permute_scatter_kernel<<<nblk, kPermTokens, sm, s>>>(
-                   idx, blk, counts, offsets, row_of, src_of, wk, c.E, c.capacity));
+                   idx, blk, counts, offsets, row_of, src_of, wk, c.E, c.capacity, tiles,
+                   ffn_row_tile(c)));
     const int g = (int)std::min<int64_t>(ceil_div(c.T, 4), 65536);
     if (c.dtype == MOE_BF16)
       MOE_LAUNCH(MOE_KERNEL_PERMUTE_COPY, s,
