@@ -173,6 +173,9 @@ VARIANT_CASES = [
     (100, 64, 40, 32, 64, "bf16", 1.0, "normal", True, "slot", "none"),  # k = 32
     (777, 128, 16, 4, 96, "bf16", 0.6, "normal", False, "token", "identity"),  # many drops
     (200, 64, 4, 4, 64, "bf16", 0.0, "normal", False, "token", "identity"),  # all dropped
+    (1, 64, 8, 2, 64, "bf16", 1.0, "zero", True, "slot", "identity"),   # a single token
+    (64, 32, 4, 1, 64, "f32", 1.25, "zero", True, "slot", "identity"),  # k = 1: gates 1
+    (300, 64, 256, 16, 64, "bf16", 0.5, "normal", True, "slot", "identity"),  # E = 256
 ]
 
 
@@ -197,6 +200,8 @@ def test_routing_variants_match_oracle(M, case):
         tok = O.assign(fw["idx"], E, fw["C"], "token")[2]
         say("  R =", R, "kept sets differ from token-major:",
             bool(np.any((tok >= 0) != (fw["row_of"] >= 0))))
+    if renorm and k == 1:
+        np.testing.assert_array_equal(to_f64(res["gate"]), 1.0)
     if fb == "identity" and cf == 0.0 and k == E:
         # every assignment dropped, gates summing to 1: the layer returns x
         assert R == 0
