@@ -59,6 +59,8 @@ def parse():
                     help="capacity priority: token-major (default) or slot-major")
     ap.add_argument("--fallback", choices=("none", "identity"), default="none",
                     help="dropped assignments: dropped (default) or the identity fallback")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step into a HIP graph and time K replays of it")
     ap.add_argument("--recompute", action="store_true",
                     help="selective recomputation: A and H are not saved and the "
                          "backward recomputes them (one extra grouped GEMM)")
@@ -269,20 +271,42 @@ def main():
     R = int(offsets[-1].item())
     log(f"[bench] warmup done, R={R} kept rows of {w.T * w.k}")
 
+    run = step
+    if a.graph:
+        # one capture on a side stream (a warm-up there first), then replays
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+
     kernel = a.kernel or "GEMM_DH"
-    M.moe_prof_arm(kernel, a.steps)
+    M.moe_prof_arm(kernel, 0 if a.graph else a.steps)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
     for i in range(a.steps):
-        step()
+        run()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
     k_ms, k_n = M.moe_prof_read()
+    if a.graph:
+        # graph replays record no kernel events: time the roofline kernel on
+        # eager steps after the timed region
+        M.moe_prof_arm(kernel, a.steps)
+        for i in range(a.steps):
+            step()
+        torch.cuda.synchronize()
+        k_ms, k_n = M.moe_prof_read()
     ms_per_step = wall * 1e3 / a.steps
     log(f"[bench] {a.steps} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms; "
         f"{kernel}: {k_n} launches, {k_ms / max(k_n, 1):.4f} ms avg")
@@ -329,7 +353,8 @@ def main():
                    "tokens": w.T, "d": w.d, "experts": w.E, "top_k": w.k, "ffn": w.f,
                    "capacity": cap, "kept_rows": R, "parallelism": "single GPU",
                    "aux_coeff": a.aux_coeff, "recompute": a.recompute,
-                   "renorm": a.renorm, "priority": a.priority, "fallback": a.fallback},
+                   "renorm": a.renorm, "priority": a.priority, "fallback": a.fallback,
+                   "graph_replay": a.graph},
         "roofline": roof,
         "gpu_event_ms_per_step": round(gpu_ms / a.steps, 4),
     }

@@ -344,3 +344,47 @@ def test_c1_full_layer_matches_oracle(M):
     err = logit_error(res, fw)
     say("C1 R", R, "logit err", err)
     assert err <= 1e-3 / 2
+
+
+def test_layer_step_replays_from_a_hip_graph(M):
+    """The whole forward + backward enqueues no allocation, copy or memset,
+    so it can be captured once into a HIP graph and replayed: every replay
+    (with the program's own eager work and synchronisations between them)
+    gives bitwise the eager step's results."""
+    import torch
+    w, inp = make_case(700, 128, 8, 2, 160, "bf16", 1.0, "normal", seed=9, aux_coeff=0.01)
+    cfg = cfg_of(M, w)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    layer = M.MoeLayer(cfg, d["Wr"], d["b"], d["W1"], d["W2"], diagnostics=True)
+    out = torch.empty_like(d["x"])
+    dX = torch.empty_like(d["x"])
+    grads = layer.alloc_grads()
+
+    def step():
+        layer.forward(d["x"], out)
+        layer.backward(d["x"], d["dOut"], dX, grads)
+
+    keys = ("out", "dX", "dWr", "db", "dW1", "dW2", "aux")
+    snap = lambda: {"out": out.clone(), "dX": dX.clone(), "aux": layer.saved["aux"].clone(),
+                    **{k: v.clone() for k, v in grads.items()}}
+    step()
+    torch.cuda.synchronize()
+    ref = snap()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for t in (out, dX, *grads.values()):   # clobber the outputs eagerly
+            t.fill_(float("nan") if t.is_floating_point() else 0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snap()
+        for k in keys:
+            assert torch.equal(got[k], ref[k]), (r, k)
