@@ -197,7 +197,7 @@ def cpu_baseline(w, seed):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py: this build is one GPU's share of the MoE layer; --gpus {a.gpus} "
+        print(f"bench.py: the library runs one GPU's share of the MoE layer; --gpus {a.gpus} "
               "is not supported (multi-GPU sharding is a design note only).",
               file=sys.stderr)
         return 2
