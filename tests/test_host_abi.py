@@ -275,3 +275,24 @@ def test_one_hip_runtime_in_the_process(repo_root):
                            cwd=repo_root, timeout=300)
         assert r.returncode == 0, r.stderr[-500:]
         assert r.stdout.strip() == "1", (order, r.stdout)
+
+
+def test_plain_c_program_uses_the_c_abi(repo_root, tmp_path):
+    """include/moe.h compiles as C99 and a C program linked against libmoe.so
+    runs the host-side entry points (no GPU, no Python in the program)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    exe = tmp_path / "abi_host"
+    lib_dir = os.path.join(repo_root, "expert_router_gemm_softmax_amd")
+    cmd = [cc, "-std=c99", "-Wall", "-Werror", "-pedantic",
+           "-I", os.path.join(repo_root, "include"),
+           os.path.join(repo_root, "tests", "c_abi", "abi_host.c"),
+           "-L", lib_dir, "-lmoe", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-2000:])
+    assert "all host checks passed" in r.stdout
