@@ -153,10 +153,19 @@ def _check(fn: str, rc: int):
 
 
 def _ptr(t):
+    """Device address of a tensor (None for None or an empty tensor); an int
+    passes through as a raw address.  The kernels read every tensor as a dense
+    row-major buffer in GPU memory, so a host tensor or a strided view is
+    refused here instead of faulting or giving wrong results in a kernel."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if t.device.type != "cuda":
+        raise ValueError(f"tensor on {t.device}: the library reads GPU memory only")
+    if not t.is_contiguous():
+        raise ValueError(f"tensor of strides {tuple(t.stride())}: the library reads "
+                         "dense row-major buffers")
     return t.data_ptr() or None
 
 

@@ -126,8 +126,11 @@ using namespace moe;
 extern "C" {
 
 int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double cf) {
-  if (cf < 0.0 || E <= 0 || T < 0 || k < 0) return MOE_NO_CAPACITY;
+  if (!(cf >= 0.0) || isinf(cf) || E <= 0 || T < 0 || k < 0) return MOE_NO_CAPACITY;
   const double v = cf * (double)T * (double)k / (double)E;
+  // C >= T*k keeps every assignment; saturating there keeps the conversion
+  // below in range for any finite factor
+  if (v >= (double)T * (double)k) return T * (int64_t)k;
   double fl = floor(v);
   if (v - fl <= 1e-9 * (v > 1.0 ? v : 1.0)) return (int64_t)fl;  // integer up to rounding
   return (int64_t)ceil(v);

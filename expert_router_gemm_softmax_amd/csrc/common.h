@@ -182,7 +182,9 @@ constexpr int kAuxTokens = 32;    // tokens per block of the balancing-loss colu
 
 inline int64_t rows_max(const moe_cfg& c) {
   const int64_t tk = c.T * c.k;
-  if (c.capacity < 0) return tk;
+  // no limit, or one that keeps every assignment (this test first also
+  // keeps C * E below 2^44, so the product cannot overflow)
+  if (c.capacity < 0 || c.capacity >= tk) return tk;
   const int64_t ec = c.capacity * (int64_t)c.E;
   return tk < ec ? tk : ec;
 }

@@ -118,6 +118,15 @@ def test_zero_tokens(M):
     assert to_f64(layer.saved["aux"]).tolist() == [0.0, 0.0]
 
 
+def test_binding_refuses_strided_views(M):
+    # refused on the host, before any launch; a contiguous slice passes
+    import torch
+    a = torch.zeros(8, 16, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="dense row-major"):
+        M.binding._ptr(a.t())
+    assert M.binding._ptr(a[2:]) == a.data_ptr() + 2 * 16 * 2
+
+
 BALANCE_CASES = [
     # T, d, E, k, f, dtype, cf, bias, alpha
     (513, 64, 40, 3, 136, "bf16", 0.75, "zipf", 1.0),  # skewed loads, drops

@@ -7,6 +7,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import oracle as O
@@ -66,6 +68,29 @@ def test_capacity_helper_matches_oracle(T, k, E, cf):
 
 def test_capacity_negative_factor_means_no_limit():
     assert M.moe_capacity(100, 2, 4, -1.0) == M.MOE_NO_CAPACITY
+
+
+def test_capacity_of_non_finite_or_huge_factors():
+    # NaN and +inf mean no limit; a factor whose C would pass T*k saturates at
+    # T*k, which drops nothing, exactly like the unsaturated value
+    assert M.moe_capacity(100, 2, 4, float("nan")) == M.MOE_NO_CAPACITY
+    assert M.moe_capacity(100, 2, 4, float("inf")) == M.MOE_NO_CAPACITY
+    assert M.moe_capacity(100, 2, 4, 1e300) == 200
+    assert M.moe_capacity(100, 2, 4, 4.0) == O.capacity(100, 2, 4, 4.0) == 200
+    # the saturated C (T*k = 8) and the unsaturated one (18) both keep all
+    idx = [[0, 1], [0, 2], [0, 1], [3, 0]]
+    for C in (M.moe_capacity(4, 2, 4, 9.0), O.capacity(4, 2, 4, 9.0)):
+        counts, offsets, row_of, _ = O.assign(np.array(idx, dtype=np.int32), 4, C)
+        assert offsets[-1] == 8 and (row_of >= 0).all()
+
+
+def test_rows_max_with_a_huge_capacity_does_not_overflow():
+    c = M.make_cfg(4096, 1024, 256, 8, 4096, "bf16", capacity=2**62)
+    assert M.moe_rows_max(c) == 4096 * 8
+    ws = M.moe_workspace_bytes(c)
+    assert 0 < ws < 2**40
+    c2 = M.make_cfg(4096, 1024, 256, 8, 4096, "bf16", capacity=4096 * 8)
+    assert M.moe_workspace_bytes(c2) == ws
 
 
 def test_rows_max_and_workspace():
@@ -296,3 +321,14 @@ def test_plain_c_program_uses_the_c_abi(repo_root, tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-2000:])
     assert "all host checks passed" in r.stdout
+
+
+def test_binding_refuses_host_tensors():
+    # checked before any library call, so no GPU is needed
+    import torch
+    assert B._ptr(None) is None and B._ptr(1024) == 1024
+    with pytest.raises(ValueError, match="GPU memory only"):
+        B._ptr(torch.zeros(4, 4))
+    c = M.make_cfg(64, 64, 4, 2, 64, "bf16")
+    with pytest.raises(ValueError, match="GPU memory only"):
+        M.moe_combine(c, torch.zeros(128, 64), None, None, None)
