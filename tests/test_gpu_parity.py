@@ -217,18 +217,25 @@ def test_routing_variants_match_oracle(M, case):
         assert_close("out = x", to_f64(res["out"]), O.to_f64(inp["x"]), dt)
 
 
-@pytest.mark.parametrize("mode", ["save", "recompute", "variants"])
+@pytest.mark.parametrize("mode", ["save", "recompute", "variants", "c1"])
 def test_step_entry_points_equal_the_layer_entry_points(M, mode):
     """moe_route .. moe_route_bwd called one by one give bitwise the layer's
     results (same kernels, same order); in the recomputation mode with no A
     and H buffers at all; with every routing variant on (renormalised gates,
     slot priority, identity fallback), whose extra inputs the step entry
-    points then take."""
+    points then take; and at C1's size, many tiles and a split-K tail per
+    GEMM, where the grouped GEMMs' M-tile schedule comes from the permute
+    and the combine backward in the layer but from the schedule kernel in
+    the steps."""
     import torch
     recompute = mode == "recompute"
     var = dict(renorm=True, priority="slot", fallback="identity") if mode == "variants" else {}
-    w, inp = make_case(700, 128, 8, 2, 160, "bf16", 1.0, "normal", seed=7, aux_coeff=0.05,
-                       **var)
+    if mode == "c1":
+        w = W.get("C1")
+        inp = W.make_inputs(w, seed=3)
+    else:
+        w, inp = make_case(700, 128, 8, 2, 160, "bf16", 1.0, "normal", seed=7,
+                           aux_coeff=0.05, **var)
     res = run_layer(M, w, inp, recompute=recompute)
     cfg, d, L = res["_cfg"], res["_dev"], res["_layer"]
     T, E, k = w.T, w.E, w.k
