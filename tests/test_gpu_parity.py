@@ -64,6 +64,27 @@ def test_tiny_workload_named(M):
     assert fw["C"] == 20
 
 
+def test_hand_worked_layer(M):
+    """The HIP path against the hand-worked three-token layer of
+    tests/golden/: expected values derived by hand in closed form, not by
+    the oracle (one drop, two experts, every output checked)."""
+    from golden_fixture import load
+    cfg, inp, exp = load("hand_worked_layer.json")
+    w = W.custom(cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["f"], dtype=cfg["dtype"],
+                 cf=cfg["cf"], name="hand_worked")
+    res = run_layer(M, w, inp)
+    R = int(exp["offsets"][-1])
+    for k in ("idx", "counts", "offsets", "row_of"):
+        np.testing.assert_array_equal(to_int(res[k]), exp[k], err_msg=k)
+    np.testing.assert_array_equal(to_int(res["src_of"])[:R], exp["src_of"], err_msg="src_of")
+    assert_close("probs", to_f64(res["probs"]), exp["probs"], "prob")
+    assert_close("gate", to_f64(res["gate"]), exp["gate"], "prob")
+    for k in ("x_perm", "A", "H", "Y"):
+        assert_close(k, to_f64(res[k])[:R], exp[k], "f32")
+    for k in ("out", "dX", "dWr", "db", "dW1", "dW2"):
+        assert_close(k, to_f64(res[k]), exp[k], "f32")
+
+
 def test_zero_capacity_drops_everything(M):
     w, inp = make_case(100, 64, 4, 2, 64, "bf16", 0.0, seed=3)
     res = run_layer(M, w, inp)
