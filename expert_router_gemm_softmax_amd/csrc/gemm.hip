@@ -864,31 +864,50 @@ int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
       A = rA;
       H = rH;
     }
-    // dA = (dYp W2^T) * gelu'(A): B = W2[e] as [N=f][K=d]
-    g.A = dYp; g.B = W2; g.C = dA; g.Aux = A;
-    g.N = c.f; g.K = c.d; g.lda = c.d; g.ldb = c.d; g.ldc = c.f;
-    g.b_estride = (int64_t)c.f * c.d;
-    rc = run_gemm<MODE_ROW, true, EPI_DGELU>(MOE_KERNEL_GEMM_DH, c, g, s);
-    if (rc != MOE_OK) return rc;
-    // dXp = dA W1^T: B = W1[e] as [N=d][K=f]
-    g.A = dA; g.B = W1; g.C = dXp; g.Aux = nullptr;
-    g.N = c.d; g.K = c.f; g.lda = c.f; g.ldb = c.f; g.ldc = c.d;
-    g.b_estride = (int64_t)c.d * c.f;
-    rc = run_gemm<MODE_ROW, true, EPI_STORE>(MOE_KERNEL_GEMM_DX, c, g, s);
-    if (rc != MOE_OK) return rc;
   }
+  const bool rows = rows_max(c) > 0;
+  // dA = (dYp W2^T) * gelu'(A): B = W2[e] as [N=f][K=d]
+  auto gemm_dh = [&]() {
+    GemmArgs h = g;
+    h.A = dYp; h.B = W2; h.C = dA; h.Aux = A;
+    h.N = c.f; h.K = c.d; h.lda = c.d; h.ldb = c.d; h.ldc = c.f;
+    h.b_estride = (int64_t)c.f * c.d;
+    return run_gemm<MODE_ROW, true, EPI_DGELU>(MOE_KERNEL_GEMM_DH, c, h, s);
+  };
+  // dXp = dA W1^T: B = W1[e] as [N=d][K=f]
+  auto gemm_dx = [&]() {
+    GemmArgs h = g;
+    h.A = dA; h.B = W1; h.C = dXp;
+    h.N = c.d; h.K = c.f; h.lda = c.f; h.ldb = c.f; h.ldc = c.d;
+    h.b_estride = (int64_t)c.d * c.f;
+    return run_gemm<MODE_ROW, true, EPI_STORE>(MOE_KERNEL_GEMM_DX, c, h, s);
+  };
   // dW2[e] = H_e^T dYp_e : M = f, N = d
-  g.part = nullptr;
-  g.A = H; g.B = dYp; g.C = dW2; g.Aux = nullptr;
-  g.M = c.f; g.N = c.d; g.lda = c.f; g.ldb = c.d; g.ldc = c.d;
-  g.c_estride = (int64_t)c.f * c.d;
-  rc = run_gemm<MODE_KRAG, false, EPI_STORE>(MOE_KERNEL_GEMM_DW2, c, g, s);
-  if (rc != MOE_OK) return rc;
+  auto gemm_dw2 = [&]() {
+    GemmArgs h = g;
+    h.part = nullptr;
+    h.A = H; h.B = dYp; h.C = dW2;
+    h.M = c.f; h.N = c.d; h.lda = c.f; h.ldb = c.d; h.ldc = c.d;
+    h.c_estride = (int64_t)c.f * c.d;
+    return run_gemm<MODE_KRAG, false, EPI_STORE>(MOE_KERNEL_GEMM_DW2, c, h, s);
+  };
   // dW1[e] = x_perm_e^T dA_e : M = d, N = f
-  g.A = x_perm; g.B = dA; g.C = dW1;
-  g.M = c.d; g.N = c.f; g.lda = c.d; g.ldb = c.f; g.ldc = c.f;
-  g.c_estride = (int64_t)c.d * c.f;
-  return run_gemm<MODE_KRAG, false, EPI_STORE>(MOE_KERNEL_GEMM_DW1, c, g, s);
+  auto gemm_dw1 = [&]() {
+    GemmArgs h = g;
+    h.part = nullptr;
+    h.A = x_perm; h.B = dA; h.C = dW1;
+    h.M = c.d; h.N = c.f; h.lda = c.d; h.ldb = c.f; h.ldc = c.f;
+    h.c_estride = (int64_t)c.d * c.f;
+    return run_gemm<MODE_KRAG, false, EPI_STORE>(MOE_KERNEL_GEMM_DW1, c, h, s);
+  };
+  // Each GEMM runs right after the one that wrote its largest input, so
+  // that input is still in the memory-side cache: dW2 after the combine
+  // backward (dYp), dW1 after dH (dA), dX after dW1 (dA again).
+  if ((rc = gemm_dw2()) != MOE_OK) return rc;
+  if (rows && (rc = gemm_dh()) != MOE_OK) return rc;
+  if ((rc = gemm_dw1()) != MOE_OK) return rc;
+  if (rows && (rc = gemm_dx()) != MOE_OK) return rc;
+  return MOE_OK;
 }
 
 }  // namespace moe
