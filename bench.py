@@ -28,6 +28,7 @@ METRIC = "MoE layer fwd+bwd tokens/sec on 1 MI355X; % bf16 MFMA peak, % HBM BW"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COLD_FLUSH_BYTES = 512 << 20  # twice the MI355X memory-side cache (256 MB)
 
 # CPU-oracle sample sizes (tokens) that take roughly 10-30 s on ~8-16 cores
 CPU_SAMPLE_T = {"tiny_f32": 64, "c1_bf16": 4096, "c2_zipf": 2048, "c3_epshare": 1024,
@@ -50,6 +51,9 @@ def parse():
                     help="kernel timed for the roofline (default: GEMM_DH, the dA = "
                          "(dYp W2^T) * gelu'(A) GEMM, the longest per launch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache timing (a 512 MiB fill before each of K "
+                         "more steps, median of the per-step times)")
     ap.add_argument("--aux-coeff", type=float, default=0.0,
                     help="coefficient of the load-balancing loss (default 0: the bare "
                          "layer); > 0 also computes the loss and drop rate every step")
@@ -311,6 +315,30 @@ def main():
     log(f"[bench] {a.steps} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms; "
         f"{kernel}: {k_n} launches, {k_ms / max(k_n, 1):.4f} ms avg")
 
+    cold = None
+    if not a.no_cold:
+        # cold caches: before each step, a 512 MiB fill (twice the 256 MB
+        # memory-side cache) evicts the step's data; each step is timed alone
+        # with events on the current stream, the fill outside them
+        flush = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        times = []
+        for i in range(a.steps):
+            flush.fill_(i & 0xFF)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del flush
+        times.sort()
+        med = times[len(times) // 2] if len(times) % 2 else 0.5 * (
+            times[len(times) // 2 - 1] + times[len(times) // 2])
+        cold = {"ms_per_step_median": round(med, 4), "flush_bytes": COLD_FLUSH_BYTES,
+                "steps": a.steps}
+        log(f"[bench] cold caches: median {med:.4f} ms per step over {a.steps} steps")
+
     # algorithmic work of the timed kernel per launch
     flops = {"GEMM_UP": 2.0 * R * w.d * w.f, "GEMM_DOWN": 2.0 * R * w.d * w.f,
              "GEMM_DH": 2.0 * R * w.d * w.f, "GEMM_DX": 2.0 * R * w.d * w.f,
@@ -358,6 +386,8 @@ def main():
         "roofline": roof,
         "gpu_event_ms_per_step": round(gpu_ms / a.steps, 4),
     }
+    if cold is not None:
+        line["cold_cache"] = cold
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(w, a.seed)
