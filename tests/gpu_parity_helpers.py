@@ -58,12 +58,17 @@ def to_dev(a: np.ndarray):
 
 
 def to_f64(t) -> np.ndarray:
-    """device tensor -> float64 numpy (bf16 converted exactly through its bits)."""
+    """device tensor -> float64 numpy (bf16 converted exactly through its bits).
+
+    Buffers sized for Rmax rows hold whatever memory held past the R rows
+    written; signaling-NaN patterns there raise numpy's invalid-cast flag
+    on conversion.  Those rows are never compared, so the flag is ignored."""
     import torch
     t = t.detach()
-    if t.dtype == torch.bfloat16:
-        return O.to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
-    return t.cpu().numpy().astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        if t.dtype == torch.bfloat16:
+            return O.to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+        return t.cpu().numpy().astype(np.float64)
 
 
 def to_int(t) -> np.ndarray:
