@@ -186,18 +186,28 @@ __device__ __forceinline__ bool decode_work(const GemmArgs& g, int* s_tiles, Til
   return true;
 }
 
-// Epilogue of 8 consecutive outputs of one row at element offset o.
-template <int EPI>
+// 16-byte store that no later kernel of the step reads soon: non-temporal,
+// so that it does not push the next kernel's inputs out of the caches
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+// Epilogue of 8 consecutive outputs of one row at element offset o.  NT:
+// the output is stored non-temporally (weight gradients).  The GELU
+// epilogue's pre-activation A (read again only in the backward) and the
+// fp32-add epilogue's output (the router's dX, a final output) always are.
+template <int EPI, bool NT = false>
 __device__ __forceinline__ void epi_write8(const GemmArgs& g, int64_t o, float (&v8)[8]) {
   if constexpr (EPI == EPI_F32) {
     float* C = static_cast<float*>(g.C) + o;
     *reinterpret_cast<f32x4*>(C) = *reinterpret_cast<const f32x4*>(v8);
     *reinterpret_cast<f32x4*>(C + 4) = *reinterpret_cast<const f32x4*>(v8 + 4);
   } else if constexpr (EPI == EPI_STORE) {
-    st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
+    if constexpr (NT) st16_nt(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
+    else st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
   } else if constexpr (EPI == EPI_GELU) {
     const u32x4 ab = St<uint16_t>::pack(v8);
-    if (g.C != nullptr) st16(static_cast<uint16_t*>(g.C) + o, ab);  // NULL: H only
+    if (g.C != nullptr) st16_nt(static_cast<uint16_t*>(g.C) + o, ab);  // NULL: H only
     float a8[8];
     St<uint16_t>::unpack(ab, a8);
 #pragma unroll
@@ -212,7 +222,7 @@ __device__ __forceinline__ void epi_write8(const GemmArgs& g, int64_t o, float (
       v8[q] += a0[q];
       v8[q + 4] += a1[q];
     }
-    st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
+    st16_nt(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
   } else {
     float x8[8];
     St<uint16_t>::unpack(ld16(static_cast<const uint16_t*>(g.Aux) + o), x8);
@@ -517,7 +527,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
         *reinterpret_cast<f32x4*>(q + 4) = *reinterpret_cast<const f32x4*>(v8 + 4);
       } else {
         const int row = t.m0 + tr, col = t.n0 + tc;
-        if (row < t.M && col < g.N) epi_write8<EPI>(g, cbase + (int64_t)row * g.ldc + col, v8);
+        if (row < t.M && col < g.N)
+          epi_write8<EPI, MODE == MODE_KRAG>(g, cbase + (int64_t)row * g.ldc + col, v8);
       }
     }
     __syncthreads();
