@@ -675,6 +675,9 @@ inline bool use_big_tile(const moe_cfg& c, int mode, int M, int N, int E) {
 // M tile of the ROW GEMMs of a layer (the schedule is built for it)
 inline int row_bm(const moe_cfg& c) {
   if (c.dtype != MOE_BF16) return kFM;
+  // fewer than 512 rows per expert on average: 256-row tiles would be
+  // mostly padding for the small experts of a skewed routing
+  if (rows_max(c) < 512 * (int64_t)c.E) return 128;
   const int nmin = c.d < c.f ? c.d : c.f;
   return use_big_tile(c, MODE_ROW, 0, nmin, c.E) ? 256 : 128;
 }
