@@ -673,11 +673,14 @@ inline bool use_big_tile(const moe_cfg& c, int mode, int M, int N, int E) {
   return tiles >= 256;
 }
 // M tile of the ROW GEMMs of a layer (the schedule is built for it)
+// Fewer than 512 rows per expert on average: 256-row tiles would be mostly
+// padding for the small experts of a skewed routing, and the weight
+// gradients' short reductions would leave one block per CU idle through
+// each 256 x 256 epilogue.  The expert GEMMs then keep 128 x 128 tiles.
+inline bool small_experts(const moe_cfg& c) { return rows_max(c) < 512 * (int64_t)c.E; }
 inline int row_bm(const moe_cfg& c) {
   if (c.dtype != MOE_BF16) return kFM;
-  // fewer than 512 rows per expert on average: 256-row tiles would be
-  // mostly padding for the small experts of a skewed routing
-  if (rows_max(c) < 512 * (int64_t)c.E) return 128;
+  if (small_experts(c)) return 128;
   const int nmin = c.d < c.f ? c.d : c.f;
   return use_big_tile(c, MODE_ROW, 0, nmin, c.E) ? 256 : 128;
 }
@@ -717,7 +720,9 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
       if (!g.offsets && g.bn) BN = g.bn;
     }
   } else {
-    BM = BN = use_big_tile(c, MODE_KRAG, g.M, g.N, g.E) ? 256 : 128;
+    // expert weight gradients (per-expert offsets) follow small_experts
+    const bool small = g.offsets != nullptr && small_experts(c);
+    BM = BN = !small && use_big_tile(c, MODE_KRAG, g.M, g.N, g.E) ? 256 : 128;
   }
   g.ntn = (int)ceil_div(g.N, BN);
   int64_t nblk;
