@@ -32,23 +32,62 @@ __device__ __forceinline__ void load_pass(const T* __restrict__ src, int64_t r, 
 // With a fallback row source fb (the identity fallback: x for the combine,
 // dOut for the unpermute-sum) a dropped j adds gate[t,j] * fb[t] in its
 // place.  One wave per token; two assignments' rows are in flight at once.
-template <typename T, typename OutT, bool GATED>
+// RV > 0 (bf16, E = 8 RV experts): the router backward's dX instead,
+// sum_e dz[t,e] Wr[i,e] plus the unpermute-sum, in fp32 starting from the
+// router term (dz = hi + lo of the bf16 pair in dzb [T][2E]; Wr [d][E]),
+// and one rounding to bf16 -- the E products per output run on the VALU,
+// and no fp32 sum goes through HBM.
+template <typename T, typename OutT, bool GATED, int RV = 0>
 __global__ __launch_bounds__(256) void gather_sum_kernel(
     const T* __restrict__ src, const int32_t* __restrict__ row_of,
     const float* __restrict__ gate, const T* __restrict__ fb, OutT* __restrict__ out,
-    int64_t T_, int d, int k) {
+    int64_t T_, int d, int k, const uint16_t* __restrict__ dzb = nullptr,
+    const uint16_t* __restrict__ Wr = nullptr) {
   constexpr int V = St<T>::kVec;
   const int lane = threadIdx.x & 63;
   const int nch = d / V;
   for (int64_t t = (int64_t)blockIdx.x * kCW + (threadIdx.x >> 6); t < T_;
        t += (int64_t)gridDim.x * kCW) {
     const int32_t* rows = row_of + t * k;
+    float dzf[RV > 0 ? 8 * RV : 1];
+    if constexpr (RV > 0) {
+      const uint16_t* dz = dzb + t * (16 * RV);
+#pragma unroll
+      for (int r = 0; r < RV; ++r) {
+        float hi[8], lo[8];
+        St<uint16_t>::unpack(ld16(dz + 8 * r), hi);
+        St<uint16_t>::unpack(ld16(dz + 8 * RV + 8 * r), lo);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dzf[8 * r + e] = hi[e] + lo[e];
+      }
+    }
     for (int g0 = 0; g0 < nch; g0 += kWave * kCPL) {
       float acc[kCPL][V];
 #pragma unroll
       for (int s = 0; s < kCPL; ++s)
 #pragma unroll
         for (int q = 0; q < V; ++q) acc[s][q] = 0.0f;
+      if constexpr (RV > 0) {
+        // the router term first: acc starts at sum_e dz[t,e] Wr[i,e]
+#pragma unroll
+        for (int s = 0; s < kCPL; ++s) {
+          const int c = g0 + s * kWave + lane;
+          if (c >= nch) continue;
+#pragma unroll
+          for (int q = 0; q < V; ++q) {
+            const uint16_t* wr = Wr + (int64_t)(c * V + q) * (8 * RV);
+            float u = 0.0f;
+#pragma unroll
+            for (int r = 0; r < RV; ++r) {
+              float w8[8];
+              St<uint16_t>::unpack(ld16(wr + 8 * r), w8);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) u += dzf[8 * r + e] * w8[e];
+            }
+            acc[s][q] = u;
+          }
+        }
+      }
       for (int j = 0; j < k; j += 2) {
         const int32_t r0 = rows[j];
         const int32_t r1 = j + 1 < k ? rows[j + 1] : -2;  // -2: no assignment
@@ -218,6 +257,28 @@ int launch_unpermute_bwd(const moe_cfg& c, const void* dXp, const int32_t* row_o
                gather_sum_kernel<float, float, false><<<grid, 256, 0, s>>>(
                    static_cast<const float*>(dXp), row_of, gate, static_cast<const float*>(fb),
                    dXe, c.T, c.d, c.k));
+  return MOE_OK;
+}
+
+int launch_unpermute_router_dx(const moe_cfg& c, const void* dXp, const int32_t* row_of,
+                               const float* gate, const void* dOut, const uint16_t* dzb,
+                               const void* Wr, void* dX, hipStream_t s) {
+  if (c.T == 0) return MOE_OK;
+  if (c.dtype != MOE_BF16 || (c.E != 8 && c.E != 16)) return MOE_ERR_UNIMPLEMENTED;
+  const int grid = token_grid(c.T);
+  const uint16_t* fb =
+      (c.flags & MOE_FLAG_DROP_IDENTITY) ? static_cast<const uint16_t*>(dOut) : nullptr;
+  const uint16_t* src = static_cast<const uint16_t*>(dXp);
+  const uint16_t* w = static_cast<const uint16_t*>(Wr);
+  uint16_t* o = static_cast<uint16_t*>(dX);
+  if (c.E == 8)
+    MOE_LAUNCH(MOE_KERNEL_ROUTE_BWD_DX, s,
+               gather_sum_kernel<uint16_t, uint16_t, false, 1><<<grid, 256, 0, s>>>(
+                   src, row_of, gate, fb, o, c.T, c.d, c.k, dzb, w));
+  else
+    MOE_LAUNCH(MOE_KERNEL_ROUTE_BWD_DX, s,
+               gather_sum_kernel<uint16_t, uint16_t, false, 2><<<grid, 256, 0, s>>>(
+                   src, row_of, gate, fb, o, c.T, c.d, c.k, dzb, w));
   return MOE_OK;
 }
 

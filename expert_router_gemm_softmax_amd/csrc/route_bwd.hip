@@ -23,6 +23,13 @@
 #include "gemm.h"
 
 namespace moe {
+
+// combine.hip: the router backward's dX for bf16 storage and E = 8 or 16,
+// the unpermute-sum of dXp plus dz Wr^T in one pass (dzb: the [T][2E] bf16
+// hi/lo pair of dz); MOE_ERR_UNIMPLEMENTED for other shapes
+int launch_unpermute_router_dx(const moe_cfg& c, const void* dXp, const int32_t* row_of,
+                               const float* gate, const void* dOut, const uint16_t* dzb,
+                               const void* Wr, void* dX, hipStream_t s);
 namespace {
 
 // wrp[i][e] = wrp[i][Ep + e] = Wr[i][e] (zero for E <= e < Ep): the router
@@ -204,7 +211,14 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
                    c.k, aux_scale, (c.flags & MOE_FLAG_RENORM) != 0,
                    (c.flags & MOE_FLAG_DROP_IDENTITY) != 0));
   int rc;
-  if (c.T > 0) {
+  if (c.T > 0 && BF && (c.E == 8 || c.E == 16) &&
+      (reinterpret_cast<uintptr_t>(Wr) & 15) == 0) {
+    // few experts: dz Wr^T is E FMAs per output, done on the VALU inside the
+    // unpermute-sum's pass (no fp32 sum through HBM, no GEMM launch); Wr's
+    // rows are read as 16-byte vectors
+    rc = launch_unpermute_router_dx(c, dXp, row_of, gate, dOut, dzb, Wr, dX, s);
+    if (rc != MOE_OK) return rc;
+  } else if (c.T > 0) {
     // dX = [dz_hi | dz_lo] [Wr | Wr]^T + unpermute-sum of dXp (fp32)
     float* dxe = ws_ptr<float>(ws, L.dxe);
     rc = launch_unpermute_bwd(c, dXp, row_of, gate, dOut, dxe, s, MOE_KERNEL_ROUTE_BWD_DX);
@@ -227,6 +241,8 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
     g.bm = g.bn = 128;
     rc = launch_gemm(MOE_KERNEL_ROUTE_BWD_DX, MODE_ROW, true, EPI_ADDF32, c, g, s);
     if (rc != MOE_OK) return rc;
+  }
+  if (c.T > 0) {
     // dWr partials = x^T [dz_hi | dz_lo] over uniform token chunks
     GemmArgs h{};
     h.E = L.dwr_chunks;
