@@ -25,14 +25,17 @@
 
 namespace moe {
 
-constexpr int kGroupM = 4;  // M tiles per traversal group
+// M tiles per traversal group: 4 for 128 x 128 tiles, 2 for 256 x 256
+// (the 32 tiles resident on one XCD then span fewer distinct operand panels)
+template <int BM>
+constexpr int group_m() { return BM >= 256 ? 2 : 4; }
 constexpr int BK_ALL = 32;  // K tile of the bf16 kernels
 
 namespace {
 
 // Block -> output tile.  Block ids are dealt round-robin to the 8 XCDs;
 // give each XCD a contiguous range of logical tiles, then walk that range
-// in groups of kGroupM M-tiles with M fastest (compact 2-D groups).
+// in groups of group_m M-tiles with M fastest (compact 2-D groups).
 __device__ __forceinline__ bool xcd_logical(int ntotal, int& lid) {
   const int per = (ntotal + 7) >> 3;
   const int bid = blockIdx.x;
@@ -41,6 +44,7 @@ __device__ __forceinline__ bool xcd_logical(int ntotal, int& lid) {
   lid = xcd * per + local;
   return lid < ntotal;
 }
+template <int kGroupM>
 __device__ __forceinline__ void group_mn(int lid, int num_m, int ntn, int& mt, int& nt) {
   const int per_group = kGroupM * ntn;
   const int g = lid / per_group;
@@ -83,7 +87,7 @@ __device__ __forceinline__ void tile_of(const GemmArgs& g, const int* s_tiles, i
   t.kofs = 0;
   if constexpr (MODE == MODE_ROW) {
     int mt, nt;
-    group_mn(lid, num_m, g.ntn, mt, nt);
+    group_mn<group_m<BM>()>(lid, num_m, g.ntn, mt, nt);
     if (!g.offsets) {  // one group of g.M rows
       t.e = 0;
       t.row0 = 0;
@@ -106,7 +110,7 @@ __device__ __forceinline__ void tile_of(const GemmArgs& g, const int* s_tiles, i
     const int per_e = g.ntm * g.ntn;
     t.e = lid / per_e;
     int mt, nt;
-    group_mn(lid - t.e * per_e, g.ntm, g.ntn, mt, nt);
+    group_mn<group_m<BM>()>(lid - t.e * per_e, g.ntm, g.ntn, mt, nt);
     if (g.offsets) {
       t.row0 = g.offsets[t.e];
       t.K = g.offsets[t.e + 1] - (int)t.row0;
