@@ -201,7 +201,8 @@ __device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
 // epilogue's pre-activation A (read again only in the backward) and the
 // fp32-add epilogue's output (the router's dX, a final output) always are.
 template <int EPI, bool NT = false>
-__device__ __forceinline__ void epi_write8(const GemmArgs& g, int64_t o, float (&v8)[8]) {
+__device__ __forceinline__ void epi_write8(const GemmArgs& g, int64_t o, float (&v8)[8],
+                                           const u32x4* pre = nullptr) {
   if constexpr (EPI == EPI_F32) {
     float* C = static_cast<float*>(g.C) + o;
     *reinterpret_cast<f32x4*>(C) = *reinterpret_cast<const f32x4*>(v8);
@@ -229,7 +230,8 @@ __device__ __forceinline__ void epi_write8(const GemmArgs& g, int64_t o, float (
     st16_nt(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
   } else {
     float x8[8];
-    St<uint16_t>::unpack(ld16(static_cast<const uint16_t*>(g.Aux) + o), x8);
+    // pre: the same 16 bytes, loaded ahead by the caller
+    St<uint16_t>::unpack(pre ? *pre : ld16(static_cast<const uint16_t*>(g.Aux) + o), x8);
 #pragma unroll
     for (int q = 0; q < 8; ++q) v8[q] *= gelu_tanh_grad(x8[q]);
     st16(static_cast<uint16_t*>(g.C) + o, St<uint16_t>::pack(v8));
@@ -512,6 +514,23 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   float* ptile = part >= 0 ? g.part + (int64_t)pid * BM * BN : nullptr;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    // GELU backward: every pass's pre-activation of this row block is loaded
+    // before the staging, so the loads are in flight together instead of one
+    // after each pass's stores
+    u32x4 pa[EPI == EPI_DGELU ? 32 / RPP : 1];
+    if constexpr (EPI == EPI_DGELU) {
+      if (ptile == nullptr) {
+#pragma unroll
+        for (int p = 0; p < 32 / RPP; ++p) {
+          const int row = t.m0 + wm * WM + i * 32 + p * RPP + lane / LPR;
+          const int col = t.n0 + wn * WN + (lane % LPR) * 8;
+          pa[p] = row < t.M && col < g.N
+                      ? ld16(static_cast<const uint16_t*>(g.Aux) + cbase +
+                             (int64_t)row * g.ldc + col)
+                      : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -532,7 +551,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
       } else {
         const int row = t.m0 + tr, col = t.n0 + tc;
         if (row < t.M && col < g.N)
-          epi_write8<EPI, MODE == MODE_KRAG>(g, cbase + (int64_t)row * g.ldc + col, v8);
+          epi_write8<EPI, MODE == MODE_KRAG>(g, cbase + (int64_t)row * g.ldc + col, v8,
+                                             EPI == EPI_DGELU ? &pa[p] : nullptr);
       }
     }
     __syncthreads();
