@@ -219,9 +219,11 @@ __device__ __forceinline__ void epi_write8(const GemmArgs& g, int64_t o, float (
     for (int q = 0; q < 8; ++q) a8[q] = gelu_tanh(a8[q]);
     st16(static_cast<uint16_t*>(g.C2) + o, St<uint16_t>::pack(a8));
   } else if constexpr (EPI == EPI_ADDF32) {
+    // pre: the 32 bytes of the addend, loaded ahead by the caller
     const float* ad = static_cast<const float*>(g.Aux) + o;
-    const f32x4 a0 = *reinterpret_cast<const f32x4*>(ad);
-    const f32x4 a1 = *reinterpret_cast<const f32x4*>(ad + 4);
+    const f32x4 a0 = pre ? __builtin_bit_cast(f32x4, pre[0]) : *reinterpret_cast<const f32x4*>(ad);
+    const f32x4 a1 =
+        pre ? __builtin_bit_cast(f32x4, pre[1]) : *reinterpret_cast<const f32x4*>(ad + 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       v8[q] += a0[q];
@@ -514,20 +516,29 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   float* ptile = part >= 0 ? g.part + (int64_t)pid * BM * BN : nullptr;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    // GELU backward: every pass's pre-activation of this row block is loaded
-    // before the staging, so the loads are in flight together instead of one
-    // after each pass's stores
-    u32x4 pa[EPI == EPI_DGELU ? 32 / RPP : 1];
-    if constexpr (EPI == EPI_DGELU) {
+    // GELU backward and fp32 add: every pass's auxiliary input of this row
+    // block (the bf16 pre-activation, 16 bytes; the fp32 addend, 32 bytes) is
+    // loaded before the staging, so the loads are in flight together instead
+    // of one after each pass's stores
+    constexpr bool kPre = EPI == EPI_DGELU || EPI == EPI_ADDF32;
+    constexpr int kPreV = EPI == EPI_ADDF32 ? 2 : 1;  // 16-byte vectors per pass
+    u32x4 pa[kPre ? 32 / RPP : 1][kPreV];
+    if constexpr (kPre) {
       if (ptile == nullptr) {
 #pragma unroll
         for (int p = 0; p < 32 / RPP; ++p) {
           const int row = t.m0 + wm * WM + i * 32 + p * RPP + lane / LPR;
           const int col = t.n0 + wn * WN + (lane % LPR) * 8;
-          pa[p] = row < t.M && col < g.N
-                      ? ld16(static_cast<const uint16_t*>(g.Aux) + cbase +
-                             (int64_t)row * g.ldc + col)
-                      : u32x4{0, 0, 0, 0};
+          const bool ok = row < t.M && col < g.N;
+          const int64_t o = cbase + (int64_t)row * g.ldc + col;
+#pragma unroll
+          for (int u = 0; u < kPreV; ++u) {
+            if constexpr (EPI == EPI_DGELU)
+              pa[p][u] = ok ? ld16(static_cast<const uint16_t*>(g.Aux) + o) : u32x4{0, 0, 0, 0};
+            else
+              pa[p][u] = ok ? ld16(static_cast<const float*>(g.Aux) + o + 4 * u)
+                            : u32x4{0, 0, 0, 0};
+          }
         }
       }
     }
@@ -552,7 +563,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
         const int row = t.m0 + tr, col = t.n0 + tc;
         if (row < t.M && col < g.N)
           epi_write8<EPI, MODE == MODE_KRAG>(g, cbase + (int64_t)row * g.ldc + col, v8,
-                                             EPI == EPI_DGELU ? &pa[p] : nullptr);
+                                             kPre ? pa[p] : nullptr);
       }
     }
     __syncthreads();
