@@ -348,7 +348,8 @@ def main():
     Tk = w.T * w.k
     hbm_bytes = {"COMBINE": R * w.d * s_b + w.T * w.d * s_b + 8 * Tk,
                  "COMBINE_BWD": w.T * w.d * s_b + 2 * R * w.d * s_b + 12 * Tk,
-                 "PERMUTE_COPY": 2 * R * w.d * s_b,
+                 # every token's row read once, each kept copy written
+                 "PERMUTE_COPY": (w.T + R) * w.d * s_b + 4 * Tk,
                  "ROUTE_AUX": 4 * w.T * w.E + 8 * w.E + 4}
     avg_s = (k_ms / 1e3) / max(k_n, 1)
     if kernel in hbm_bytes and avg_s > 0:
