@@ -591,6 +591,8 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
     if (row >= t.M || col >= g.N) continue;
     float v8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const float* q = g.part + ((int64_t)i * sp.sp) * BM * BN + tr * BN + tc;
+    // in part order; unrolled so that several parts' loads are in flight
+#pragma unroll 4
     for (int p = 0; p < sp.sp; ++p, q += BM * BN) {
       const f32x4 a = *reinterpret_cast<const f32x4*>(q);
       const f32x4 b = *reinterpret_cast<const f32x4*>(q + 4);
