@@ -96,6 +96,36 @@ def test_zero_capacity_drops_everything(M):
     assert np.all(to_f64(res["dW1"]) == 0) and np.all(to_f64(res["dWr"]) == 0)
 
 
+def test_router_weights_only_4_byte_aligned(M):
+    """With 8 experts (bf16) the router backward computes dz Wr^T inside the
+    unpermute-sum's pass, reading Wr rows as 16-byte vectors, and takes that
+    pass only for a 16-byte-aligned Wr.  A Wr the ABI allows but that is only
+    4-byte aligned takes the GEMM path instead; both layers match the
+    oracle, and their dX agree within the bf16 tolerance."""
+    import copy
+
+    import torch
+    w, inp = make_case(300, 64, 8, 2, 96, "bf16", 1.0, "normal", seed=11)
+    res = run_layer(M, w, inp)
+    d = res["_dev"]
+    Wr = d["Wr"]
+    buf = torch.zeros(Wr.numel() + 2, dtype=Wr.dtype, device="cuda")
+    buf[2:].copy_(Wr.reshape(-1))
+    Wr_u = buf[2:].view(Wr.shape)
+    assert Wr_u.data_ptr() % 16 == 4 and torch.equal(Wr_u, Wr)
+    layer = M.MoeLayer(copy.copy(res["_cfg"]), Wr_u, d["b"], d["W1"], d["W2"])
+    out = layer.forward(d["x"])
+    dX, g = layer.backward(d["x"], d["dOut"])
+    torch.cuda.synchronize()
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    check_layer_full(res, fw, bw, w)
+    res_u = dict(out=out, dX=dX, **layer.saved, **g)
+    check_layer_full(res_u, fw, bw, w)
+    assert torch.equal(out, res["out"])  # forward: same kernels
+    assert_close("dX aligned vs unaligned Wr", to_f64(dX), to_f64(res["dX"]), "bf16")
+
+
 def test_one_hot_expert_overflows_capacity(M):
     # a large bias sends every token's first choice to expert 2
     w, inp = make_case(600, 64, 8, 2, 64, "bf16", 1.0, seed=4)
