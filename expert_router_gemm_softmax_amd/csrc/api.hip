@@ -5,6 +5,7 @@
 #include <float.h>
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -127,13 +128,47 @@ extern "C" {
 
 int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double cf) {
   if (!(cf >= 0.0) || isinf(cf) || E <= 0 || T < 0 || k < 0) return MOE_NO_CAPACITY;
-  const double v = cf * (double)T * (double)k / (double)E;
-  // C >= T*k keeps every assignment; saturating there keeps the conversion
-  // below in range for any finite factor
-  if (v >= (double)T * (double)k) return T * (int64_t)k;
-  double fl = floor(v);
-  if (v - fl <= 1e-9 * (v > 1.0 ? v : 1.0)) return (int64_t)fl;  // integer up to rounding
-  return (int64_t)ceil(v);
+  if (k > 0 && T > INT64_MAX / k) return MOE_NO_CAPACITY;  // T*k not representable
+  const int64_t tk = T * (int64_t)k;
+  if (tk == 0 || cf == 0.0) return 0;
+  // C >= T*k keeps every assignment: saturate there (cf >= E suffices)
+  if (cf >= (double)E) return tk;
+  // The factor is read as its shortest decimal that converts back to the
+  // same double (what a user typed, e.g. 1.1 rather than the binary value
+  // just above it): digits M and exponent q with cf = M * 10^q.
+  char buf[40];
+  int p = 1;
+  for (; p <= 17; ++p) {
+    snprintf(buf, sizeof buf, "%.*e", p - 1, cf);
+    if (strtod(buf, nullptr) == cf) break;
+  }
+  if (p > 17) p = 17;
+  snprintf(buf, sizeof buf, "%.*e", p - 1, cf);
+  // buf = "D.DDDDe[+-]X": mantissa digits, then the decimal exponent
+  unsigned __int128 M = 0;
+  int nd = 0;
+  const char* c = buf;
+  for (; *c && *c != 'e'; ++c)
+    if (*c >= '0' && *c <= '9') {
+      M = M * 10 + (unsigned)(*c - '0');
+      ++nd;
+    }
+  const int q = atoi(c + 1) - (nd - 1);
+  // C = ceil(M * 10^q * T * k / E) in exact integer arithmetic: M < 2^57
+  // and T k < 2^63, so M T k < 2^120; for q > 0, M 10^q = cf < E < 2^31.
+  unsigned __int128 num = M * (unsigned __int128)tk;
+  unsigned __int128 den = (unsigned __int128)E;
+  if (q >= 0) {
+    for (int i = 0; i < q; ++i) num *= 10;
+  } else {
+    for (int i = 0; i < -q; ++i) {
+      // den past 2^120 exceeds num: 0 < value < 1, so C = 1
+      if (den > ((unsigned __int128)1 << 120)) return 1;
+      den *= 10;
+    }
+  }
+  const unsigned __int128 C = (num + den - 1) / den;
+  return C >= (unsigned __int128)tk ? tk : (int64_t)C;
 }
 
 int64_t moe_rows_max(const moe_cfg* cfg) {

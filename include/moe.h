@@ -121,11 +121,12 @@ typedef struct moe_cfg {
                          gradient. */
 } moe_cfg;
 
-/* Capacity of the capacity-factor rule: C = ceil(cf * T * k / E).  A value
- * of cf*T*k/E within 1e-9 (relative) above an integer counts as that
- * integer, so decimal factors such as 1.1 are not pushed up by binary
- * rounding.  cf < 0, NaN or +infinity returns MOE_NO_CAPACITY (no limit).
- * A C above T*k is returned as T*k: like any C >= T, it keeps every
+/* Capacity of the capacity-factor rule: C = ceil(cf * T * k / E), exact.
+ * cf is read as its shortest decimal that converts back to the same double
+ * (so 1.1 means 11/10, not the binary value just above it) and the ceiling
+ * is taken in integer arithmetic.  cf < 0, NaN or +infinity returns
+ * MOE_NO_CAPACITY (no limit), as does a T*k that does not fit int64.  A C
+ * above T*k is returned as T*k: like any C >= T, it keeps every
  * assignment.
  * Distributed-training tutorial, section "The Capacity Factor". */
 MOE_API int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double cf);

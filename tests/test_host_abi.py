@@ -66,6 +66,33 @@ def test_capacity_helper_matches_oracle(T, k, E, cf):
     assert M.moe_capacity(T, k, E, cf) == O.capacity(T, k, E, cf)
 
 
+def test_capacity_helper_is_exact_at_large_sizes_and_decimal_boundaries():
+    """The factor is read as its shortest round-trip decimal, like the
+    oracle's Fraction(str(cf)), and the ceiling is taken exactly: no slack
+    that grows with T*k/E, and no binary rounding of decimals such as 0.1."""
+    cases = [(2 ** 30, 1, 3, 1.0), (1000, 1, 2, 1.0000000005), (1000, 1, 2, 1.0000000000000002),
+             (10, 1, 1, 0.1), (30, 1, 1, 0.1), (3, 1, 10, 0.1), (7, 3, 21, 1.0),
+             (2 ** 31 - 1, 1, 256, 1.1), (2 ** 31 - 1, 1, 255, 0.9999999999999999),
+             (1, 1, 1, 1e-300), (5, 1, 1, 5e-324), (10 ** 6, 32, 7, 2.3333333333333335),
+             (4096, 2, 8, 1.25), (32768, 8, 128, 1.0), (2 ** 40, 1, 1000, 0.001)]
+    rng = np.random.default_rng(0)
+    for _ in range(400):
+        digits = int(rng.integers(1, 8))
+        cf = float(f"{rng.integers(1, 10 ** digits)}e{-int(rng.integers(0, digits + 2))}")
+        cases.append((int(rng.integers(1, 1 << 22)), int(rng.integers(1, 33)),
+                      int(rng.integers(1, 257)), cf))
+        # T k / E an exact multiple of 1 / cf's decimal: the value is an integer
+        E = int(rng.integers(1, 257))
+        cases.append((E * 10 ** 3, 1, E, float(f"{rng.integers(1, 999)}e-3")))
+    for T, k, E, cf in cases:
+        want = O.capacity(T, k, E, cf)
+        want = min(want, T * k)   # the helper saturates at T*k (drops nothing either way)
+        assert M.moe_capacity(T, k, E, cf) == want, (T, k, E, cf)
+    assert M.moe_capacity(2 ** 30, 1, 3, 1.0) == 357913942
+    assert M.moe_capacity(1000, 1, 2, 1.0000000005) == 501
+    assert M.moe_capacity(2 ** 62, 4, 1, 0.5) == M.MOE_NO_CAPACITY  # T*k overflows int64
+
+
 def test_capacity_negative_factor_means_no_limit():
     assert M.moe_capacity(100, 2, 4, -1.0) == M.MOE_NO_CAPACITY
 
