@@ -1,13 +1,16 @@
 """Benchmark of one GPU's share of the MoE layer, forward + backward.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C4]
 
 A step is one forward + backward of the whole layer (router, permute,
 grouped FFN, combine and their backward) over one batch of seeded synthetic
-input already resident in HBM.  Prints ONE JSON line with tokens/s, the
-roofline position of the dominant kernel (timed with HIP events on its own
-stream inside the timed region) and the CPU oracle timed on a bounded
-sample of the same workload.
+input already resident in HBM.  The default workload is the largest one
+(c4_large: T=32768, d=4096, E=128, top-8, f=1536).  Prints ONE JSON line
+with tokens/s -- the primary value with cold caches (a 512 MiB fill before
+each timed step, outside its timing), the back-to-back warm rate beside it
+-- the roofline position of the dominant kernel (its launches timed with
+HIP events on the stream they run on, inside the timed region) and the CPU
+oracle timed on a bounded sample of the same workload.
 
 This build runs on one GPU: --gpus above 1 exits with a message.
 """
@@ -30,7 +33,9 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 COLD_FLUSH_BYTES = 512 << 20  # twice the MI355X memory-side cache (256 MB)
 
-# CPU-oracle sample sizes (tokens) that take roughly 10-30 s on ~8-16 cores
+# CPU-oracle sample sizes (tokens).  Most take 10-30 s on 8-16 cores; the
+# c4_large oracle is bound by its 128 experts' weights (about 1 min on 8
+# cores whatever the token count), so it gets a small token sample.
 CPU_SAMPLE_T = {"tiny_f32": 64, "c1_bf16": 4096, "c2_zipf": 2048, "c3_epshare": 1024,
                 "c4_large": 256}
 
@@ -44,16 +49,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="C1",
-                    help="workload: C0..C4 or its name (default C1)")
+    ap.add_argument("--config", default="C4",
+                    help="workload: C0..C4 or its name (default C4, the largest)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kernel", default=None,
-                    help="kernel timed for the roofline (default: GEMM_DH, the dA = "
-                         "(dYp W2^T) * gelu'(A) GEMM, the longest per launch)")
+                    help="kernel timed for the roofline (default: GEMM_DOWN, Y = H W2, "
+                         "the longest single launch on c4_large)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
-                    help="skip the cold-cache timing (a 512 MiB fill before each of K "
-                         "more steps, median of the per-step times)")
+                    help="time warm back-to-back steps only (the primary value is then the "
+                         "warm rate)")
     ap.add_argument("--aux-coeff", type=float, default=0.0,
                     help="coefficient of the load-balancing loss (default 0: the bare "
                          "layer); > 0 also computes the loss and drop rate every step")
@@ -168,17 +173,20 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def cpu_baseline(w, seed):
-    """The oracle, as it stands, on the first T' tokens of the workload."""
-    import numpy as np
+def cpu_baseline(w, seed, inp_full=None):
+    """The oracle, as it stands, on the first T' tokens of the workload: the
+    same weights and the first T' rows of x and dOut of the inputs the GPU
+    ran (an expert-share workload draws its ragged batch for T' rows)."""
     import oracle as O
     import workloads as W
     Ts = min(w.T, CPU_SAMPLE_T.get(w.name, 1024))
     ws = w.replace(T=Ts)
-    inp = W.make_inputs(ws, seed=seed)
-    if w.kind == "ep_share":
-        # the generator draws the ragged batch for T' rows
-        pass
+    if w.kind == "layer" and inp_full is not None:
+        inp = dict(inp_full)
+        inp["x"] = inp_full["x"][:Ts]
+        inp["dOut"] = inp_full["dOut"][:Ts]
+    else:
+        inp = W.make_inputs(ws, seed=seed)
     threads = None
     try:
         import threadpoolctl
@@ -191,10 +199,11 @@ def cpu_baseline(w, seed):
     O.layer_bwd(inp, ws, fw)
     dt = time.perf_counter() - t0
     unit = "rows/s" if w.kind == "ep_share" else "tokens/s"
+    cap = "" if ws.cf is None else f", capacity C'={O.capacity(Ts, w.k, w.E, w.cf)} from cf={w.cf}"
     return {"value": Ts / dt, "unit": unit, "cores": threads or os.cpu_count(),
             "kind": "oracle",
-            "sample": f"oracle fwd+bwd of the same layer shape on the first {Ts} of "
-                      f"{w.T} tokens (seed {seed}), one run, {dt:.1f} s; host has "
+            "sample": f"oracle fwd+bwd of the same layer (same weights) on the first {Ts} of "
+                      f"{w.T} tokens (seed {seed}{cap}), one run, {dt:.1f} s; host has "
                       f"{os.cpu_count()} logical CPUs"}
 
 
@@ -289,57 +298,53 @@ def main():
         torch.cuda.synchronize()
         run = graph.replay
 
-    kernel = a.kernel or "GEMM_DH"
-    M.moe_prof_arm(kernel, 0 if a.graph else a.steps)
+    # warm: K steps back to back
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev0.record()
     for i in range(a.steps):
         run()
-    ev1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    k_ms, k_n = M.moe_prof_read()
+    warm_wall = time.perf_counter() - t0
+    log(f"[bench] warm: {a.steps} steps back to back, {warm_wall * 1e3 / a.steps:.4f} ms/step")
+
+    # The timed region of the primary value: K steps, each with cold caches
+    # (a 512 MiB fill, twice the 256 MB memory-side cache, evicts the step's
+    # data first) and bracketed by its own synchronisations; the fill is
+    # outside the timing.  The probe records the roofline kernel's launches
+    # inside these steps, on the stream they run on.  (Graph replays record
+    # no probe events: the kernel is then timed on as many eager steps.)
+    kernel = a.kernel or "GEMM_DOWN"
+    probe = M.KernelProbe(kernel, a.steps)
+    if not a.graph:
+        probe.attach(cfg)
+    flush = None if a.no_cold else torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8,
+                                               device="cuda")
+    step_s = []
+    for i in range(a.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run()
+        torch.cuda.synchronize()
+        step_s.append(time.perf_counter() - t0)
+    wall = sum(step_s)
     if a.graph:
-        # graph replays record no kernel events: time the roofline kernel on
-        # eager steps after the timed region
-        M.moe_prof_arm(kernel, a.steps)
+        probe.attach(cfg)
         for i in range(a.steps):
             step()
         torch.cuda.synchronize()
-        k_ms, k_n = M.moe_prof_read()
+    probe.detach(cfg)
+    k_ms, k_n, k_each = probe.read()
+    probe.close()
+    del flush
     ms_per_step = wall * 1e3 / a.steps
-    log(f"[bench] {a.steps} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms; "
-        f"{kernel}: {k_n} launches, {k_ms / max(k_n, 1):.4f} ms avg")
+    log(f"[bench] {'cold' if not a.no_cold else 'warm'}: {a.steps} steps, "
+        f"{ms_per_step:.4f} ms/step; {kernel}: {k_n} launches, "
+        f"{k_ms / max(k_n, 1):.4f} ms avg")
 
-    cold = None
-    if not a.no_cold:
-        # cold caches: before each step, a 512 MiB fill (twice the 256 MB
-        # memory-side cache) evicts the step's data; each step is timed alone
-        # with events on the current stream, the fill outside them
-        flush = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device="cuda")
-        times = []
-        for i in range(a.steps):
-            flush.fill_(i & 0xFF)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            run()
-            e1.record()
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        del flush
-        times.sort()
-        med = times[len(times) // 2] if len(times) % 2 else 0.5 * (
-            times[len(times) // 2 - 1] + times[len(times) // 2])
-        cold = {"ms_per_step_median": round(med, 4), "flush_bytes": COLD_FLUSH_BYTES,
-                "steps": a.steps}
-        log(f"[bench] cold caches: median {med:.4f} ms per step over {a.steps} steps")
-
-    # algorithmic work of the timed kernel per launch
+    # algorithmic work of the timed kernel per launch: 2 R d f flop per expert
+    # GEMM; bytes the method must move for the gathers
     flops = {"GEMM_UP": 2.0 * R * w.d * w.f, "GEMM_DOWN": 2.0 * R * w.d * w.f,
              "GEMM_DH": 2.0 * R * w.d * w.f, "GEMM_DX": 2.0 * R * w.d * w.f,
              "GEMM_DW1": 2.0 * R * w.d * w.f, "GEMM_DW2": 2.0 * R * w.d * w.f,
@@ -356,14 +361,16 @@ def main():
         achieved = hbm_bytes[kernel] / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": kernel, "avg_ms": round(avg_s * 1e3, 5)}
+                "kernel": kernel, "avg_ms": round(avg_s * 1e3, 5),
+                "algorithmic_bytes": hbm_bytes[kernel]}
     elif kernel in flops:
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
         achieved = flops[kernel] / avg_s / 1e12 if avg_s > 0 else 0.0
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": recorded_traffic(kernel, w.name),
-                "kernel": kernel, "avg_ms": round(avg_s * 1e3, 5)}
+                "kernel": kernel, "avg_ms": round(avg_s * 1e3, 5),
+                "algorithmic_flop": flops[kernel]}
     else:
         roof = {"bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": None, "traffic": None, "kernel": kernel,
@@ -381,17 +388,19 @@ def main():
                                f"cf={w.cf} bias={w.bias}",
                    "tokens": w.T, "d": w.d, "experts": w.E, "top_k": w.k, "ffn": w.f,
                    "capacity": cap, "kept_rows": R, "parallelism": "single GPU",
+                   "caches": "warm" if a.no_cold else
+                             "cold (512 MiB fill before each timed step, outside its timing)",
                    "aux_coeff": a.aux_coeff, "recompute": a.recompute,
                    "renorm": a.renorm, "priority": a.priority, "fallback": a.fallback,
                    "graph_replay": a.graph},
         "roofline": roof,
-        "gpu_event_ms_per_step": round(gpu_ms / a.steps, 4),
+        "warm": {"value": round(w.T * a.steps / warm_wall, 1),
+                 "ms_per_step": round(warm_wall * 1e3 / a.steps, 4),
+                 "note": "the same K steps back to back, one synchronisation each side"},
     }
-    if cold is not None:
-        line["cold_cache"] = cold
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline(w, a.seed)
+        line["cpu_baseline"] = cpu_baseline(w, a.seed, inp)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -37,7 +37,7 @@ KERNELS = dict(ROUTE=0, PERMUTE_COUNT=1, PERMUTE_SCAN=2, PERMUTE_SCATTER=3,
                GEMM_DX=9, GEMM_DW2=10, GEMM_DW1=11, UNPERMUTE_BWD=12,
                ROUTE_BWD_DZ=13, ROUTE_BWD_DX=14, ROUTE_BWD_DW=15, SCHEDULE=16,
                ROUTE_PREP=17, PERMUTE_COPY=18, ROUTE_LOGITS=19, ROUTE_AUX=20,
-               GEMM_RECOMPUTE=21)
+               GEMM_RECOMPUTE=21, GEMM_FIXUP=22)
 
 
 class MoeLibraryError(ImportError):
@@ -51,10 +51,16 @@ class MoeError(RuntimeError):
         self.status = status
 
 
+class MoeProbe(ctypes.Structure):
+    _fields_ = [("kernel_id", c_int32), ("capacity", c_int32), ("count", c_int32),
+                ("reserved_", c_int32), ("begin", POINTER(c_void_p)), ("end", POINTER(c_void_p))]
+
+
 class MoeCfg(ctypes.Structure):
     _fields_ = [("T", c_int64), ("d", c_int32), ("E", c_int32), ("k", c_int32),
                 ("f", c_int32), ("dtype", c_int32), ("capacity", c_int64),
-                ("route_margin", c_float), ("flags", c_uint32), ("aux_coeff", c_float)]
+                ("route_margin", c_float), ("flags", c_uint32), ("aux_coeff", c_float),
+                ("probe", c_void_p)]
 
     def __repr__(self):
         return (f"MoeCfg(T={self.T}, d={self.d}, E={self.E}, k={self.k}, f={self.f}, "
@@ -92,13 +98,11 @@ _SIGS = {
     "moe_grouped_ffn_bwd": (c_int, [_CFG] + [_P] * 11 + [c_size_t, _P]),
     "moe_unpermute_bwd": (c_int, [_CFG, _P, _P, _P, _P, _P, _P]),
     "moe_router_aux": (c_int, [_CFG, _P, _P, _P, _P, _P, c_size_t, _P]),
-    "moe_route_bwd": (c_int, [_CFG] + [_P] * 14 + [c_size_t, _P]),
+    "moe_route_bwd": (c_int, [_CFG] + [_P] * 12 + [c_size_t, _P]),
     "moe_layer_fwd": (c_int, [_CFG, POINTER(MoeWeights), _P, _P, POINTER(MoeCtx), _P,
                               c_size_t, _P]),
     "moe_layer_bwd": (c_int, [_CFG, POINTER(MoeWeights), _P, _P, POINTER(MoeCtx), _P,
                               POINTER(MoeGrads), _P, c_size_t, _P]),
-    "moe_prof_arm": (c_int, [c_int, c_int]),
-    "moe_prof_read": (c_int, [POINTER(c_float), POINTER(c_int)]),
 }
 
 
@@ -275,14 +279,14 @@ def moe_router_aux(cfg, probs, counts, offsets, aux, ws, stream=None):
         _nbytes(ws), _stream(stream)))
 
 
-def moe_route_bwd(cfg, x, Wr, probs, idx, row_of, counts, dgate, dXp, dX, dWr, db, ws,
-                  gate=None, dOut=None, stream=None):
-    """counts may be None when cfg.aux_coeff is 0; gate and dOut are only
-    read under the identity fallback."""
+def moe_route_bwd(cfg, x, Wr, probs, idx, row_of, counts, dgate, dXe, dX, dWr, db, ws,
+                  stream=None):
+    """dXe: the fp32 unpermute-sum written by moe_unpermute_bwd; counts may be
+    None when cfg.aux_coeff is 0."""
     _check("moe_route_bwd", lib.moe_route_bwd(
         byref(cfg), _ptr(x), _ptr(Wr), _ptr(probs), _ptr(idx), _ptr(row_of), _ptr(counts),
-        _ptr(gate), _ptr(dOut), _ptr(dgate), _ptr(dXp), _ptr(dX), _ptr(dWr), _ptr(db),
-        _ptr(ws), _nbytes(ws), _stream(stream)))
+        _ptr(dgate), _ptr(dXe), _ptr(dX), _ptr(dWr), _ptr(db), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
 
 
 def moe_layer_fwd(cfg, weights: MoeWeights, x, out, ctx: MoeCtx, ws, stream=None):
@@ -298,12 +302,61 @@ def moe_layer_bwd(cfg, weights: MoeWeights, x, dOut, ctx: MoeCtx, dX, grads: Moe
         byref(grads), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def moe_prof_arm(kernel, max_launches):
-    kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
-    _check("moe_prof_arm", lib.moe_prof_arm(kid, int(max_launches)))
+class KernelProbe:
+    """Kernel timing through moe_cfg.probe: HIP events created here with the
+    process's HIP runtime (torch's), recorded by the library around the
+    launches of one kernel made with a cfg that carries the probe, and read
+    here after the caller has synchronised.  All state is this object's."""
 
+    def __init__(self, kernel, capacity: int):
+        self._hip = ctypes.CDLL(_hip_runtimes()[0])
+        self._hip.hipEventCreate.argtypes = [POINTER(c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [POINTER(c_float), c_void_p, c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [c_void_p]
+        self._hip.hipEventDestroy.argtypes = [c_void_p]
+        n = max(int(capacity), 0)
+        self._begin = (c_void_p * max(n, 1))()
+        self._end = (c_void_p * max(n, 1))()
+        for arr in (self._begin, self._end):
+            for i in range(n):
+                ev = c_void_p()
+                if self._hip.hipEventCreate(byref(ev)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = ev
+        self._n = n
+        kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+        self.struct = MoeProbe(kernel_id=kid, capacity=n, count=0, reserved_=0,
+                               begin=ctypes.cast(self._begin, POINTER(c_void_p)),
+                               end=ctypes.cast(self._end, POINTER(c_void_p)))
 
-def moe_prof_read():
-    ms, n = c_float(0.0), c_int(0)
-    _check("moe_prof_read", lib.moe_prof_read(byref(ms), byref(n)))
-    return float(ms.value), int(n.value)
+    def attach(self, cfg: MoeCfg) -> MoeCfg:
+        cfg.probe = ctypes.addressof(self.struct)
+        return cfg
+
+    @staticmethod
+    def detach(cfg: MoeCfg) -> MoeCfg:
+        cfg.probe = None
+        return cfg
+
+    def reset(self):
+        self.struct.count = 0
+
+    def read(self):
+        """(summed ms, launches, per-launch ms) of the recorded launches."""
+        times = []
+        for i in range(self.struct.count):
+            if self._hip.hipEventSynchronize(self._end[i]) != 0:
+                raise RuntimeError("hipEventSynchronize failed")
+            ms = c_float(0.0)
+            if self._hip.hipEventElapsedTime(byref(ms), self._begin[i], self._end[i]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            times.append(float(ms.value))
+        return sum(times), len(times), times
+
+    def close(self):
+        for arr in (self._begin, self._end):
+            for i in range(self._n):
+                if arr[i]:
+                    self._hip.hipEventDestroy(arr[i])
+                    arr[i] = None
+        self._n = 0

@@ -1,6 +1,5 @@
-// C-ABI of the MoE layer library: argument validation, workspace layout,
-// the step sequence of the layer forward and backward, and opt-in kernel
-// timing.  Every entry point validates everything before it enqueues
+// C-ABI of the MoE layer library: argument validation, workspace layout and
+// the step sequence of the layer forward and backward.  Every entry point validates everything before it enqueues
 // anything; on an error nothing is enqueued and nothing is written.
 #include <float.h>
 #include <math.h>
@@ -8,33 +7,9 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <vector>
-
 #include "common.h"
 
 namespace moe {
-
-// ------------------------------------------------------------------ timing hook
-namespace {
-struct Prof {
-  int kid = -1;
-  int cap = 0;
-  int n = 0;
-  bool open = false;
-  std::vector<hipEvent_t> ev0, ev1;
-};
-Prof g_prof;
-}  // namespace
-
-void prof_begin(int kid, hipStream_t s) {
-  if (kid != g_prof.kid || g_prof.n >= g_prof.cap) return;
-  if (hipEventRecord(g_prof.ev0[g_prof.n], s) == hipSuccess) g_prof.open = true;
-}
-void prof_end(int kid, hipStream_t s) {
-  if (!g_prof.open || kid != g_prof.kid) return;
-  if (hipEventRecord(g_prof.ev1[g_prof.n], s) == hipSuccess) g_prof.n++;
-  g_prof.open = false;
-}
 
 namespace {
 thread_local char g_last_error[160] = "";
@@ -68,6 +43,12 @@ int check_cfg(const moe_cfg* c) {
   if (c->T * c->k > 0x7fffffffLL) return MOE_ERR_SHAPE;
   if (!(c->route_margin == c->route_margin)) return MOE_ERR_ARG;  // NaN
   if (!(c->aux_coeff >= 0.0f && c->aux_coeff <= FLT_MAX)) return MOE_ERR_ARG;  // NaN, <0, inf
+  if (c->probe) {
+    const moe_probe* p = c->probe;
+    if (p->kernel_id < 0 || p->kernel_id >= MOE_KERNEL_COUNT_ || p->capacity < 0 ||
+        p->count < 0 || (p->capacity > 0 && (!p->begin || !p->end)))
+      return MOE_ERR_ARG;
+  }
   const size_t s = elem_bytes(*c);
   if ((c->d * s) % 16 != 0 || (c->f * s) % 16 != 0) return MOE_ERR_ALIGN;
   return MOE_OK;
@@ -341,9 +322,8 @@ int moe_router_aux(const moe_cfg* cfg, const float* probs, const int32_t* counts
 
 int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr, const float* probs,
                   const int32_t* idx, const int32_t* row_of, const int32_t* counts,
-                  const float* gate, const void* dOut, const float* dgate, const void* dXp,
-                  void* dX, void* dWr, float* db, void* ws, size_t ws_bytes,
-                  moe_stream_t stream) {
+                  const float* dgate, const float* dXe, void* dX, void* dWr, float* db,
+                  void* ws, size_t ws_bytes, moe_stream_t stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_cfg& c = *cfg;
   const Sizes z = sizes(c);
@@ -353,19 +333,15 @@ int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr, const float
   MOE_TRY(need(idx, z.Tk, 4));
   MOE_TRY(need(row_of, z.Tk, 4));
   if (c.aux_coeff > 0.0f) MOE_TRY(need(counts, (size_t)c.E * 4, 4));
-  if (fallback(c)) {
-    MOE_TRY(need(gate, z.Tk, 4));
-    MOE_TRY(need(dOut, z.Td, 16));
-  }
   MOE_TRY(need(dgate, z.Tk, 4));
-  MOE_TRY(need(dXp, z.Rd, 16));
+  MOE_TRY(need(dXe, (size_t)c.T * c.d * 4, 16));
   MOE_TRY(need(dX, z.Td, 16));
   MOE_TRY(need(dWr, z.dE, 4));
   if (db) MOE_TRY(need(db, (size_t)c.E * 4, 4));
   MOE_TRY(need_ws(c, ws, ws_bytes));
   clear_stale_error();
-  return launch_route_bwd(c, x, Wr, probs, idx, row_of, counts, gate, dOut, dgate, dXp, dX,
-                          dWr, db, ws, S(stream));
+  return launch_route_bwd(c, x, Wr, probs, idx, row_of, counts, nullptr, nullptr, dgate,
+                          nullptr, dXe, dX, dWr, db, ws, S(stream));
 }
 
 static int check_ctx(const moe_cfg& c, const moe_ctx* x) {
@@ -452,44 +428,11 @@ int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* x, const
                              ctx->offsets, tiles));
   MOE_TRY(launch_ffn_bwd(c, ctx->x_perm, ctx->offsets, w->W1, w->W2, ctx->A, ctx->H, dYp,
                          dXp, g->dW1, g->dW2, ws, s, /*have_tiles=*/true));
+  // the unpermute-sum of dXp is fused into the router's dX
   return launch_route_bwd(c, x, w->Wr, ctx->probs, ctx->idx, ctx->row_of, ctx->counts,
-                          ctx->gate, dOut, dgate, dXp, dX, g->dWr, g->db, ws, s);
+                          ctx->gate, dOut, dgate, dXp, nullptr, dX, g->dWr, g->db, ws, s);
 }
 
 const char* moe_last_error(void) { return g_last_error; }
-
-int moe_prof_arm(int kernel_id, int max_launches) {
-  if (kernel_id < 0 || kernel_id >= MOE_KERNEL_COUNT_ || max_launches < 0)
-    return MOE_ERR_ARG;
-  while ((int)g_prof.ev0.size() < max_launches) {
-    hipEvent_t a, b;
-    if (hipEventCreate(&a) != hipSuccess) return MOE_ERR_LAUNCH;
-    if (hipEventCreate(&b) != hipSuccess) return MOE_ERR_LAUNCH;
-    g_prof.ev0.push_back(a);
-    g_prof.ev1.push_back(b);
-  }
-  g_prof.kid = kernel_id;
-  g_prof.cap = max_launches;
-  g_prof.n = 0;
-  g_prof.open = false;
-  return MOE_OK;
-}
-
-int moe_prof_read(float* total_ms, int* launches) {
-  if (!total_ms || !launches) return MOE_ERR_ARG;
-  float sum = 0.0f;
-  for (int i = 0; i < g_prof.n; ++i) {
-    if (hipEventSynchronize(g_prof.ev1[i]) != hipSuccess) return MOE_ERR_LAUNCH;
-    float ms = 0.0f;
-    if (hipEventElapsedTime(&ms, g_prof.ev0[i], g_prof.ev1[i]) != hipSuccess)
-      return MOE_ERR_LAUNCH;
-    sum += ms;
-  }
-  *total_ms = sum;
-  *launches = g_prof.n;
-  g_prof.kid = -1;
-  g_prof.n = 0;
-  return MOE_OK;
-}
 
 }  // extern "C"

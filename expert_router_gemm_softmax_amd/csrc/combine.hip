@@ -27,16 +27,48 @@ __device__ __forceinline__ void load_pass(const T* __restrict__ src, int64_t r, 
   }
 }
 
+// The router backward's dz of one token for E = 8 RV experts, dz = hi + lo
+// of the bf16 pair in dzb [T][2E]
+template <int RV>
+__device__ __forceinline__ void load_dz(const uint16_t* __restrict__ dzb, int64_t t,
+                                        float (&dzf)[8 * RV]) {
+  const uint16_t* dz = dzb + t * (16 * RV);
+#pragma unroll
+  for (int r = 0; r < RV; ++r) {
+    float hi[8], lo[8];
+    St<uint16_t>::unpack(ld16(dz + 8 * r), hi);
+    St<uint16_t>::unpack(ld16(dz + 8 * RV + 8 * r), lo);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dzf[8 * r + e] = hi[e] + lo[e];
+  }
+}
+// sum_e dz[e] Wr[i,e] in fp32, expert order (Wr [d][8 RV] bf16, 16-byte rows)
+template <int RV>
+__device__ __forceinline__ float router_term(const float (&dzf)[8 * RV],
+                                             const uint16_t* __restrict__ Wr, int i) {
+  const uint16_t* wr = Wr + (int64_t)i * (8 * RV);
+  float u = 0.0f;
+#pragma unroll
+  for (int r = 0; r < RV; ++r) {
+    float w8[8];
+    St<uint16_t>::unpack(ld16(wr + 8 * r), w8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u += dzf[8 * r + e] * w8[e];
+  }
+  return u;
+}
+
 // out[t] = sum over kept j (ascending) of g_j * src[row_of[t,j]], with
 // g_j = gate[t,j] (combine) or 1 (gradient unpermute-sum, fp32 output).
 // With a fallback row source fb (the identity fallback: x for the combine,
 // dOut for the unpermute-sum) a dropped j adds gate[t,j] * fb[t] in its
 // place.  One wave per token; two assignments' rows are in flight at once.
 // RV > 0 (bf16, E = 8 RV experts): the router backward's dX instead,
-// sum_e dz[t,e] Wr[i,e] plus the unpermute-sum, in fp32 starting from the
-// router term (dz = hi + lo of the bf16 pair in dzb [T][2E]; Wr [d][E]),
-// and one rounding to bf16 -- the E products per output run on the VALU,
-// and no fp32 sum goes through HBM.
+// RN_bf16(unpermute-sum + sum_e dz[t,e] Wr[i,e]), the unpermute-sum taken
+// exactly as the fp32 one above and the router term added last (dz = hi +
+// lo of the bf16 pair in dzb [T][2E]; Wr [d][E]) -- the E products per
+// output run on the VALU, and no fp32 sum goes through HBM.  The result is
+// bitwise router_dx_kernel's on the fp32 unpermute-sum.
 template <typename T, typename OutT, bool GATED, int RV = 0>
 __global__ __launch_bounds__(256) void gather_sum_kernel(
     const T* __restrict__ src, const int32_t* __restrict__ row_of,
@@ -50,44 +82,13 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(
        t += (int64_t)gridDim.x * kCW) {
     const int32_t* rows = row_of + t * k;
     float dzf[RV > 0 ? 8 * RV : 1];
-    if constexpr (RV > 0) {
-      const uint16_t* dz = dzb + t * (16 * RV);
-#pragma unroll
-      for (int r = 0; r < RV; ++r) {
-        float hi[8], lo[8];
-        St<uint16_t>::unpack(ld16(dz + 8 * r), hi);
-        St<uint16_t>::unpack(ld16(dz + 8 * RV + 8 * r), lo);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dzf[8 * r + e] = hi[e] + lo[e];
-      }
-    }
+    if constexpr (RV > 0) load_dz<RV>(dzb, t, dzf);
     for (int g0 = 0; g0 < nch; g0 += kWave * kCPL) {
       float acc[kCPL][V];
 #pragma unroll
       for (int s = 0; s < kCPL; ++s)
 #pragma unroll
         for (int q = 0; q < V; ++q) acc[s][q] = 0.0f;
-      if constexpr (RV > 0) {
-        // the router term first: acc starts at sum_e dz[t,e] Wr[i,e]
-#pragma unroll
-        for (int s = 0; s < kCPL; ++s) {
-          const int c = g0 + s * kWave + lane;
-          if (c >= nch) continue;
-#pragma unroll
-          for (int q = 0; q < V; ++q) {
-            const uint16_t* wr = Wr + (int64_t)(c * V + q) * (8 * RV);
-            float u = 0.0f;
-#pragma unroll
-            for (int r = 0; r < RV; ++r) {
-              float w8[8];
-              St<uint16_t>::unpack(ld16(wr + 8 * r), w8);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) u += dzf[8 * r + e] * w8[e];
-            }
-            acc[s][q] = u;
-          }
-        }
-      }
       for (int j = 0; j < k; j += 2) {
         const int32_t r0 = rows[j];
         const int32_t r1 = j + 1 < k ? rows[j + 1] : -2;  // -2: no assignment
@@ -113,6 +114,16 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(
           }
         }
       }
+      if constexpr (RV > 0) {
+        // the router term last: RN(unpermute-sum + sum_e dz[t,e] Wr[i,e])
+#pragma unroll
+        for (int s = 0; s < kCPL; ++s) {
+          const int c = g0 + s * kWave + lane;
+          if (c >= nch) continue;
+#pragma unroll
+          for (int q = 0; q < V; ++q) acc[s][q] += router_term<RV>(dzf, Wr, c * V + q);
+        }
+      }
 #pragma unroll
       for (int s = 0; s < kCPL; ++s) {
         const int c = g0 + s * kWave + lane;
@@ -127,6 +138,36 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(
                               __float_as_uint(acc[s][q + 2]), __float_as_uint(acc[s][q + 3])});
         }
       }
+    }
+  }
+}
+
+// The router backward's dX from the fp32 unpermute-sum dXe [T][d] (bf16,
+// E = 8 RV experts): dX[t,i] = RN_bf16(dXe[t,i] + sum_e dz[t,e] Wr[i,e]),
+// one wave per token, 8 consecutive outputs per lane and pass.
+template <int RV>
+__global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict__ dxe,
+                                                        const uint16_t* __restrict__ dzb,
+                                                        const uint16_t* __restrict__ Wr,
+                                                        uint16_t* __restrict__ dX, int64_t T_,
+                                                        int d) {
+  const int lane = threadIdx.x & 63;
+  const int nch = d / 8;
+  for (int64_t t = (int64_t)blockIdx.x * kCW + (threadIdx.x >> 6); t < T_;
+       t += (int64_t)gridDim.x * kCW) {
+    float dzf[8 * RV];
+    load_dz<RV>(dzb, t, dzf);
+    for (int c = lane; c < nch; c += kWave) {
+      const float* src = dxe + t * d + c * 8;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + 4);
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = a0[q] + router_term<RV>(dzf, Wr, c * 8 + q);
+        v[q + 4] = a1[q] + router_term<RV>(dzf, Wr, c * 8 + q + 4);
+      }
+      st16(dX + t * d + c * 8, St<uint16_t>::pack(v));
     }
   }
 }
@@ -257,6 +298,22 @@ int launch_unpermute_bwd(const moe_cfg& c, const void* dXp, const int32_t* row_o
                gather_sum_kernel<float, float, false><<<grid, 256, 0, s>>>(
                    static_cast<const float*>(dXp), row_of, gate, static_cast<const float*>(fb),
                    dXe, c.T, c.d, c.k));
+  return MOE_OK;
+}
+
+int launch_router_dx(const moe_cfg& c, const float* dXe, const uint16_t* dzb, const void* Wr,
+                     void* dX, hipStream_t s) {
+  if (c.T == 0) return MOE_OK;
+  if (c.dtype != MOE_BF16 || (c.E != 8 && c.E != 16)) return MOE_ERR_UNIMPLEMENTED;
+  const int grid = token_grid(c.T);
+  const uint16_t* w = static_cast<const uint16_t*>(Wr);
+  uint16_t* o = static_cast<uint16_t*>(dX);
+  if (c.E == 8)
+    MOE_LAUNCH(MOE_KERNEL_ROUTE_BWD_DX, s,
+               router_dx_kernel<1><<<grid, 256, 0, s>>>(dXe, dzb, w, o, c.T, c.d));
+  else
+    MOE_LAUNCH(MOE_KERNEL_ROUTE_BWD_DX, s,
+               router_dx_kernel<2><<<grid, 256, 0, s>>>(dXe, dzb, w, o, c.T, c.d));
   return MOE_OK;
 }
 

@@ -259,13 +259,27 @@ inline P* ws_ptr(void* ws, size_t off) {
 }
 
 // ------------------------------------------------------------------ launch + timing
-void prof_begin(int kernel_id, hipStream_t s);
-void prof_end(int kernel_id, hipStream_t s);
+// The caller's kernel timing (moe_cfg.probe): event records around the
+// launches of the probed kernel
+inline void prof_begin(const moe_cfg& c, int kid, hipStream_t s) {
+  moe_probe* p = c.probe;
+  if (p && p->kernel_id == kid && p->count < p->capacity)
+    (void)hipEventRecord(static_cast<hipEvent_t>(p->begin[p->count]), s);
+}
+inline void prof_end(const moe_cfg& c, int kid, hipStream_t s) {
+  moe_probe* p = c.probe;
+  if (p && p->kernel_id == kid && p->count < p->capacity) {
+    (void)hipEventRecord(static_cast<hipEvent_t>(p->end[p->count]), s);
+    p->count++;
+  }
+}
 void note_launch_error(int kernel_id, hipError_t e);
 
-// Launch, then check that launch.  Entry points clear any error state left
-// by earlier, unrelated HIP calls of the process before their first launch.
-// A launch whose timing belongs to an enclosing prof_begin/prof_end pair.
+// Launch, then check that launch (a failed event record of the probe shows
+// up here too).  Entry points clear any error state left by earlier,
+// unrelated HIP calls of the process before their first launch.  Both
+// macros need the launch's moe_cfg in scope as `c`.
+// A launch that the probe does not time.
 #define MOE_LAUNCH_NP(kid, ...)                                       \
   do {                                                                \
     __VA_ARGS__;                                                      \
@@ -278,10 +292,10 @@ void note_launch_error(int kernel_id, hipError_t e);
 
 #define MOE_LAUNCH(kid, stream, ...)                                  \
   do {                                                                \
-    ::moe::prof_begin((kid), (stream));                               \
+    ::moe::prof_begin(c, (kid), (stream));                            \
     __VA_ARGS__;                                                      \
+    ::moe::prof_end(c, (kid), (stream));                              \
     hipError_t e_ = hipGetLastError();                                \
-    ::moe::prof_end((kid), (stream));                                 \
     if (e_ != hipSuccess) {                                           \
       ::moe::note_launch_error((kid), e_);                            \
       return MOE_ERR_LAUNCH;                                          \
@@ -323,10 +337,12 @@ int launch_combine_bwd(const moe_cfg& c, const void* dOut, const void* Y,
 int launch_unpermute_bwd(const moe_cfg& c, const void* dXp, const int32_t* row_of,
                          const float* gate, const void* dOut, float* dXe, hipStream_t s,
                          int kernel_id = MOE_KERNEL_UNPERMUTE_BWD);
+// dX = dXe + dz Wr^T: dXe is the caller's fp32 unpermute-sum, or (dXe NULL)
+// gathered from dXp, row_of and, under the identity fallback, gate and dOut
 int launch_route_bwd(const moe_cfg& c, const void* x, const void* Wr,
                      const float* probs, const int32_t* idx, const int32_t* row_of,
                      const int32_t* counts, const float* gate, const void* dOut,
-                     const float* dgate, const void* dXp, void* dX, void* dWr, float* db,
-                     void* ws, hipStream_t s);
+                     const float* dgate, const void* dXp, const float* dXe, void* dX,
+                     void* dWr, float* db, void* ws, hipStream_t s);
 
 }  // namespace moe

@@ -800,19 +800,20 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
   }
   if constexpr (MODE == MODE_ROW) {
     if (g.part != nullptr) {
-      // the GEMM and its tail fixup are timed as one launch
-      // grid-stride over the split tiles' 8-column chunks; few blocks, so that
-      // a problem whose tail was not split pays little for the launch
+      // the fixup is timed under its own id, so that a probe of the GEMM
+      // times the main kernel alone; grid-stride over the split tiles'
+      // 8-column chunks, few blocks, so that a problem whose tail was not
+      // split pays little for the launch
       const int fgrid = (int)std::min<int64_t>(ceil_div((int64_t)g.slots * BM * BN / 8, 256), 512);
-      prof_begin(kid, s);
       if (BM == 256) {
-        MOE_LAUNCH_NP(kid, gemm_bf16_kernel<MODE, B_KC, EPI, 256, 256><<<grid, 256, 0, s>>>(g));
-        MOE_LAUNCH_NP(kid, gemm_fixup_kernel<EPI, 256, 256><<<fgrid, 256, 0, s>>>(g));
+        MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 256, 256><<<grid, 256, 0, s>>>(g));
+        MOE_LAUNCH(MOE_KERNEL_GEMM_FIXUP, s,
+                   gemm_fixup_kernel<EPI, 256, 256><<<fgrid, 256, 0, s>>>(g));
       } else {
-        MOE_LAUNCH_NP(kid, gemm_bf16_kernel<MODE, B_KC, EPI, 128, 128><<<grid, 256, 0, s>>>(g));
-        MOE_LAUNCH_NP(kid, gemm_fixup_kernel<EPI, 128, 128><<<fgrid, 256, 0, s>>>(g));
+        MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 128, 128><<<grid, 256, 0, s>>>(g));
+        MOE_LAUNCH(MOE_KERNEL_GEMM_FIXUP, s,
+                   gemm_fixup_kernel<EPI, 128, 128><<<fgrid, 256, 0, s>>>(g));
       }
-      prof_end(kid, s);
       return MOE_OK;
     }
   }

@@ -98,14 +98,14 @@ int launch_route_aux(const moe_cfg& c, const float* probs, const int32_t* counts
   const WsLayout L = ws_layout(c);
   float* part = ws_ptr<float>(ws, L.aux_part);
   // both kernels are timed as one launch
-  prof_begin(MOE_KERNEL_ROUTE_AUX, s);
+  prof_begin(c, MOE_KERNEL_ROUTE_AUX, s);
   MOE_LAUNCH_NP(MOE_KERNEL_ROUTE_AUX,
                 route_aux_part_kernel<<<L.nblk_aux, 256, 0, s>>>(probs, part, c.T, c.E));
   MOE_LAUNCH_NP(MOE_KERNEL_ROUTE_AUX,
                 route_aux_final_kernel<<<1, 1024, 0, s>>>(part, counts, offsets, aux,
                                                          L.nblk_aux, c.T, c.E, c.k,
                                                          c.aux_coeff));
-  prof_end(MOE_KERNEL_ROUTE_AUX, s);
+  prof_end(c, MOE_KERNEL_ROUTE_AUX, s);
   return MOE_OK;
 }
 

@@ -1,25 +1,26 @@
-// Router backward (B1, with the gradient unpermute-sum B2 fused in).  The
-// router is a shared parameter with an ordinary gradient ("GPU expert
-// parallel", section "Sharded by expert, replicated everywhere else");
-// index, top-k and capacity steps are piecewise constant and pass no
-// gradient.
+// Router backward (B1).  The router is a shared parameter with an ordinary
+// gradient ("GPU expert parallel", section "Sharded by expert, replicated
+// everywhere else"); index, top-k and capacity steps are piecewise constant
+// and pass no gradient.
 //   dp[t, e] = a_e + dgate[t,j] if e = idx[t,j] for a kept j, else a_e
 //   (with renormalised gates g_j = p_j / S the gate term of a selected j is
 //   (dgate_j - sum_i g_i dgate_i) / S instead, dropped j included)
 //   dz = p * (dp - sum_e p dp)
 // where a_e = alpha E counts[e] / (T k T) is the gradient of the
 // load-balancing loss (zero when its coefficient alpha is zero); under the
-// identity fallback of dropped assignments their dgate counts as well, and
-// dX gains gate * dOut for each of them (in the unpermute-sum).
-//   dX  = sum_{kept j} dXp[row_of[t,j]] + dz Wr^T
-//   dWr = x^T dz,  db = sum_t dz
-// Both products run on the grouped GEMM kernels.  For bf16 storage dz is
-// split into bf16 high and low parts (dz = hi + lo to ~2^-16 relative), and
-// the products use [hi | lo] against Wr stacked twice, so the router
-// gradient keeps ~fp32 accuracy on bf16 MFMA.  dX is one row-GEMM whose
-// epilogue adds the unpermute-sum (gathered beforehand into an fp32 row
-// buffer by a bandwidth-bound kernel); dWr is a k-ragged GEMM over uniform
-// token chunks writing fp32 partials, summed in fixed order with db.
+// identity fallback of dropped assignments their dgate counts as well.
+//   dX  = dXe + dz Wr^T,  dWr = x^T dz,  db = sum_t dz
+// dXe is the gradient unpermute-sum (B2): either the caller's fp32 buffer
+// (the per-step entry point) or, in the layer backward, gathered here from
+// dXp (B2 fused in).  Both products run on the grouped GEMM kernels.  For
+// bf16 storage dz is split into bf16 high and low parts (dz = hi + lo to
+// ~2^-16 relative), and the products use [hi | lo] against Wr stacked
+// twice, so the router gradient keeps ~fp32 accuracy on bf16 MFMA.  dX is
+// one row-GEMM whose epilogue adds dXe; dWr is a k-ragged GEMM over uniform
+// token chunks writing fp32 partials, summed in fixed order with db.  With
+// 8 or 16 experts (bf16) dz Wr^T runs on the VALU instead (combine.hip),
+// fused with the gather in the layer backward.  The two forms give bitwise
+// the same dX.
 #include "gemm.h"
 
 namespace moe {
@@ -30,6 +31,9 @@ namespace moe {
 int launch_unpermute_router_dx(const moe_cfg& c, const void* dXp, const int32_t* row_of,
                                const float* gate, const void* dOut, const uint16_t* dzb,
                                const void* Wr, void* dX, hipStream_t s);
+// the same from a finished fp32 unpermute-sum dXe [T][d]
+int launch_router_dx(const moe_cfg& c, const float* dXe, const uint16_t* dzb, const void* Wr,
+                     void* dX, hipStream_t s);
 namespace {
 
 // wrp[i][e] = wrp[i][Ep + e] = Wr[i][e] (zero for E <= e < Ep): the router
@@ -187,8 +191,8 @@ __global__ __launch_bounds__(256) void route_bwd_reduce_kernel(
 template <typename T>
 int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
                 const int32_t* idx, const int32_t* row_of, const int32_t* counts,
-                const float* gate, const void* dOut, const float* dgate, const T* dXp, T* dX,
-                T* dWr, float* db, void* ws, hipStream_t s) {
+                const float* gate, const void* dOut, const float* dgate, const T* dXp,
+                const float* dXe, T* dX, T* dWr, float* db, void* ws, hipStream_t s) {
   constexpr bool BF = sizeof(T) == 2;
   const WsLayout L = ws_layout(c);
   const int Ep = bwd_ep(c.E);
@@ -213,16 +217,21 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
   int rc;
   if (c.T > 0 && BF && (c.E == 8 || c.E == 16) &&
       (reinterpret_cast<uintptr_t>(Wr) & 15) == 0) {
-    // few experts: dz Wr^T is E FMAs per output, done on the VALU inside the
-    // unpermute-sum's pass (no fp32 sum through HBM, no GEMM launch); Wr's
-    // rows are read as 16-byte vectors
-    rc = launch_unpermute_router_dx(c, dXp, row_of, gate, dOut, dzb, Wr, dX, s);
+    // few experts: dz Wr^T is E FMAs per output, done on the VALU (inside the
+    // unpermute-sum's pass when dXp is given: no fp32 sum through HBM, no GEMM
+    // launch); Wr's rows are read as 16-byte vectors
+    rc = dXe ? launch_router_dx(c, dXe, dzb, Wr, dX, s)
+             : launch_unpermute_router_dx(c, dXp, row_of, gate, dOut, dzb, Wr, dX, s);
     if (rc != MOE_OK) return rc;
   } else if (c.T > 0) {
-    // dX = [dz_hi | dz_lo] [Wr | Wr]^T + unpermute-sum of dXp (fp32)
-    float* dxe = ws_ptr<float>(ws, L.dxe);
-    rc = launch_unpermute_bwd(c, dXp, row_of, gate, dOut, dxe, s, MOE_KERNEL_ROUTE_BWD_DX);
-    if (rc != MOE_OK) return rc;
+    // dX = [dz_hi | dz_lo] [Wr | Wr]^T + dXe (fp32), dXe gathered from dXp
+    // into the workspace unless the caller gives it
+    float* dxe = const_cast<float*>(dXe);
+    if (dxe == nullptr) {
+      dxe = ws_ptr<float>(ws, L.dxe);
+      rc = launch_unpermute_bwd(c, dXp, row_of, gate, dOut, dxe, s, MOE_KERNEL_ROUTE_BWD_DX);
+      if (rc != MOE_OK) return rc;
+    }
     GemmArgs g{};
     g.E = 1;
     g.M = (int)c.T;
@@ -273,19 +282,18 @@ int route_bwd_t(const moe_cfg& c, const T* x, const T* Wr, const float* probs,
 int launch_route_bwd(const moe_cfg& c, const void* x, const void* Wr,
                      const float* probs, const int32_t* idx, const int32_t* row_of,
                      const int32_t* counts, const float* gate, const void* dOut,
-                     const float* dgate, const void* dXp, void* dX, void* dWr, float* db,
-                     void* ws, hipStream_t s) {
+                     const float* dgate, const void* dXp, const float* dXe, void* dX,
+                     void* dWr, float* db, void* ws, hipStream_t s) {
   if (c.dtype == MOE_BF16)
     return route_bwd_t<uint16_t>(c, static_cast<const uint16_t*>(x),
                                  static_cast<const uint16_t*>(Wr), probs, idx, row_of, counts,
-                                 gate, dOut, dgate,
-                                 static_cast<const uint16_t*>(dXp),
+                                 gate, dOut, dgate, static_cast<const uint16_t*>(dXp), dXe,
                                  static_cast<uint16_t*>(dX), static_cast<uint16_t*>(dWr), db,
                                  ws, s);
   return route_bwd_t<float>(c, static_cast<const float*>(x), static_cast<const float*>(Wr),
                             probs, idx, row_of, counts, gate, dOut, dgate,
-                            static_cast<const float*>(dXp),
-                            static_cast<float*>(dX), static_cast<float*>(dWr), db, ws, s);
+                            static_cast<const float*>(dXp), dXe, static_cast<float*>(dX),
+                            static_cast<float*>(dWr), db, ws, s);
 }
 
 }  // namespace moe

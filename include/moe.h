@@ -96,12 +96,28 @@ typedef enum { MOE_FP32 = 0, MOE_BF16 = 1 } moe_dtype;
  * dOut[t] to dX[t] with dgate[t,j] = <dOut[t], x[t]>.  "The Capacity
  * Factor" lets excess tokens take a fallback path without defining it; the
  * pass-through is the plainest one.  Under it, moe_combine and
- * moe_combine_bwd need x, and moe_unpermute_bwd and moe_route_bwd need gate
- * and dOut. */
+ * moe_combine_bwd need x, and moe_unpermute_bwd needs gate and dOut. */
 #define MOE_FLAG_DROP_IDENTITY 8u
 
 /* hipStream_t, passed opaquely so that this header needs no HIP headers. */
 typedef void* moe_stream_t;
+
+/* Kernel timing for benchmarks, owned entirely by the caller (the library
+ * keeps no state of its own).  When cfg->probe is set, each launch of kernel
+ * `kernel_id` made by a call with that cfg is bracketed by hipEventRecord of
+ * begin[count] and end[count] on the launch's stream, and count is
+ * incremented, until count reaches capacity.  The events are hipEvent_t
+ * handles the caller created; the library neither creates, waits on nor
+ * reads them.  Calls that share one probe must not run concurrently.  Kernel
+ * ids: moe_kernel_id below. */
+typedef struct moe_probe {
+  int32_t kernel_id;
+  int32_t capacity;   /* entries of begin and end */
+  int32_t count;      /* launches recorded so far */
+  int32_t reserved_;  /* 0 */
+  void** begin;       /* hipEvent_t[capacity] */
+  void** end;         /* hipEvent_t[capacity] */
+} moe_probe;
 
 typedef struct moe_cfg {
   int64_t T;          /* tokens; for the expert-share use (a ragged batch
@@ -119,6 +135,7 @@ typedef struct moe_cfg {
                          load-balancing loss (0 = none); see moe_router_aux.
                          When > 0, moe_route_bwd and moe_layer_bwd add its
                          gradient. */
+  moe_probe* probe;   /* NULL, or kernel timing (see moe_probe) */
 } moe_cfg;
 
 /* Capacity of the capacity-factor rule: C = ceil(cf * T * k / E), exact.
@@ -283,18 +300,18 @@ MOE_API int moe_unpermute_bwd(const moe_cfg* cfg, const void* dXp,
  *       (dgate of a dropped assignment counts as 0, except under
  *       MOE_FLAG_DROP_IDENTITY, where every assignment's dgate counts)
  *   dz  = probs * (dp - sum_e probs * dp)
- *   db  = sum_t dz                       [E] float
+ *   db  = sum_t dz                       [E] float (db may be NULL)
  *   dWr = x^T dz                         [d,E] s
- *   dX  = sum_{kept j} dXp[row_of[t,j]] + dz Wr^T   [T,d] s
- *         (+ gate[t,j] * dOut[t] for each dropped j under
- *         MOE_FLAG_DROP_IDENTITY; gate and dOut may be NULL otherwise)
- * (the unpermute-sum of B2 is fused in).  Workspace as above. */
+ *   dX  = RN_s(dXe + dz Wr^T)            [T,d] s
+ * dXe [T,d] float is the unpermute-sum written by moe_unpermute_bwd (which
+ * already holds the identity fallback's terms).  counts [E] may be NULL
+ * when cfg->aux_coeff == 0.  moe_layer_bwd computes the same dX with the
+ * unpermute-sum fused in.  Workspace as above. */
 MOE_API int moe_route_bwd(const moe_cfg* cfg, const void* x, const void* Wr,
-                  const float* probs, const int32_t* idx,
-                  const int32_t* row_of, const int32_t* counts /* [E]; may be NULL
-                  when cfg->aux_coeff == 0 */, const float* gate, const void* dOut,
-                  const float* dgate, const void* dXp, void* dX, void* dWr, float* db,
-                  void* ws, size_t ws_bytes, moe_stream_t stream);
+                  const float* probs, const int32_t* idx, const int32_t* row_of,
+                  const int32_t* counts, const float* dgate, const float* dXe,
+                  void* dX, void* dWr, float* db, void* ws, size_t ws_bytes,
+                  moe_stream_t stream);
 
 /* ------------------------------------------------------------ whole layer */
 
@@ -346,12 +363,8 @@ MOE_API int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* 
                   const moe_grads* g, void* ws, size_t ws_bytes,
                   moe_stream_t stream);
 
-/* ----------------------------------------------------------- measurement
- * Kernel timing for benchmarks: after moe_prof_arm(kernel, n), the next n
- * launches of that kernel are bracketed by HIP events on their stream;
- * moe_prof_read waits for them and returns the summed milliseconds and
- * the number of launches recorded.  Process-wide state: not for use from
- * several threads at once.  Kernel ids: */
+/* ----------------------------------------------------------- kernel ids
+ * Values of moe_probe.kernel_id. */
 typedef enum {
   MOE_KERNEL_ROUTE = 0,          /* softmax, top-k, certification */
   MOE_KERNEL_PERMUTE_COUNT = 1,
@@ -375,11 +388,9 @@ typedef enum {
   MOE_KERNEL_ROUTE_LOGITS = 19,  /* fast router logits x Wr (GEMM) */
   MOE_KERNEL_ROUTE_AUX = 20,     /* load-balancing loss and drop rate */
   MOE_KERNEL_GEMM_RECOMPUTE = 21, /* A, H recomputed in backward (MOE_FLAG_RECOMPUTE) */
-  MOE_KERNEL_COUNT_ = 22
+  MOE_KERNEL_GEMM_FIXUP = 22,    /* split-K tail sums of any row GEMM */
+  MOE_KERNEL_COUNT_ = 23
 } moe_kernel_id;
-
-MOE_API int moe_prof_arm(int kernel_id, int max_launches);
-MOE_API int moe_prof_read(float* total_ms, int* launches);
 
 #ifdef __cplusplus
 }

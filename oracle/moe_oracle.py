@@ -24,7 +24,7 @@ What is computed, and where the pages say so:
 * Expert FFN = per-expert feed-forward weights ("Sharded by expert"), here
   W1 (d x f) -> tanh-GELU -> W2 (f x d), no biases.
 
-Readings taken where the pages are silent (numbered as in the design doc; R8
+Readings taken where the pages are silent (numbered R1..R19 throughout; R8
 (bias) and R9 (FFN form) are stated with the inputs and the FFN above):
   R1 softmax over all E logits, then top-k; gate = probability of the chosen
      expert, not renormalised.

@@ -26,7 +26,7 @@ int main(void) {
   c.f = 4096;
   c.dtype = MOE_BF16;
   c.capacity = moe_capacity(4096, 2, 8, 1.25);
-  CHECK(sizeof(moe_cfg) == 56);
+  CHECK(sizeof(moe_cfg) == 64);
   CHECK(c.capacity == 1280);
   CHECK(moe_check_cfg(&c) == MOE_OK);
   CHECK(moe_rows_max(&c) == 8192);
@@ -49,7 +49,14 @@ int main(void) {
   CHECK(moe_route(&c, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == MOE_ERR_ARG);
   CHECK(strcmp(moe_status_str(MOE_OK), "ok") == 0);
   CHECK(strlen(moe_status_str(MOE_ERR_WORKSPACE)) > 0);
-  CHECK(moe_prof_arm(MOE_KERNEL_COUNT_, 1) == MOE_ERR_ARG);
+  {
+    moe_probe p = {MOE_KERNEL_COUNT_, 0, 0, 0, NULL, NULL};
+    c.probe = &p;
+    CHECK(moe_check_cfg(&c) == MOE_ERR_ARG);
+    p.kernel_id = MOE_KERNEL_GEMM_DH;
+    CHECK(moe_check_cfg(&c) == MOE_OK);
+    c.probe = NULL;
+  }
   printf("all host checks passed\n");
   return 0;
 }

@@ -268,22 +268,29 @@ def test_routing_variants_match_oracle(M, case):
         assert_close("out = x", to_f64(res["out"]), O.to_f64(inp["x"]), dt)
 
 
-@pytest.mark.parametrize("mode", ["save", "recompute", "variants", "c1"])
+@pytest.mark.parametrize("mode", ["save", "recompute", "variants", "c1", "gemm_router"])
 def test_step_entry_points_equal_the_layer_entry_points(M, mode):
-    """moe_route .. moe_route_bwd called one by one give bitwise the layer's
-    results (same kernels, same order); in the recomputation mode with no A
-    and H buffers at all; with every routing variant on (renormalised gates,
-    slot priority, identity fallback), whose extra inputs the step entry
-    points then take; and at C1's size, many tiles and a split-K tail per
-    GEMM, where the grouped GEMMs' M-tile schedule comes from the permute
-    and the combine backward in the layer but from the schedule kernel in
-    the steps."""
+    """The per-step entry points chained exactly as the header declares them
+    (moe_route, moe_permute, moe_router_aux, moe_grouped_ffn, moe_combine;
+    moe_combine_bwd, moe_grouped_ffn_bwd, moe_unpermute_bwd writing dXe,
+    moe_route_bwd reading it) give bitwise the layer's results and match the
+    oracle; in the recomputation mode with no A and H buffers at all; with
+    every routing variant on (renormalised gates, slot priority, identity
+    fallback), whose extra inputs the step entry points then take; at C1's
+    size, many tiles and a split-K tail per GEMM, where the grouped GEMMs'
+    M-tile schedule comes from the permute and the combine backward in the
+    layer but from the schedule kernel in the steps; and with 12 experts,
+    where the router's dX runs on the GEMM (the others, with 8 experts, on
+    the VALU)."""
     import torch
     recompute = mode == "recompute"
     var = dict(renorm=True, priority="slot", fallback="identity") if mode == "variants" else {}
     if mode == "c1":
         w = W.get("C1")
         inp = W.make_inputs(w, seed=3)
+    elif mode == "gemm_router":
+        w, inp = make_case(700, 128, 12, 3, 160, "bf16", 1.0, "normal", seed=5,
+                           aux_coeff=0.05)
     else:
         w, inp = make_case(700, 128, 8, 2, 160, "bf16", 1.0, "normal", seed=7,
                            aux_coeff=0.05, **var)
@@ -313,8 +320,8 @@ def test_step_entry_points_equal_the_layer_entry_points(M, mode):
     dXe = z(T, w.d, dt=torch.float32)
     M.moe_unpermute_bwd(cfg, dXp, row_of, dXe, gate=gate, dOut=d["dOut"])
     dX, dWr, db = z(T, w.d), torch.zeros_like(d["Wr"]), z(E, dt=torch.float32)
-    M.moe_route_bwd(cfg, d["x"], d["Wr"], probs, idx, row_of, counts, dg, dXp, dX, dWr, db,
-                    ws, gate=gate, dOut=d["dOut"])
+    M.moe_route_bwd(cfg, d["x"], d["Wr"], probs, idx, row_of, counts, dg, dXe, dX, dWr, db,
+                    ws)
     torch.cuda.synchronize()
     R = int(to_int(offsets)[-1])
     for name, a, b in [("probs", probs, res["probs"]), ("idx", idx, res["idx"]),
@@ -330,10 +337,11 @@ def test_step_entry_points_equal_the_layer_entry_points(M, mode):
             assert b is None, name
             continue
         assert torch.equal(a[:R], b[:R]), name
-    # unpermute-sum against the oracle definition on the GPU's own dXp
+    # the chain's own outputs against the oracle
     fw = O.layer_fwd(inp, w)
     bw = O.layer_bwd(inp, w, fw)
     assert_close("dXe", to_f64(dXe), bw["dXe"], "bf16")
+    assert_close("dX", to_f64(dX), bw["dX"], "bf16")
     gn = np.zeros_like(bw["dgate"])
     dOut = O.to_f64(inp["dOut"])
     for j in range(w.k):
@@ -455,3 +463,37 @@ def test_layer_step_replays_from_a_hip_graph(M):
         got = snap()
         for k in keys:
             assert torch.equal(got[k], ref[k]), (r, k)
+
+
+def test_kernel_probe_records_the_probed_launches_only(M):
+    """A caller-owned probe in cfg times exactly the launches of its kernel
+    (the split-K fixup under its own id), stops at its capacity, and leaves
+    every result bitwise unchanged."""
+    import torch
+    w = W.get("C1")
+    inp = W.make_inputs(w, seed=0)
+    res = run_layer(M, w, inp)
+    layer, d = res["_layer"], res["_dev"]
+    probe = M.KernelProbe("GEMM_DH", 3)
+    probe.attach(layer.cfg)
+    outs = []
+    for _ in range(4):
+        out = layer.forward(d["x"])
+        dX, g = layer.backward(d["x"], d["dOut"])
+        outs.append((out, dX, g["dW1"]))
+    torch.cuda.synchronize()
+    probe.detach(layer.cfg)
+    ms, n, each = probe.read()
+    probe.close()
+    assert n == 3 and all(t > 0 for t in each), (n, each)
+    for out, dX, dW1 in outs:
+        assert torch.equal(out, res["out"]) and torch.equal(dX, res["dX"])
+        assert torch.equal(dW1, res["dW1"])
+    fix = M.KernelProbe("GEMM_FIXUP", 64)
+    fix.attach(layer.cfg)
+    layer.backward(d["x"], d["dOut"])
+    torch.cuda.synchronize()
+    fix.detach(layer.cfg)
+    _, nf, _ = fix.read()
+    fix.close()
+    assert nf == 2  # the dH and dX GEMMs' fixups (the weight gradients have none)

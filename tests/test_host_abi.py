@@ -207,7 +207,14 @@ def test_entry_points_reject_bad_arguments_before_launch():
                              None) == B.MOE_ERR_WORKSPACE
     assert B.lib.moe_layer_fwd(ctypes.byref(c), None, _A, _A, None, _A, 1 << 30,
                                None) == B.MOE_ERR_ARG
-    assert B.lib.moe_prof_arm(99, 1) == B.MOE_ERR_ARG
+    # a probe with an unknown kernel id, or events missing, is rejected
+    probe = B.MoeProbe(kernel_id=99, capacity=1, count=0)
+    c.probe = ctypes.addressof(probe)
+    assert B.lib.moe_check_cfg(ctypes.byref(c)) == B.MOE_ERR_ARG
+    probe.kernel_id = B.KERNELS["GEMM_DH"]
+    assert B.lib.moe_check_cfg(ctypes.byref(c)) == B.MOE_ERR_ARG  # begin/end NULL
+    probe.capacity = 0
+    assert B.lib.moe_check_cfg(ctypes.byref(c)) == B.MOE_OK
 
 
 def test_status_strings():
@@ -218,10 +225,11 @@ def test_status_strings():
 
 def test_cfg_struct_layout_matches_header():
     # int64 T; 5 x int32; int64 capacity (8-aligned); float; uint32; float
-    # aux_coeff -> 52 bytes, padded to 56 for the int64 members
-    assert ctypes.sizeof(B.MoeCfg) == 56
+    # aux_coeff -> 52 bytes, padded to 56 for the probe pointer
+    assert ctypes.sizeof(B.MoeCfg) == 64
     assert B.MoeCfg.capacity.offset == 32 and B.MoeCfg.flags.offset == 44
-    assert B.MoeCfg.aux_coeff.offset == 48
+    assert B.MoeCfg.aux_coeff.offset == 48 and B.MoeCfg.probe.offset == 56
+    assert ctypes.sizeof(B.MoeProbe) == 32 and B.MoeProbe.begin.offset == 16
     # MoeCtx: eleven tensors, then the optional diagnostics output
     assert B.MoeCtx.aux.offset == 11 * ctypes.sizeof(ctypes.c_void_p)
 
@@ -264,11 +272,13 @@ def test_identity_fallback_entry_points_need_its_extra_inputs():
                                                     None)
     assert ub(fb, None, _A) == B.MOE_ERR_ARG and ub(fb, _A, None) == B.MOE_ERR_ARG
     assert ub(plain, None, None) == B.MOE_ERR_ARG  # dXe NULL
-    rb = lambda cfg, g, dO: B.lib.moe_route_bwd(
-        ctypes.byref(cfg), _A, _A, _A, _A, _A, None, g, dO, _A, _A, _A, _A, None, _A, 10, None)
-    assert rb(fb, None, _A) == B.MOE_ERR_ARG and rb(fb, _A, None) == B.MOE_ERR_ARG
-    assert rb(fb, _A, _A) == B.MOE_ERR_WORKSPACE
-    assert rb(plain, None, None) == B.MOE_ERR_WORKSPACE
+    # the router backward takes the finished unpermute-sum: no fallback inputs
+    rb = lambda cfg, dxe: B.lib.moe_route_bwd(
+        ctypes.byref(cfg), _A, _A, _A, _A, _A, None, _A, dxe, _A, _A, None, _A, 10, None)
+    assert rb(fb, None) == B.MOE_ERR_ARG and rb(plain, None) == B.MOE_ERR_ARG
+    assert rb(fb, _A + 4) == B.MOE_ERR_ALIGN
+    assert rb(fb, _A) == B.MOE_ERR_WORKSPACE
+    assert rb(plain, _A) == B.MOE_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("coeff", [-0.01, float("nan"), float("inf")])
@@ -291,8 +301,7 @@ def test_balancing_entry_points_validate_arguments():
     assert aux(ctypes.byref(c), _A, _A, _A, _A, _A, 10, None) == B.MOE_ERR_WORKSPACE
     # the router backward needs counts only when the loss is on
     rb = lambda cfg, counts: B.lib.moe_route_bwd(
-        ctypes.byref(cfg), _A, _A, _A, _A, _A, counts, None, None, _A, _A, _A, _A, None, _A,
-        10, None)
+        ctypes.byref(cfg), _A, _A, _A, _A, _A, counts, _A, _A, _A, _A, None, _A, 10, None)
     assert rb(c, None) == B.MOE_ERR_ARG
     assert rb(c, _A) == B.MOE_ERR_WORKSPACE
     c.aux_coeff = 0.0
