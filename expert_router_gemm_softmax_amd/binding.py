@@ -62,6 +62,10 @@ class MoeCfg(ctypes.Structure):
                 ("route_margin", c_float), ("flags", c_uint32), ("aux_coeff", c_float),
                 ("probe", c_void_p)]
 
+    def __copy__(self):
+        # ctypes cannot pickle a structure holding a pointer: copy field by field
+        return MoeCfg(**{n: getattr(self, n) for n, _ in self._fields_})
+
     def __repr__(self):
         return (f"MoeCfg(T={self.T}, d={self.d}, E={self.E}, k={self.k}, f={self.f}, "
                 f"dtype={self.dtype}, capacity={self.capacity}, aux_coeff={self.aux_coeff})")

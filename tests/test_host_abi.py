@@ -217,6 +217,16 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert B.lib.moe_check_cfg(ctypes.byref(c)) == B.MOE_OK
 
 
+def test_cfg_copies_field_by_field():
+    import copy
+    c = M.make_cfg(16, 64, 8, 2, 64, "bf16", capacity=5, aux_coeff=0.5)
+    probe = B.MoeProbe(kernel_id=1, capacity=0, count=0)
+    c.probe = ctypes.addressof(probe)
+    c2 = copy.copy(c)
+    c2.aux_coeff = 1.0
+    assert c.aux_coeff == 0.5 and c2.capacity == 5 and c2.probe == c.probe
+
+
 def test_status_strings():
     for st in range(-7, 1):
         assert M.status_str(st) and M.status_str(st) != "unknown status"
