@@ -1,8 +1,8 @@
 """Loader of the hand-worked fixtures under tests/golden/.
 
 A fixture holds the inputs of a tiny case and its expected outputs, each
-written as an arithmetic expression (numbers, + - * /, and the symbols the
-fixture defines, e.g. s2 = 1/(1+exp(-2))).  The expressions were derived by
+written as an arithmetic expression (numbers, + - * /, exp, tanh, and the
+symbols the fixture defines, e.g. s2 = 1/(1+exp(-2))).  The expressions were derived by
 hand; this module only evaluates them, with a parser that admits nothing
 but that arithmetic.
 """
@@ -21,7 +21,7 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 _BIN = {ast.Add: operator.add, ast.Sub: operator.sub, ast.Mult: operator.mul,
         ast.Div: operator.truediv}
 _UN = {ast.USub: operator.neg, ast.UAdd: operator.pos}
-_FUN = {"exp": math.exp}
+_FUN = {"exp": math.exp, "tanh": math.tanh}
 
 
 def _eval(node, env):
@@ -51,6 +51,19 @@ def _values(v, env):
     if isinstance(v, str):
         return evaluate(v, env)
     return v
+
+
+def symbols(fx):
+    """The fixture's symbols, evaluated in order (later ones may use earlier)."""
+    env = {}
+    for sym, expr in fx.get("symbols", {}).items():
+        env[sym] = evaluate(expr, env)
+    return env
+
+
+def load_raw(name: str):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
 
 
 def load(name: str):

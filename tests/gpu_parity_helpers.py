@@ -14,22 +14,47 @@ TOL = {  # (rtol, atol), numpy allclose semantics |g - o| <= atol + rtol |o|
     "f32": (1e-5, 1e-5),
     "prob": (1e-5, 1e-6),      # probs / gates: fp32 quantities from near-equal logits
 }
-# Outputs that are sums over the token (row) axis -- dW1, dW2, dWr, db,
-# dgate -- of products whose operands were rounded to the storage type
-# upstream: two correct implementations that round at the same points still
-# flip single upstream roundings (fp32 vs fp64 accumulation before the
-# rounding), and a flipped operand moves its summand a_i b_i by at most one
-# unit in the last place, u |a_i b_i| (u = 2^-7 for bf16's 8 significant
-# bits, 2^-23 for fp32).  Independent flips of a fraction rho of the n
-# summands move the sum by ~u sqrt(rho) ||(a_i b_i)_i||_2, and a single flip
-# by at most u max_i |a_i b_i| <= u ||(a_i b_i)_i||_2.  The absolute
-# tolerance of such an output element is therefore
-#     max(atol, 2 u ||(a_i b_i)_i||_2),
-# with ||(a_i b_i)_i||_2 = sqrt((a*a)^T (b*b)) computed from the oracle's own
-# operands (factor 2: several flips).  When the summands are not at hand
-# the rms of the sum stands in for their norm (random-sign sums:
-# rms(sum) ~ ||(a_i b_i)||_2 for a typical element).
+# Four outputs are sums over the token (row) axis of products whose
+# operands were rounded to the storage type upstream: dW1 = x_perm^T dA,
+# dW2 = H^T dYp (per expert), dgate = <dOut, Y> and dWr = x^T dz.  Two
+# correct implementations that round at the same points still flip single
+# upstream roundings (fp32 versus fp64 accumulation before the rounding),
+# and a flipped operand moves its summand a_i b_i by at most one unit in the
+# last place, u |a_i b_i| (u = 2^-7 for bf16's 8 significant bits, 2^-23 for
+# fp32), so one flip moves the sum by at most u ||(a_i b_i)_i||_2.  Where
+# the sum cancels, that exceeds rtol |sum| + atol: tests/test_tolerance_needed.py
+# shows on the CPU that an fp32-accumulating implementation rounding at the
+# oracle's storage points exceeds the stated bound for exactly these four
+# outputs (up to 4.5x, dW2 on the expert-share workload's small experts) and
+# needs at most 0.76 u ||.||_2 (dW1, dW2) and 0.13 u ||.||_2 (dgate, dWr)
+# beyond rtol |sum|.  Their absolute tolerance is therefore
+#     max(atol, RED_C[name] u ||(a_i b_i)_i||_2)
+# with ||(a_i b_i)_i||_2 = sqrt((a*a)^T (b*b)) from the oracle's own
+# operands: two flips' worth for the expert weight gradients, one for dgate
+# and dWr.  Every other output, db included, is held to the stated bound.
 RED_UNIT = {"bf16": 2.0 ** -7, "f32": 2.0 ** -23}
+RED_C = {"dW1": 2.0, "dW2": 2.0, "dgate": 1.0, "dWr": 1.0}
+
+# max |gpu - oracle| / (atol + rtol |oracle|) at the stated tolerance, per
+# (case, output): printed by the tests and written to the file named by
+# $MOE_PARITY_REPORT at the end of the session (tests/conftest.py)
+RATIOS = {}
+CASE = ["?"]
+
+
+def set_case(name):
+    CASE[0] = name
+
+
+def record_ratio(name, got, ref, dtype):
+    rtol, atol = TOL[dtype]
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    r = float(np.max(np.abs(got - ref) / (atol + rtol * np.abs(ref))))
+    RATIOS[f"{CASE[0]}:{name}"] = r
+    return r
 
 
 def term_norm(a, b):
@@ -40,10 +65,11 @@ def term_norm(a, b):
     return np.sqrt((a * a).T @ (b * b))
 
 
-def terms_tol(norm, dtype):
-    """(rtol, atol array) for a sum whose summand norms are `norm`."""
+def terms_tol(norm, dtype, name):
+    """(rtol, atol array) for the sum output `name` whose summand norms are
+    `norm`."""
     rtol, atol = TOL[dtype]
-    return rtol, np.maximum(atol, 2.0 * RED_UNIT[dtype] * np.asarray(norm, np.float64))
+    return rtol, np.maximum(atol, RED_C[name] * RED_UNIT[dtype] * np.asarray(norm, np.float64))
 
 
 def say(*a):
@@ -82,30 +108,27 @@ def cfg_of(M, w, route_margin=0.0, recompute=False):
                       renorm=w.renorm, priority=w.priority, fallback=w.fallback)
 
 
-def red_tol(ref, dtype):
-    """(rtol, atol) for a sum over the token axis whose summands are not at
-    hand: the rms of the oracle output stands in for the summand norm."""
-    rtol, atol = TOL[dtype]
-    ref = np.asarray(ref, np.float64)
-    if ref.size == 0:
-        return rtol, atol
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    return rtol, max(atol, 2.0 * RED_UNIT[dtype] * rms)
-
-
-def expert_grad_tols(fw, bw, dtype):
-    """Per-element tolerances of dW1 and dW2 from the oracle's operands:
-    dW1[e] = x_e^T dA_e, dW2[e] = H_e^T dYp_e over the expert's rows."""
+def check_expert_grads(dW1, dW2, fw, bw, dtype):
+    """dW1 and dW2 (device tensors [E, ...]) against the oracle expert by
+    expert, each with its summand-norm tolerance; the ratio at the stated
+    tolerance is recorded as the maximum over experts.  Empty experts must
+    be exactly zero."""
     off = fw["offsets"]
-    E = len(off) - 1
-    n1 = np.zeros(bw["dW1"].shape)
-    n2 = np.zeros(bw["dW2"].shape)
-    for e in range(E):
+    worst = {"dW1": 0.0, "dW2": 0.0}
+    for e in range(len(off) - 1):
         lo, hi = int(off[e]), int(off[e + 1])
-        if hi > lo:
-            n1[e] = term_norm(fw["x_perm"][lo:hi], bw["dA"][lo:hi])
-            n2[e] = term_norm(fw["H"][lo:hi], bw["dYp"][lo:hi])
-    return terms_tol(n1, dtype), terms_tol(n2, dtype)
+        for name, got_t, ref, a, b in (("dW1", dW1, bw["dW1"], fw["x_perm"], bw["dA"]),
+                                       ("dW2", dW2, bw["dW2"], fw["H"], bw["dYp"])):
+            got = to_f64(got_t[e])
+            if hi == lo:
+                assert np.all(got == 0), f"{name}[e={e}] of an empty expert is not zero"
+                continue
+            r = record_ratio(name, got, ref[e], dtype)
+            worst[name] = max(worst[name], r)
+            assert_close(f"{name}[e={e}]", got, ref[e],
+                         terms_tol(term_norm(a[lo:hi], b[lo:hi]), dtype, name))
+    for name, r in worst.items():
+        RATIOS[f"{CASE[0]}:{name}"] = r
 
 
 def assert_close(name, got, ref, tol):
@@ -115,6 +138,8 @@ def assert_close(name, got, ref, tol):
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     if got.size == 0:
         return
+    if isinstance(tol, str) and tol in ("bf16", "f32"):
+        record_ratio(name, got, ref, tol)
     err = np.abs(got - ref)
     bad = err > atol + rtol * np.abs(ref)
     if bad.any():
@@ -123,6 +148,13 @@ def assert_close(name, got, ref, tol):
         raise AssertionError(
             f"{name}: {int(bad.sum())}/{bad.size} elements outside rtol={rtol} "
             f"atol={at}; worst at {i}: gpu={got[i]!r} oracle={ref[i]!r}")
+
+
+def assert_close_sum(name, got, ref, norm, dtype):
+    """A sum-over-rows output (dW1, dW2, dgate, dWr): its ratio at the stated
+    tolerance is recorded, then it is checked against the summand-norm bound."""
+    record_ratio(name, got, ref, dtype)
+    assert_close(name, got, ref, terms_tol(norm, dtype, name.split("[")[0]))
 
 
 def run_layer(M, w, inp, route_margin=0.0, bwd=True, recompute=False):
@@ -212,12 +244,9 @@ def check_layer_full(res, fw, bw, w, check_bwd=True):
         assert_close("dX", to_f64(res["dX"]), bw["dX"], tol)
         dz = bw["dz"]
         x = fw["x"]
-        assert_close("dWr", to_f64(res["dWr"]), bw["dWr"], terms_tol(term_norm(x, dz), tol))
-        assert_close("db", to_f64(res["db"]), bw["db"],
-                     terms_tol(np.sqrt((dz * dz).sum(axis=0)), tol))
-        t1, t2 = expert_grad_tols(fw, bw, tol)
-        assert_close("dW1", to_f64(res["dW1"]), bw["dW1"], t1)
-        assert_close("dW2", to_f64(res["dW2"]), bw["dW2"], t2)
+        assert_close_sum("dWr", to_f64(res["dWr"]), bw["dWr"], term_norm(x, dz), tol)
+        assert_close("db", to_f64(res["db"]), bw["db"], tol)
+        check_expert_grads(res["dW1"], res["dW2"], fw, bw, tol)
     return R
 
 

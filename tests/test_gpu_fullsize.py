@@ -1,22 +1,19 @@
 """GPU parity at the full sizes of the named workloads (c2_zipf, c3_epshare,
-c4_large), in the launch configuration bench.py times.
-
-c2_zipf and c3_epshare are compared against the full oracle.  c4_large is
-too large for a full CPU backward: routing is compared in full (bit-exact),
-the forward activations and the output of every expert are compared in
-full by streaming the oracle expert by expert, the router gradients (dWr,
-db) in full from the oracle's gate gradients, dX on sampled tokens and the
-expert weight gradients on sampled experts.
+c4_large), in the launch configuration bench.py times, every output against
+the full oracle: routing bit-exact, every activation, the output, and every
+gradient (dX of every token, dW1 and dW2 of every expert -- zero for the
+empty ones -- dWr, db, dgate) element by element.  The c4_large oracle
+(about 10 TFLOP in fp64 and some 40 GB of host memory) takes a few minutes.
 """
 import numpy as np
 import pytest
 
 import oracle as O
 import workloads as W
-from gpu_parity_helpers import (assert_close, check_aux, check_gate_formula,
-                                check_layer_full, check_routing_exact,
-                                expert_grad_tols, logit_error, run_layer, say, term_norm,
-                                terms_tol, to_dev, to_f64, to_int)
+from gpu_parity_helpers import (RATIOS, assert_close, assert_close_sum,
+                                check_expert_grads, check_gate_formula, check_layer_full,
+                                check_routing_exact, logit_error, run_layer, say, to_dev,
+                                to_f64)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -77,10 +74,10 @@ def test_c3_epshare_full(M):
     dOut = O.to_f64(inp["dOut"])
     rows = inp["row_of"][:, 0]
     gn = np.sqrt(((dOut * fw["Y"][rows]) ** 2).sum(axis=1))[:, None]
-    assert_close("dgate", to_f64(dg), bw["dgate"], terms_tol(gn, "bf16"))
-    t1, t2 = expert_grad_tols(fw, bw, "bf16")
-    assert_close("dW1", to_f64(dW1), bw["dW1"], t1)
-    assert_close("dW2", to_f64(dW2), bw["dW2"], t2)
+    assert_close_sum("dgate", to_f64(dg), bw["dgate"], gn, "bf16")
+    check_expert_grads(dW1, dW2, fw, bw, "bf16")
+    say("C3 stated-tolerance ratios",
+        {k.split(":")[1]: round(v, 3) for k, v in RATIOS.items() if "c3" in k})
 
 
 def test_c4_routing_variants(M):
@@ -99,93 +96,33 @@ def test_c4_routing_variants(M):
 
 
 def test_c4_large(M):
+    """Every output of the c4_large layer against the oracle's own forward
+    and backward (layer_fwd, layer_bwd), element by element."""
+    import torch
     w = W.get("C4")
     inp = W.make_inputs(w, seed=0)
     say("C4 inputs ready")
     res = run_layer(M, w, inp)
+    # bring every result to the host and free the device copies
+    got = {}
+    for key in ("idx", "counts", "offsets", "row_of", "src_of", "probs", "gate", "aux1"):
+        got[key] = res[key]
+    for key in ("x_perm", "A", "H", "Y", "out", "dX", "dWr", "db", "dW1", "dW2"):
+        got[key] = torch.empty(res[key].shape, dtype=res[key].dtype).copy_(res[key])
+    del res
+    torch.cuda.empty_cache()
     say("C4 GPU layer done")
-    rnd = O.rounder("bf16")
-    r32 = O.rounder("f32")
-    fw = O.route(inp, w)
-    R = check_routing_exact(res, fw, w)
-    err = logit_error(res, fw)
-    say(f"C4 routing bit-exact: R={R} dropped={w.T * w.k - R} C={fw['C']} logit err={err:.3g}")
+    fw = O.layer_fwd(inp, w)
+    say("C4 oracle forward done")
+    bw = O.layer_bwd(inp, w, fw)
+    say("C4 oracle backward done")
+    R = check_layer_full(got, fw, bw, w)
+    err = logit_error(got, fw)
+    empty = int(np.sum(np.diff(fw["offsets"]) == 0))
+    say(f"C4 full layer: R={R} dropped={w.T * w.k - R} C={fw['C']} logit err={err:.3g}, "
+        f"{empty} empty experts; stated-tolerance ratios",
+        {k.split(":")[1]: round(v, 3) for k, v in RATIOS.items() if "c4_large" in k})
     assert err <= TAU / 2
-    assert_close("probs", to_f64(res["probs"]), fw["probs"], "prob")
-    assert_close("gate", to_f64(res["gate"]), fw["gate"], "prob")
-    check_aux("aux1", res["aux1"], res["probs"], fw, w, 1.0)
-    say(f"C4 balancing loss (coefficient 1) {float(to_f64(res['aux1'])[0]):.6f}, "
-        f"drop rate {float(to_f64(res['aux1'])[1]):.6f}")
-
-    off, src, k = fw["offsets"], fw["src_of"], w.k
-    x = fw["x"]
-    dOut = O.to_f64(inp["dOut"])
-    gpu = {n: res[n] for n in ("A", "H", "Y", "x_perm")}
-    dg = np.zeros((w.T, k))
-    out_acc = np.zeros((w.T, w.d))
-    keep = {}
-    e_sorted = np.argsort(np.diff(off))
-    sample_e = sorted({int(e_sorted[-1]), int(e_sorted[len(e_sorted) // 2]),
-                       int(e_sorted[0])})
-    for e in range(w.E):
-        lo, hi = int(off[e]), int(off[e + 1])
-        if hi == lo:
-            continue
-        xe = x[src[lo:hi] // k]
-        A, H, Y = O.expert_ffn_fwd(xe, O.to_f64(inp["W1"][e]), O.to_f64(inp["W2"][e]), rnd)
-        for name, ref in (("A", A), ("H", H), ("Y", Y)):
-            assert_close(f"{name}[e={e}]", to_f64(gpu[name][lo:hi]), ref, "bf16")
-        t = src[lo:hi] // k
-        j = src[lo:hi] % k
-        dg[t, j] = np.einsum("rd,rd->r", dOut[t], Y)
-        np.add.at(out_acc, t, fw["gate"][t, j][:, None] * Y)
-        if e in sample_e:
-            keep[e] = (xe, A, H, Y)
-    say("C4 forward activations match for every expert")
-    # out: the oracle's combine sums j in ascending order; this sum runs
-    # expert by expert (fp64, one rounding), well inside the bf16 tolerance
-    assert_close("out", to_f64(res["out"]), rnd(out_acc), "bf16")
-    dg = r32(dg)
-    dz = O.router_dz(fw["probs"], fw["idx"], fw["row_of"], dg)
-    db = r32(dz.sum(axis=0))
-    dWr = rnd(x.T @ dz)
-    assert_close("dWr", to_f64(res["dWr"]), dWr, terms_tol(term_norm(x, dz), "bf16"))
-    assert_close("db", to_f64(res["db"]), db, terms_tol(np.sqrt((dz * dz).sum(axis=0)), "bf16"))
-    say("C4 router gradients match")
-    # dX on sampled tokens: per-row backward of each kept assignment
-    rng = np.random.default_rng(1)
-    toks = np.sort(rng.choice(w.T, 48, replace=False))
-    dX_ref = np.zeros((len(toks), w.d))
-    for n, t in enumerate(toks):
-        acc = np.zeros(w.d)
-        for jj in range(k):
-            r = int(fw["row_of"][t, jj])
-            if r < 0:
-                continue
-            e = int(np.searchsorted(off, r, side="right") - 1)
-            W1e, W2e = O.to_f64(inp["W1"][e]), O.to_f64(inp["W2"][e])
-            A_r, _, _ = O.expert_ffn_fwd(x[t][None], W1e, W2e, rnd)
-            dYp_r = rnd(fw["gate"][t, jj] * dOut[t][None])
-            dA_r = rnd((dYp_r @ W2e.T) * O.gelu_tanh_grad(A_r))
-            acc += rnd(dA_r @ W1e.T)[0]
-        dX_ref[n] = rnd(r32(acc) + dz[t] @ O.to_f64(inp["Wr"]).T)
-    assert_close("dX[sampled]", to_f64(res["dX"])[toks], dX_ref, "bf16")
-    # expert weight gradients on the sampled experts (full expert backward)
-    for e, (xe, A, H, Y) in keep.items():
-        lo, hi = int(off[e]), int(off[e + 1])
-        t = src[lo:hi] // k
-        j = src[lo:hi] % k
-        dYe = rnd(fw["gate"][t, j][:, None] * dOut[t])
-        _, dW1, dW2, dA = O.expert_ffn_bwd(xe, O.to_f64(inp["W1"][e]),
-                                           O.to_f64(inp["W2"][e]), A, H, dYe, rnd)
-        assert_close(f"dW1[e={e}]", to_f64(res["dW1"][e]), dW1,
-                     terms_tol(term_norm(xe, dA), "bf16"))
-        assert_close(f"dW2[e={e}]", to_f64(res["dW2"][e]), dW2,
-                     terms_tol(term_norm(H, dYe), "bf16"))
-    say(f"C4 dX (sampled) and dW1/dW2 of experts {sorted(keep)} match")
-    empty = np.nonzero(np.diff(off) == 0)[0]
-    for e in empty[:4]:
-        assert np.all(to_f64(res["dW1"][int(e)]) == 0)
 
 
 def test_c4_recompute_mode_is_bitwise_the_save_mode(M):

@@ -3,16 +3,20 @@
 Integer routing outputs (idx, counts, offsets, row_of, src_of) must be
 bit-exact and x_perm bitwise; float outputs within the stated tolerances:
 bf16 configs rtol 2e-2 / atol 1e-2, fp32 configs 1e-5 / 1e-5, router
-probabilities and gates 1e-5 / 1e-6 in every config.
+probabilities and gates 1e-5 / 1e-6 in every config.  The four sums over
+rows whose stated bound no correct fp32-accumulating implementation meets
+(dW1, dW2, dgate, dWr; see tests/test_tolerance_needed.py) take a
+summand-norm absolute tolerance instead (gpu_parity_helpers.RED_C).
 """
 import numpy as np
 import pytest
 
 import oracle as O
 import workloads as W
-from gpu_parity_helpers import (TOL, assert_close, cfg_of, check_aux, check_layer_full,
+from gpu_parity_helpers import (TOL, assert_close, assert_close_sum, cfg_of, check_aux,
+                                check_layer_full,
                                 check_routing_exact, logit_error, make_case,
-                                run_layer, say, terms_tol, to_dev, to_f64, to_int)
+                                run_layer, say, to_dev, to_f64, to_int)
 
 pytestmark = pytest.mark.gpu
 
@@ -349,7 +353,7 @@ def test_step_entry_points_equal_the_layer_entry_points(M, mode):
         gn[m, j] = np.sqrt(((dOut[m] * fw["Y"][fw["row_of"][m, j]]) ** 2).sum(axis=1))
         if w.fallback == "identity":   # dropped: <dOut, x>
             gn[~m, j] = np.sqrt(((dOut[~m] * fw["x"][~m]) ** 2).sum(axis=1))
-    assert_close("dgate", to_f64(dg), bw["dgate"], terms_tol(gn, "bf16"))
+    assert_close_sum("dgate", to_f64(dg), bw["dgate"], gn, "bf16")
 
 
 RECOMPUTE_CASES = [
