@@ -15,12 +15,17 @@
 //        reduction runs over a ragged K = m_e (H^T dYp, x_perm^T dA).
 //        Experts with m_e = 0 get a zero matrix.
 //
-// bf16 kernel (gfx950): v_mfma_f32_32x32x16_bf16, block tile BM x BN x 64,
-// 4 waves in 2 x 2, LDS double buffer of K-contiguous tiles with an XOR
-// swizzle; operands stored MN-contiguous in HBM are transposed in
-// registers on their way into LDS.  Tiles are ordered so that the blocks
-// resident on one XCD (block id mod 8) work on a compact group of output
-// tiles, which keeps their operand panels in that XCD's L2.
+// bf16 kernel (gfx950): v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
+// block tile 256 x 256 or 128 x 128 (4 waves in 2 x 2), K tiles of 32 held
+// in a ring of 4 (256 x 256) or 3 LDS stages filled straight from HBM by
+// global_load_lds_dwordx4.  Operands keep their HBM orientation in LDS:
+// K-contiguous tiles with an XOR swizzle, read as 16-byte fragments;
+// M/N-contiguous tiles read with the transposing ds_read_b64_tr_b16.  Tiles
+// are ordered so that the blocks resident on one XCD (block id mod 8) work
+// on a compact group of output tiles, which keeps their operand panels in
+// that XCD's L2; the last, partial round of row-GEMM tiles is split along K
+// and summed by a fixup kernel in part order.  The epilogue is staged
+// through LDS for 16-byte row stores.
 #include "gemm.h"
 
 namespace moe {
