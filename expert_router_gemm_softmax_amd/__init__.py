@@ -13,7 +13,8 @@ from .binding import (KERNELS, KernelProbe, MOE_BF16, MOE_FLAG_DROP_IDENTITY, MO
                       MoeError, MoeGrads, MoeLibraryError, MoeWeights, LIB_PATH,
                       make_cfg, moe_capacity, moe_check_cfg, moe_combine,
                       moe_combine_bwd, moe_grouped_ffn, moe_grouped_ffn_bwd,
-                      moe_layer_bwd, moe_layer_fwd, moe_permute, moe_route, moe_route_bwd, moe_router_aux,
+                      moe_layer_bwd, moe_layer_fwd, moe_permute, moe_permute_noalloc,
+                      moe_route, moe_route_bwd, moe_router_aux,
                       moe_rows_max,
                       moe_unpermute_bwd, moe_workspace_bytes, status_str)
 from .layer import MoeLayer

@@ -96,6 +96,7 @@ _SIGS = {
     "moe_last_error": (c_char_p, []),
     "moe_route": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_permute": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "moe_permute_noalloc": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_ffn": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_combine": (c_int, [_CFG, _P, _P, _P, _P, _P, _P]),
     "moe_combine_bwd": (c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -241,6 +242,12 @@ def moe_permute(cfg, x, idx, counts, offsets, row_of, src_of, x_perm, ws, stream
     _check("moe_permute", lib.moe_permute(
         byref(cfg), _ptr(x), _ptr(idx), _ptr(counts), _ptr(offsets), _ptr(row_of),
         _ptr(src_of), _ptr(x_perm), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_permute_noalloc(cfg, x, idx, counts, offsets, row_of, src_of, x_perm, stream=None):
+    _check("moe_permute_noalloc", lib.moe_permute_noalloc(
+        byref(cfg), _ptr(x), _ptr(idx), _ptr(counts), _ptr(offsets), _ptr(row_of),
+        _ptr(src_of), _ptr(x_perm), _stream(stream)))
 
 
 def moe_grouped_ffn(cfg, x_perm, offsets, W1, W2, A, H, Y, ws, stream=None):

@@ -213,6 +213,30 @@ int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx, int32_t* 
   return launch_permute(c, x, idx, counts, offsets, row_of, src_of, x_perm, ws, S(stream));
 }
 
+int moe_permute_noalloc(const moe_cfg* cfg, const void* x, const int32_t* idx,
+                        int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_of,
+                        void* x_perm, moe_stream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_cfg& c = *cfg;
+  const Sizes z = sizes(c);
+  MOE_TRY(need(x, z.Td, 16));
+  MOE_TRY(need(idx, z.Tk, 4));
+  MOE_TRY(need(counts, (size_t)c.E * 4, 4));
+  MOE_TRY(need(offsets, z.E1, 4));
+  MOE_TRY(need(row_of, z.Tk, 4));
+  MOE_TRY(need(src_of, z.Rmax * 4, 4));
+  MOE_TRY(need(x_perm, z.Rd, 16));
+  clear_stale_error();
+  if (permute_noalloc_scratch_bytes(c) > permute_noalloc_scratch_max()) {
+    snprintf(g_last_error, sizeof g_last_error,
+             "moe_permute_noalloc: %zu bytes of scratch needed, %zu available",
+             permute_noalloc_scratch_bytes(c), permute_noalloc_scratch_max());
+    return MOE_ERR_WORKSPACE;
+  }
+  return launch_permute_noalloc(c, x, idx, counts, offsets, row_of, src_of, x_perm,
+                                S(stream));
+}
+
 int moe_grouped_ffn(const moe_cfg* cfg, const void* x_perm, const int32_t* offsets,
                     const void* W1, const void* W2, void* A, void* H, void* Y, void* ws,
                     size_t ws_bytes, moe_stream_t stream) {

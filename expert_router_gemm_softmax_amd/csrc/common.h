@@ -316,6 +316,14 @@ int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
                    int32_t* counts, int32_t* offsets, int32_t* row_of,
                    int32_t* src_of, void* x_perm, void* ws, hipStream_t s,
                    int32_t* tiles = nullptr);
+// the same with its scratch (per-block histograms) in a fixed device array
+// of permute_noalloc_scratch_max() bytes; MOE_ERR_WORKSPACE when the cfg
+// needs more
+size_t permute_noalloc_scratch_bytes(const moe_cfg& c);
+size_t permute_noalloc_scratch_max();
+int launch_permute_noalloc(const moe_cfg& c, const void* x, const int32_t* idx,
+                           int32_t* counts, int32_t* offsets, int32_t* row_of,
+                           int32_t* src_of, void* x_perm, hipStream_t s);
 // have_tiles: the workspace already holds the M-tile prefix for offsets
 // (written by the permute or the combine backward), so no schedule kernel
 int launch_ffn_fwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,

@@ -11,9 +11,19 @@
 // Determinism: atomics are used only to count (order-independent) and to
 // OR lane bits into 64-bit LDS masks; every position comes from scans and
 // popcounts in token order.
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
+
+// Scratch of moe_permute_noalloc: the per-block expert histograms, in a
+// fixed device array instead of the caller's workspace.  Host code must
+// not use the array's name as a device address: its address on each device
+// comes from hipGetSymbolAddress (noalloc_scratch below).
+constexpr size_t kNoallocScratchInts = (size_t)1 << 20;  // 4 MiB
+static __device__ __align__(256) int32_t scratch[kNoallocScratchInts];
+
 namespace {
 
 constexpr int kPW = kPermTokens / kWave;  // waves per permute block
@@ -189,11 +199,11 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(
 
 }  // namespace
 
-int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
-                   int32_t* counts, int32_t* offsets, int32_t* row_of,
-                   int32_t* src_of, void* x_perm, void* ws, hipStream_t s, int32_t* tiles) {
-  const WsLayout L = ws_layout(c);
-  int32_t* blk = ws_ptr<int32_t>(ws, L.perm_blk);
+namespace {
+
+int permute_with(const moe_cfg& c, const void* x, const int32_t* idx, int32_t* counts,
+                 int32_t* offsets, int32_t* row_of, int32_t* src_of, void* x_perm,
+                 int32_t* blk, hipStream_t s, int32_t* tiles) {
   Walk wk;
   wk.T = c.T;
   wk.k = c.k;
@@ -225,6 +235,63 @@ int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
                      c.T, c.d, c.k));
   }
   return MOE_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device and kept (the array lives as long as the process)
+constexpr int kMaxDevices = 64;
+int32_t* g_scratch[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+int noalloc_scratch(int32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    note_launch_error(MOE_KERNEL_PERMUTE_COUNT, e);
+    return MOE_ERR_LAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNIMPLEMENTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      note_launch_error(MOE_KERNEL_PERMUTE_COUNT, e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return MOE_ERR_LAUNCH;
+    }
+    g_scratch[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+int launch_permute(const moe_cfg& c, const void* x, const int32_t* idx,
+                   int32_t* counts, int32_t* offsets, int32_t* row_of,
+                   int32_t* src_of, void* x_perm, void* ws, hipStream_t s, int32_t* tiles) {
+  const WsLayout L = ws_layout(c);
+  return permute_with(c, x, idx, counts, offsets, row_of, src_of, x_perm,
+                      ws_ptr<int32_t>(ws, L.perm_blk), s, tiles);
+}
+
+size_t permute_noalloc_scratch_bytes(const moe_cfg& c) {
+  return (size_t)ws_layout(c).nblk_perm * c.E * 4;
+}
+
+size_t permute_noalloc_scratch_max() { return kNoallocScratchInts * 4; }
+
+int launch_permute_noalloc(const moe_cfg& c, const void* x, const int32_t* idx,
+                           int32_t* counts, int32_t* offsets, int32_t* row_of,
+                           int32_t* src_of, void* x_perm, hipStream_t s) {
+  if (permute_noalloc_scratch_bytes(c) > permute_noalloc_scratch_max())
+    return MOE_ERR_WORKSPACE;
+  int32_t* blk = nullptr;
+  const int rc = noalloc_scratch(&blk);
+  if (rc != MOE_OK) return rc;
+  // every histogram entry is written by the count kernel before it is read:
+  // nothing left by an earlier call needs clearing
+  return permute_with(c, x, idx, counts, offsets, row_of, src_of, x_perm, blk, s, nullptr);
 }
 
 }  // namespace moe

@@ -205,6 +205,23 @@ MOE_API int moe_permute(const moe_cfg* cfg, const void* x, const int32_t* idx,
                 int32_t* src_of, void* x_perm, void* ws, size_t ws_bytes,
                 moe_stream_t stream);
 
+/* moe_permute for callers that cannot allocate device memory -- code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc: the same kernels and results as moe_permute (bitwise), with
+ * no workspace argument.  Its scratch (the per-block expert histograms,
+ * ceil(T'/256) * E * 4 bytes with T' = T, or T*k under
+ * MOE_FLAG_SLOT_PRIORITY) lives in a fixed 4 MiB device array that each
+ * GPU the library runs on holds until the process ends; a cfg needing more
+ * returns MOE_ERR_WORKSPACE (moe_last_error gives both sizes) before
+ * anything is enqueued.  It never calls hipMalloc or hipFree.  The array is
+ * the current device's, and every call on one GPU shares it: calls that
+ * overlap on one GPU (different streams, or threads) race and must be
+ * ordered by the caller.  Every entry is written before it is read, so a
+ * call needs nothing cleared from the previous one. */
+MOE_API int moe_permute_noalloc(const moe_cfg* cfg, const void* x, const int32_t* idx,
+                int32_t* counts, int32_t* offsets, int32_t* row_of,
+                int32_t* src_of, void* x_perm, moe_stream_t stream);
+
 /* F3+F4 grouped expert FFN over the ragged per-expert segments
  * [offsets[e], offsets[e+1]) of x_perm: every local expert runs on the rows
  * routed to it, as one grouped GEMM rather than one small GEMM per expert

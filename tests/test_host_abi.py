@@ -217,6 +217,17 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert B.lib.moe_check_cfg(ctypes.byref(c)) == B.MOE_OK
 
 
+def test_noalloc_permute_validates_before_anything_else():
+    # argument checks and the scratch-size check need no GPU
+    c = M.make_cfg(1000, 64, 16, 2, 64, "bf16", capacity=None)
+    f = B.lib.moe_permute_noalloc
+    assert f(ctypes.byref(c), None, _A, _A, _A, _A, _A, _A, None) == B.MOE_ERR_ARG
+    assert f(ctypes.byref(c), _A + 2, _A, _A, _A, _A, _A, _A, None) == B.MOE_ERR_ALIGN
+    big = M.make_cfg(2 ** 22, 64, 256, 2, 64, "bf16", capacity=None)
+    assert f(ctypes.byref(big), _A, _A, _A, _A, _A, _A, _A, None) == B.MOE_ERR_WORKSPACE
+    assert b"4194304 available" in B.lib.moe_last_error()
+
+
 def test_cfg_copies_field_by_field():
     import copy
     c = M.make_cfg(16, 64, 8, 2, 64, "bf16", capacity=5, aux_coeff=0.5)
