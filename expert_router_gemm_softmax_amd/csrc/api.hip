@@ -446,10 +446,12 @@ int moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const void* x, const
   void* dYp = ws_ptr<void>(ws, L.dYp);
   void* dXp = ws_ptr<void>(ws, L.dXp);
   clear_stale_error();
-  // the combine backward also writes the grouped GEMMs' tile schedule
+  // the combine backward also writes the grouped GEMMs' tile schedule and
+  // the weight-gradient split plan
   int32_t* tiles = ws_ptr<int32_t>(ws, L.tiles);
+  int32_t* plan = c.dtype == MOE_BF16 ? ws_ptr<int32_t>(ws, L.kplan) : nullptr;
   MOE_TRY(launch_combine_bwd(c, dOut, ctx->Y, ctx->row_of, ctx->gate, x, dYp, dgate, s,
-                             ctx->offsets, tiles));
+                             ctx->offsets, tiles, plan));
   MOE_TRY(launch_ffn_bwd(c, ctx->x_perm, ctx->offsets, w->W1, w->W2, ctx->A, ctx->H, dYp,
                          dXp, g->dW1, g->dW2, ws, s, /*have_tiles=*/true));
   // the unpermute-sum of dXp is fused into the router's dX

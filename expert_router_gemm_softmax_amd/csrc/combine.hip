@@ -181,17 +181,28 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const T* __restrict__ dOut, const T* __restrict__ Y, const int32_t* __restrict__ row_of,
     const float* __restrict__ gate, const T* __restrict__ x, T* __restrict__ dYp,
     float* __restrict__ dgate, int64_t T_, int d, int k, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ tiles, int E, int BM) {
+    int32_t* __restrict__ tiles, int E, int BM, int32_t* __restrict__ plan, int te) {
   constexpr int V = St<T>::kVec;
-  if (blockIdx.x == 0 && tiles != nullptr) {  // the grouped GEMMs' M-tile prefix
-    __shared__ int s_wave[4];
-    const int e = threadIdx.x;
-    block_tile_prefix(e < E ? offsets[e + 1] - offsets[e] : 0, E, BM, tiles, s_wave);
+  int blk = blockIdx.x, nblk = gridDim.x;
+  if (tiles != nullptr) {
+    // the first block writes the grouped GEMMs' M-tile prefix and the
+    // weight-gradient split plan and nothing else, so that this work runs
+    // beside the token blocks rather than before one of them
+    if (blk == 0) {
+      __shared__ int s_wave[4];
+      const int e = threadIdx.x;
+      const int m = e < E ? offsets[e + 1] - offsets[e] : 0;
+      block_tile_prefix(m, E, BM, tiles, s_wave);
+      if (plan != nullptr) block_krag_plan(m, E, te, plan, s_wave);
+      return;
+    }
+    --blk;
+    --nblk;
   }
   const int lane = threadIdx.x & 63;
   const int nch = d / V;
-  for (int64_t t = (int64_t)blockIdx.x * kCW + (threadIdx.x >> 6); t < T_;
-       t += (int64_t)gridDim.x * kCW) {
+  for (int64_t t = (int64_t)blk * kCW + (threadIdx.x >> 6); t < T_;
+       t += (int64_t)nblk * kCW) {
     const int32_t* rows = row_of + t * k;
     float mine = 0.0f;  // lane j < k: dgate[t, j]
     for (int g0 = 0; g0 < nch; g0 += kWave * kBwdCPL) {
@@ -262,23 +273,26 @@ int launch_combine(const moe_cfg& c, const void* Y, const int32_t* row_of,
 
 int launch_combine_bwd(const moe_cfg& c, const void* dOut, const void* Y,
                        const int32_t* row_of, const float* gate, const void* x, void* dYp,
-                       float* dgate, hipStream_t s, const int32_t* offsets, int32_t* tiles) {
+                       float* dgate, hipStream_t s, const int32_t* offsets, int32_t* tiles,
+                       int32_t* plan) {
   if (c.T == 0) return MOE_OK;
   const int BM = ffn_row_tile(c);
-  const int grid = token_grid(c.T);
+  // one more block for the schedule when the tiles are asked for
+  const int grid = token_grid(c.T) + (tiles != nullptr ? 1 : 0);
   const void* fb = (c.flags & MOE_FLAG_DROP_IDENTITY) ? x : nullptr;
   if (c.dtype == MOE_BF16)
     MOE_LAUNCH(MOE_KERNEL_COMBINE_BWD, s,
                combine_bwd_kernel<uint16_t><<<grid, 256, 0, s>>>(
                    static_cast<const uint16_t*>(dOut), static_cast<const uint16_t*>(Y),
                    row_of, gate, static_cast<const uint16_t*>(fb),
-                   static_cast<uint16_t*>(dYp), dgate, c.T, c.d, c.k, offsets, tiles, c.E, BM));
+                   static_cast<uint16_t*>(dYp), dgate, c.T, c.d, c.k, offsets, tiles, c.E, BM,
+                   plan, (int)krag_te(c)));
   else
     MOE_LAUNCH(MOE_KERNEL_COMBINE_BWD, s,
                combine_bwd_kernel<float><<<grid, 256, 0, s>>>(
                    static_cast<const float*>(dOut), static_cast<const float*>(Y), row_of,
                    gate, static_cast<const float*>(fb), static_cast<float*>(dYp), dgate,
-                   c.T, c.d, c.k, offsets, tiles, c.E, BM));
+                   c.T, c.d, c.k, offsets, tiles, c.E, BM, nullptr, 0));
   return MOE_OK;
 }
 

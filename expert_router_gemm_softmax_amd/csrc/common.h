@@ -141,6 +141,95 @@ __device__ __forceinline__ void block_tile_prefix(int m, int E, int BM, int32_t*
   if (e == 0) tiles[E] = tot;
 }
 
+// The split plan of the expert weight-gradient GEMMs (dW1, dW2: a
+// reduction over each expert's m_e rows, te output tiles per expert).
+// Thread e of a 256-thread block holds m = m_e (0 for e >= E; E <= 256);
+// every thread calls it (it synchronises).  With R = sum m_e and
+// Kc = max(256, ceil(R te / 512)) rounded up to 32, an expert with more than
+// 2 Kc rows is split into ceil(m_e / Kc) parts of about equal rows, so that
+// no single tile's reduction is long against the chip's share of the work
+// (about 512 part-tiles of Kc rows or more in all).  The work units
+// (parts x tiles, expert-major) are then cut into 8 contiguous ranges of
+// about equal work, one per XCD, a unit weighing its rows plus kKragUnitRows
+// for its prologue and epilogue; with few units per XCD a cut close to an
+// expert boundary moves onto it.  Written:
+//   plan[e]          first work unit of expert e (units = parts x te)
+//   plan[E]          number of units
+//   plan[E+1+e]      first fp32 partial slab of expert e (split experts only)
+//   plan[2E+1]       number of slabs
+//   plan[2E+2]       Kc
+//   plan[2E+3+x]     first unit of XCD x (x = 0..8; plan[2E+11] = units)
+constexpr int kKragUnitRows = 128;
+inline int krag_plan_ints(int E) { return 3 * E + 12; }
+__device__ __forceinline__ void block_krag_plan(int m, int E, int te, int32_t* plan,
+                                                int* s_wave) {
+  __shared__ double s_wsum[4];
+  const int e = threadIdx.x;
+  int R;
+  (void)block_exclusive_scan_256(m, s_wave, &R);
+  // integer quantities below 2^53 are exact in double, whose division is
+  // cheaper here than a 64-bit integer one
+  int kc = (int)ceil((double)R * te / 512.0);
+  kc = (kc + 31) / 32 * 32;
+  if (kc < 256) kc = 256;
+  const int parts = (e < E && m > 2 * kc) ? (int)ceil((double)m / kc) : 1;
+  int tot_u, tot_s;
+  const int ex_u = block_exclusive_scan_256(e < E ? parts * te : 0, s_wave, &tot_u);
+  const int ex_s = block_exclusive_scan_256(e < E && parts > 1 ? parts : 0, s_wave, &tot_s);
+  if (e < E) {
+    plan[e] = ex_u;
+    plan[E + 1 + e] = ex_s;
+  }
+  if (e == 0) {
+    plan[E] = tot_u;
+    plan[2 * E + 1] = tot_s;
+    plan[2 * E + 2] = kc;
+  }
+  // work of one of this expert's units (its parts have equal rows but the
+  // last), and of all its units; their exclusive scan
+  const int rows = parts > 1 ? ((m + parts - 1) / parts + 31) / 32 * 32 : m;
+  const double wu = (double)(rows + kKragUnitRows);
+  const double we = e < E ? wu * parts * te : 0.0;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  double incl = we;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  __syncthreads();
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();
+  double base = 0.0;
+  for (int i = 0; i < w; ++i) base += s_wsum[i];
+  const double W = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+  const double pre = base + incl - we;
+  // XCD x starts at the unit holding work x W / 8: the expert whose work
+  // interval holds that point writes it.  With few units per XCD (under 256
+  // on average, a handful of rounds of tiles) the cut moves to the nearer
+  // end of that expert when this shifts it by at most W / 32 (a quarter of
+  // an XCD's share): an XCD then serves whole experts from its L2, and a
+  // layer of near-equal experts keeps the same number of tiles on every XCD
+  // (a cut inside an expert there adds a round of tiles to one XCD).
+  if (e < E) {
+    const bool snap = tot_u < 8 * 256;
+    for (int x = 1; x < 8; ++x) {
+      const double target = floor(W * x / 8.0);
+      if (target >= pre && target < pre + we) {
+        int cut = ex_u + (int)floor((target - pre) / wu);
+        const double slack = W / 32.0;
+        if (snap && target - pre <= slack && target - pre <= pre + we - target) cut = ex_u;
+        else if (snap && pre + we - target <= slack) cut = ex_u + parts * te;
+        plan[2 * E + 3 + x] = cut;
+      }
+    }
+  }
+  if (e == 0) {
+    plan[2 * E + 3] = 0;
+    plan[2 * E + 11] = tot_u;
+  }
+}
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -164,9 +253,12 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 //   dgate    [T, k] f32         combine-backward gate gradient
 //   dYp, dA, dXp                backward row gradients (Rmax rows, s)
 //   dxe      [T, d] f32         unpermute-sum of dXp (router backward)
+//   rA, rH   [Rmax, f] s        A and H of the recomputation mode
+//   kplan    [3E+12] i32        split plan of the weight-gradient GEMMs
+//   kslab    [slabs, d, f] f32  their fp32 partial sums (split experts)
 struct WsLayout {
   size_t wrT, zf, wl_count, wl_tok, wl_n, wl_e, gpart, perm_blk, tiles, aux_part, dz, dzb, wrp,
-      dwr_part, db_part, dgate, dYp, dA, dXp, dxe, rA, rH, total;
+      dwr_part, db_part, dgate, dYp, dA, dXp, dxe, rA, rH, kplan, kslab, total;
   int nblk_perm;
   int nblk_aux;
   int nblk_dz;
@@ -190,6 +282,26 @@ inline int64_t rows_max(const moe_cfg& c) {
 }
 
 // experts padded to 32, 64, 128 or 256 (whole 32-wide MFMA tiles) in the router
+// Block tile of the expert weight-gradient GEMMs (bf16): 256 x 256 when
+// the experts are not small (at least 512 rows each on average) and the
+// problem has a full round of such tiles for the chip, else 128 x 128
+inline int krag_tile(const moe_cfg& c) {
+  const bool small = rows_max(c) < 512 * (int64_t)c.E;
+  const int64_t big = (int64_t)c.E * ceil_div(c.d, 256) * ceil_div(c.f, 256);
+  return (!small && big >= 256) ? 256 : 128;
+}
+// output tiles per expert of the weight-gradient GEMMs
+inline int64_t krag_te(const moe_cfg& c) {
+  const int b = krag_tile(c);
+  return ceil_div(c.d, b) * ceil_div(c.f, b);
+}
+// fp32 partial slabs (d x f floats each) the split plan can need: split
+// experts hold at most 1.5 R / Kc <= 768 / te slabs (Kc >= R te / 512)
+inline int64_t krag_slabs_max(const moe_cfg& c) {
+  if (c.dtype != MOE_BF16) return 0;
+  return ceil_div(768, krag_te(c)) + 2;
+}
+
 inline int route_epad(int E) {
   const int nt = (E + 31) / 32;
   return 32 * (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8);
@@ -249,6 +361,9 @@ inline WsLayout ws_layout(const moe_cfg& c) {
   const bool rec = (c.flags & MOE_FLAG_RECOMPUTE) != 0;
   L.rA = take(rec ? (size_t)Rmax * c.f * s : 0);
   L.rH = take(rec ? (size_t)Rmax * c.f * s : 0);
+  // split plan and fp32 partial slabs of the weight-gradient GEMMs
+  L.kplan = take((size_t)krag_plan_ints(c.E) * 4);
+  L.kslab = take((size_t)krag_slabs_max(c) * c.d * c.f * 4);
   L.total = off;
   return L;
 }
@@ -338,10 +453,11 @@ int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
 int launch_combine(const moe_cfg& c, const void* Y, const int32_t* row_of,
                    const float* gate, const void* x, void* out, hipStream_t s);
 // offsets and tiles (nullable): also write the grouped GEMMs' M-tile prefix
+// (and, plan non-null, the weight-gradient split plan)
 int launch_combine_bwd(const moe_cfg& c, const void* dOut, const void* Y,
                        const int32_t* row_of, const float* gate, const void* x, void* dYp,
                        float* dgate, hipStream_t s, const int32_t* offsets = nullptr,
-                       int32_t* tiles = nullptr);
+                       int32_t* tiles = nullptr, int32_t* plan = nullptr);
 int launch_unpermute_bwd(const moe_cfg& c, const void* dXp, const int32_t* row_of,
                          const float* gate, const void* dOut, float* dXe, hipStream_t s,
                          int kernel_id = MOE_KERNEL_UNPERMUTE_BWD);

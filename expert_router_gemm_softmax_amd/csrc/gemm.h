@@ -36,6 +36,9 @@ struct GemmArgs {
                          // each for fp32, 128 x 128 for fp32-add); 0 = auto
   float* part;           // ROW, bf16: workspace for the split-K tail (fp32
                          // partial tiles, kGemmPartFloats); nullptr = no split
+  const int32_t* kplan;  // KRAG with per-expert offsets, bf16: the split plan
+                         // (block_krag_plan); nullptr = no split
+  float* kslab;          // its fp32 partial slabs [slab][M][N]
   int slots;             // filled by the launcher: concurrent blocks per round
   int ntn, ntm;          // filled by the launcher
 };

@@ -64,6 +64,7 @@ struct Tile {
   int e, m0, n0, M, K;
   int64_t row0;  // ROW: first row of the expert; KRAG: first K row
   int kofs;      // split-K part: first K element of the part (0 otherwise)
+  int slab;      // KRAG split part: its fp32 partial slab (-1 otherwise)
 };
 
 // Number of output tiles (and of M tiles for ROW).  ROW problems with a
@@ -81,6 +82,11 @@ __device__ __forceinline__ int tile_count(const GemmArgs& g, int* s_tiles, int& 
     return num_m * g.ntn;
   } else {
     num_m = g.ntm;
+    if (g.kplan != nullptr) {  // the split plan's work units
+      for (int i = threadIdx.x; i <= g.E; i += blockDim.x) s_tiles[i] = g.kplan[i];
+      __syncthreads();
+      return s_tiles[g.E];
+    }
     return g.E * g.ntm * g.ntn;
   }
 }
@@ -90,6 +96,7 @@ template <int MODE, int BM, int BN>
 __device__ __forceinline__ void tile_of(const GemmArgs& g, const int* s_tiles, int num_m, int lid,
                                         Tile& t) {
   t.kofs = 0;
+  t.slab = -1;
   if constexpr (MODE == MODE_ROW) {
     int mt, nt;
     group_mn<group_m<BM>()>(lid, num_m, g.ntn, mt, nt);
@@ -111,6 +118,35 @@ __device__ __forceinline__ void tile_of(const GemmArgs& g, const int* s_tiles, i
     }
     t.n0 = nt * BN;
     t.K = g.K;
+  } else if (g.kplan != nullptr) {
+    // unit lid of the split plan: expert, part, then the part's tile
+    const int te = g.ntm * g.ntn;
+    int lo = 0, hi = g.E - 1;  // last e with s_tiles[e] <= lid
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tiles[mid] <= lid) lo = mid; else hi = mid - 1;
+    }
+    t.e = lo;
+    const int u = lid - s_tiles[lo];
+    const int parts = (s_tiles[lo + 1] - s_tiles[lo]) / te;
+    const int part = u / te;
+    int mt, nt;
+    group_mn<group_m<BM>()>(u - part * te, g.ntm, g.ntn, mt, nt);
+    const int64_t r0 = g.offsets[t.e];
+    const int m = g.offsets[t.e + 1] - (int)r0;
+    t.row0 = r0;
+    t.K = m;
+    if (parts > 1) {
+      // parts of equal rows, rounded up to whole K tiles
+      const int chunk = ((m + parts - 1) / parts + BK_ALL - 1) / BK_ALL * BK_ALL;
+      const int k0 = min(part * chunk, m);
+      t.row0 = r0 + k0;
+      t.K = min(chunk, m - k0);
+      t.slab = g.kplan[g.E + 1 + t.e] + part;
+    }
+    t.M = g.M;
+    t.m0 = mt * BM;
+    t.n0 = nt * BN;
   } else {
     const int per_e = g.ntm * g.ntn;
     t.e = lid / per_e;
@@ -367,8 +403,19 @@ struct Operand {
   }
 };
 
+// LDS of one block: the operand ring, reused as the epilogue staging area
+template <int MODE, bool B_KC, int BM, int BN>
+constexpr int smem_elems() {
+  return ring_stages<BM, BN>() *
+         (Operand<MODE == MODE_ROW, BM>::kElems + Operand<(MODE == MODE_ROW) && B_KC, BN>::kElems);
+}
+
+// One output tile (or split part) t: main loop and epilogue.  Every thread
+// of the block calls it; it ends with a barrier, so the block may go on to
+// another tile.
 template <int MODE, bool B_KC, int EPI, int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, int part, int pid,
+                                          uint16_t* smem) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr bool A_KC = (MODE == MODE_ROW);
@@ -377,16 +424,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   using OpB = Operand<BKC, BN>;
   constexpr int kStageElems = OpA::kElems + OpB::kElems;
   constexpr int kStages = ring_stages<BM, BN>();
-  // the operand ring; reused as the epilogue staging area
-  __shared__ __align__(16) uint16_t smem[kStages * kStageElems];
-  __shared__ int s_tiles[MODE == MODE_ROW ? 257 : 1];
-
-  Tile t;
-  int part, pid;
-  if (!decode_work<MODE, BM, BN>(g, s_tiles, t, part, pid)) return;
-  if constexpr (MODE == MODE_ROW) {
-    if (t.m0 >= t.M) return;
-  }
+  constexpr int kSmemBytes = smem_elems<MODE, B_KC, BM, BN>() * 2;
 
   // operand origins, advanced to the first K element of a split part
   const uint16_t* A = static_cast<const uint16_t*>(g.A) + t.row0 * g.lda + t.kofs;
@@ -513,12 +551,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int SP = WN + 4;        // staging row stride (floats)
   constexpr int LPR = WN / 8;       // lanes per staged row
   constexpr int RPP = kWave / LPR;  // rows per pass
-  static_assert(4 * 32 * SP * 4 <= (int)sizeof(smem), "staging does not fit");
+  static_assert(4 * 32 * SP * 4 <= kSmemBytes, "staging does not fit");
   float* stage = reinterpret_cast<float*>(smem) + w * 32 * SP;
   int64_t cbase;
   if constexpr (MODE == MODE_ROW) cbase = t.row0 * g.ldc;
   else cbase = (int64_t)t.e * g.c_estride;
   float* ptile = part >= 0 ? g.part + (int64_t)pid * BM * BN : nullptr;
+  // KRAG split part: fp32 partial sums into the part's [M][N] slab
+  float* pslab = nullptr;
+  if constexpr (MODE == MODE_KRAG) {
+    if (t.slab >= 0) pslab = g.kslab + (int64_t)t.slab * g.M * g.N;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     // GELU backward and fp32 add: every pass's auxiliary input of this row
@@ -564,6 +607,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
         float* q = ptile + tr * BN + tc;
         *reinterpret_cast<f32x4*>(q) = *reinterpret_cast<const f32x4*>(v8);
         *reinterpret_cast<f32x4*>(q + 4) = *reinterpret_cast<const f32x4*>(v8 + 4);
+      } else if (pslab) {
+        const int row = t.m0 + tr, col = t.n0 + tc;
+        if (row < g.M && col < g.N) {
+          float* q = pslab + (int64_t)row * g.N + col;
+          *reinterpret_cast<f32x4*>(q) = *reinterpret_cast<const f32x4*>(v8);
+          *reinterpret_cast<f32x4*>(q + 4) = *reinterpret_cast<const f32x4*>(v8 + 4);
+        }
       } else {
         const int row = t.m0 + tr, col = t.n0 + tc;
         if (row < t.M && col < g.N)
@@ -573,6 +623,36 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
     }
     __syncthreads();
   }
+}
+
+template <int MODE, bool B_KC, int EPI, int BM, int BN>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __align__(16) uint16_t smem[smem_elems<MODE, B_KC, BM, BN>()];
+  __shared__ int s_tiles[257];
+  if constexpr (MODE == MODE_KRAG) {
+    if (g.kplan != nullptr) {
+      // Split plan: XCD x (block id mod 8) walks the work-balanced unit range
+      // [plan[2E+3+x], plan[2E+4+x]) with its blocks in turn.
+      int num_m;
+      (void)tile_count<MODE, BM>(g, s_tiles, num_m);
+      const int x = blockIdx.x & 7;
+      const int first = g.kplan[2 * g.E + 3 + x], last = g.kplan[2 * g.E + 4 + x];
+      const int step = (int)(gridDim.x >> 3);
+      for (int lid = first + (int)(blockIdx.x >> 3); lid < last; lid += step) {
+        Tile t;
+        tile_of<MODE, BM, BN>(g, s_tiles, num_m, lid, t);
+        gemm_tile<MODE, B_KC, EPI, BM, BN>(g, t, -1, 0, smem);
+      }
+      return;
+    }
+  }
+  Tile t;
+  int part, pid;
+  if (!decode_work<MODE, BM, BN>(g, s_tiles, t, part, pid)) return;
+  if constexpr (MODE == MODE_ROW) {
+    if (t.m0 >= t.M) return;
+  }
+  gemm_tile<MODE, B_KC, EPI, BM, BN>(g, t, part, pid, smem);
 }
 
 // Sums the split-K parts of the tail tiles (in part order) and applies the
@@ -611,6 +691,39 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
   }
 }
 
+// Sums the fp32 partial slabs of the split experts of a weight-gradient
+// GEMM in part order and stores the bf16 result (non-temporally, like the
+// unsplit tiles); experts that were not split are skipped.
+__global__ __launch_bounds__(256) void gemm_krag_fixup_kernel(GemmArgs g) {
+  const int32_t* plan = g.kplan;
+  const int E = g.E;
+  const int te = g.ntm * g.ntn;
+  const int64_t chunks = (int64_t)g.M * (g.N / 8);
+  for (int e = 0; e < E; ++e) {
+    const int parts = (plan[e + 1] - plan[e]) / te;
+    if (parts <= 1) continue;
+    const float* s0 = g.kslab + (int64_t)plan[E + 1 + e] * g.M * g.N;
+    for (int64_t it = blockIdx.x * 256 + threadIdx.x; it < chunks;
+         it += (int64_t)gridDim.x * 256) {
+      const int64_t row = it / (g.N / 8);
+      const int col = (int)(it - row * (g.N / 8)) * 8;
+      float v8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      const float* q = s0 + row * g.N + col;
+#pragma unroll 4
+      for (int p = 0; p < parts; ++p, q += (int64_t)g.M * g.N) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(q);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(q + 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v8[u] += a[u];
+          v8[u + 4] += b[u];
+        }
+      }
+      epi_write8<EPI_STORE, true>(g, (int64_t)e * g.c_estride + row * g.ldc + col, v8);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ fp32 VALU kernel
 // Plain LDS-tiled fp32 GEMM with the same problem decode and epilogues,
 // used for float storage (64 x 64 tile, 4 x 4 outputs per thread).
@@ -619,7 +732,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   constexpr int BM = 64, BN = 64, BKF = 16;
   __shared__ float sA[BKF][BM + 1];
   __shared__ float sB[BKF][BN + 1];
-  __shared__ int s_tiles[MODE == MODE_ROW ? 257 : 1];
+  __shared__ int s_tiles[257];
   Tile t;
   if (!decode_tile<MODE, BM, BN>(g, s_tiles, t)) return;
   if constexpr (MODE == MODE_ROW) {
@@ -695,12 +808,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 
 // tiles[e] = sum_{e' < e} ceil(m_e' / BM); tiles[E] = number of M tiles
 // (one thread per expert, E <= 256, block scan)
+// and, when plan is given, the split plan of the weight-gradient GEMMs
 __global__ __launch_bounds__(256) void gemm_schedule_kernel(const int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ tiles, int E,
-                                                            int BM) {
+                                                            int BM, int32_t* __restrict__ plan,
+                                                            int te) {
   __shared__ int s_wave[4];
   const int e = threadIdx.x;
-  block_tile_prefix(e < E ? offsets[e + 1] - offsets[e] : 0, E, BM, tiles, s_wave);
+  const int m = e < E ? offsets[e + 1] - offsets[e] : 0;
+  block_tile_prefix(m, E, BM, tiles, s_wave);
+  if (plan != nullptr) block_krag_plan(m, E, te, plan, s_wave);
 }
 
 constexpr int kFM = 64, kFN = 64;    // fp32 block tile
@@ -763,8 +880,10 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
     }
   } else {
     // expert weight gradients (per-expert offsets) follow small_experts
-    const bool small = g.offsets != nullptr && small_experts(c);
-    BM = BN = !small && use_big_tile(c, MODE_KRAG, g.M, g.N, g.E) ? 256 : 128;
+    // expert weight gradients (per-expert offsets) follow krag_tile, whose
+    // tile count the split plan was built for
+    BM = BN = g.offsets != nullptr ? krag_tile(c)
+                                   : (use_big_tile(c, MODE_KRAG, g.M, g.N, g.E) ? 256 : 128);
   }
   g.ntn = (int)ceil_div(g.N, BN);
   int64_t nblk;
@@ -773,6 +892,8 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
   } else {
     g.ntm = (int)ceil_div(g.M, BM);
     nblk = (int64_t)g.E * g.ntm * g.ntn;
+    // the split plan adds at most R / Kc <= 512 / te parts' worth of tiles
+    if (g.kplan != nullptr) nblk += 512 + g.ntm * g.ntn;
   }
   if (nblk == 0) return MOE_OK;
   if constexpr (MODE == MODE_ROW) {
@@ -826,12 +947,19 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
     MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 256, 256><<<grid, 256, 0, s>>>(g));
   else
     MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 128, 128><<<grid, 256, 0, s>>>(g));
+  if constexpr (MODE == MODE_KRAG && EPI == EPI_STORE) {
+    // the split experts' slabs, summed in part order (a no-op without splits)
+    if (g.kplan != nullptr)
+      MOE_LAUNCH(MOE_KERNEL_GEMM_FIXUP, s, gemm_krag_fixup_kernel<<<1024, 256, 0, s>>>(g));
+  }
   return MOE_OK;
 }
 
-int schedule(const moe_cfg& c, const int32_t* offsets, int32_t* tiles, hipStream_t s) {
+int schedule(const moe_cfg& c, const int32_t* offsets, int32_t* tiles, hipStream_t s,
+             int32_t* plan = nullptr) {
   MOE_LAUNCH(MOE_KERNEL_SCHEDULE, s,
-             gemm_schedule_kernel<<<1, 256, 0, s>>>(offsets, tiles, c.E, row_bm(c)));
+             gemm_schedule_kernel<<<1, 256, 0, s>>>(offsets, tiles, c.E, row_bm(c), plan,
+                                                    (int)krag_te(c)));
   return MOE_OK;
 }
 
@@ -902,6 +1030,8 @@ int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
                    hipStream_t s, bool have_tiles) {
   const WsLayout L = ws_layout(c);
   int32_t* tiles = ws_ptr<int32_t>(ws, L.tiles);
+  // split plan of the weight-gradient GEMMs (bf16), built with the tiles
+  int32_t* plan = c.dtype == MOE_BF16 ? ws_ptr<int32_t>(ws, L.kplan) : nullptr;
   void* dA = ws_ptr<void>(ws, L.dA);
   int rc;
   GemmArgs g{};
@@ -910,7 +1040,7 @@ int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
   g.E = c.E;
   g.part = ws_ptr<float>(ws, L.gpart);
   if (rows_max(c) > 0) {
-    rc = have_tiles ? MOE_OK : schedule(c, offsets, tiles, s);
+    rc = have_tiles ? MOE_OK : schedule(c, offsets, tiles, s, plan);
     if (rc != MOE_OK) return rc;
     if (c.flags & MOE_FLAG_RECOMPUTE) {
       // recompute A and H exactly as the forward does (same kernel, inputs
@@ -945,9 +1075,14 @@ int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
     return run_gemm<MODE_ROW, true, EPI_STORE>(MOE_KERNEL_GEMM_DX, c, h, s);
   };
   // dW2[e] = H_e^T dYp_e : M = f, N = d
+  // without rows the plan was never built: every expert is empty, nothing
+  // to split
+  const int32_t* kplan = rows_max(c) > 0 ? plan : nullptr;
   auto gemm_dw2 = [&]() {
     GemmArgs h = g;
     h.part = nullptr;
+    h.kplan = kplan;
+    h.kslab = ws_ptr<float>(ws, L.kslab);
     h.A = H; h.B = dYp; h.C = dW2;
     h.M = c.f; h.N = c.d; h.lda = c.f; h.ldb = c.d; h.ldc = c.d;
     h.c_estride = (int64_t)c.f * c.d;
@@ -957,6 +1092,8 @@ int launch_ffn_bwd(const moe_cfg& c, const void* x_perm, const int32_t* offsets,
   auto gemm_dw1 = [&]() {
     GemmArgs h = g;
     h.part = nullptr;
+    h.kplan = kplan;
+    h.kslab = ws_ptr<float>(ws, L.kslab);
     h.A = x_perm; h.B = dA; h.C = dW1;
     h.M = c.d; h.N = c.f; h.lda = c.d; h.ldb = c.f; h.ldc = c.f;
     h.c_estride = (int64_t)c.d * c.f;

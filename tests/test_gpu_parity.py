@@ -500,4 +500,6 @@ def test_kernel_probe_records_the_probed_launches_only(M):
     fix.detach(layer.cfg)
     _, nf, _ = fix.read()
     fix.close()
-    assert nf == 2  # the dH and dX GEMMs' fixups (the weight gradients have none)
+    # the dH and dX GEMMs' split-K fixups and the weight gradients' slab sums
+    # (no-ops here: no expert of this layer is split)
+    assert nf == 4
