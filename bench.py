@@ -53,8 +53,8 @@ def parse():
                     help="workload: C0..C4 or its name (default C4, the largest)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kernel", default=None,
-                    help="kernel timed for the roofline (default: GEMM_DOWN, Y = H W2, "
-                         "the longest single launch on c4_large)")
+                    help="kernel timed for the roofline (default: GEMM_DH, dA = (dYp W2^T) "
+                         "* gelu'(A), the longest single launch on c4_large)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="time warm back-to-back steps only (the primary value is then the "
@@ -85,10 +85,10 @@ def parse():
 
 # name fragment of each timed kernel in a rocprofv3 trace (template arguments:
 # mode, B K-contiguous, epilogue)
-KERNEL_NAMES = {"GEMM_UP": "gemm_bf16_kernel<0, false, 1,",
-                "GEMM_DOWN": "gemm_bf16_kernel<0, false, 0,",
-                "GEMM_DH": "gemm_bf16_kernel<0, true, 2,",
-                "GEMM_DX": "gemm_bf16_kernel<0, true, 0,"}
+KERNEL_NAMES = {"GEMM_UP": "gemm_bf16_kernel<0, false, 1, 256",
+                "GEMM_DOWN": "gemm_bf16_kernel<0, false, 0, 256",
+                "GEMM_DH": "gemm_bf16_kernel<0, true, 2, 256",
+                "GEMM_DX": "gemm_bf16_kernel<0, true, 0, 256"}
 GEMM_SOURCES = ("expert_router_gemm_softmax_amd/csrc/gemm.hip",
                 "expert_router_gemm_softmax_amd/csrc/gemm.h",
                 "expert_router_gemm_softmax_amd/csrc/common.h")
@@ -313,7 +313,7 @@ def main():
     # outside the timing.  The probe records the roofline kernel's launches
     # inside these steps, on the stream they run on.  (Graph replays record
     # no probe events: the kernel is then timed on as many eager steps.)
-    kernel = a.kernel or "GEMM_DOWN"
+    kernel = a.kernel or "GEMM_DH"
     probe = M.KernelProbe(kernel, a.steps)
     if not a.graph:
         probe.attach(cfg)

@@ -879,7 +879,6 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
       if (!g.offsets && g.bn) BN = g.bn;
     }
   } else {
-    // expert weight gradients (per-expert offsets) follow small_experts
     // expert weight gradients (per-expert offsets) follow krag_tile, whose
     // tile count the split plan was built for
     BM = BN = g.offsets != nullptr ? krag_tile(c)
