@@ -85,10 +85,10 @@ def parse():
 
 # name fragment of each timed kernel in a rocprofv3 trace (template arguments:
 # mode, B K-contiguous, epilogue)
-KERNEL_NAMES = {"GEMM_UP": "gemm_bf16_kernel<0, false, 1, 256",
-                "GEMM_DOWN": "gemm_bf16_kernel<0, false, 0, 256",
-                "GEMM_DH": "gemm_bf16_kernel<0, true, 2, 256",
-                "GEMM_DX": "gemm_bf16_kernel<0, true, 0, 256"}
+KERNEL_NAMES = {"GEMM_UP": "gemm_bf16_kernel<0, false, 1,",
+                "GEMM_DOWN": "gemm_bf16_kernel<0, false, 0,",
+                "GEMM_DH": "gemm_bf16_kernel<0, true, 2,",
+                "GEMM_DX": "gemm_bf16_kernel<0, true, 0,"}
 GEMM_SOURCES = ("expert_router_gemm_softmax_amd/csrc/gemm.hip",
                 "expert_router_gemm_softmax_amd/csrc/gemm.h",
                 "expert_router_gemm_softmax_amd/csrc/common.h")
