@@ -301,8 +301,11 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, int* s_tiles, Til
 //   KC (K contiguous) tile [rows][32]: 16-byte chunk q of a row stored at
 //      chunk q ^ ((row >> 2) & 3); MFMA fragments are plain 16-byte reads.
 //   MN (M or N contiguous) tile [32][R]: chunk c of k-row k stored at chunk
-//      c ^ 4 (k & 3); fragments come from two ds_read_b64_tr_b16, which
+//      c ^ mn_swz(k); fragments come from two ds_read_b64_tr_b16, which
 //      transpose 4 x 4 blocks of 16-bit elements across each 16-lane group.
+//      The XOR spreads the four k-rows of one such read, and two reads 8
+//      k-rows apart (the 16-lane groups of a 16 x 16 x 32 fragment), over
+//      distinct banks.
 // Rows (KC) or column chunks (MN) past the tile's M or N edge are clamped
 // to the last valid one; they only feed outputs that are never stored.  A
 // final partial K tile goes through registers with zero fill.
@@ -319,9 +322,10 @@ typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 __device__ __forceinline__ int kc_off(int row, int q) {
   return row * BK + ((q ^ ((row >> 2) & 3)) << 3);
 }
+__device__ __forceinline__ int mn_swz(int k) { return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1); }
 template <int R>
 __device__ __forceinline__ int mn_off(int k, int m) {
-  return k * R + ((((m >> 3) ^ ((k & 3) << 2))) << 3) + (m & 7);
+  return k * R + (((m >> 3) ^ mn_swz(k)) << 3) + (m & 7);
 }
 
 // One operand tile of R rows (M or N extent) per stage.
@@ -349,7 +353,7 @@ struct Operand {
         const int row = p >> 2, q = (p & 3) ^ ((row >> 2) & 3);
         src[j] = (int64_t)min(mn0 + row, lim - 1) * ld + q * 8;
       } else {
-        const int k = p / (R / 8), c = (p % (R / 8)) ^ ((k & 3) << 2);
+        const int k = p / (R / 8), c = (p % (R / 8)) ^ mn_swz(k);
         src[j] = (int64_t)k * ld + min(mn0 + c * 8, lim - 8);
       }
     }
@@ -401,7 +405,131 @@ struct Operand {
       return __builtin_bit_cast(bf16x8, both);
     }
   }
+  // MFMA 16x16x32 fragment of the 16 rows starting at mb (the whole K tile):
+  // lane l gets the 8 k values 8 (l / 16) .. +7 of row mb + l % 16
+  __device__ __forceinline__ bf16x8 frag16(const uint16_t* s, int mb, int lane) const {
+    if constexpr (KC) {
+      return *reinterpret_cast<const bf16x8*>(s + kc_off(mb + (lane & 15), lane >> 4));
+    } else {
+      const int G = lane >> 4, a4 = (lane >> 2) & 3, b4 = lane & 3;
+      const int m = mb + 4 * b4, k = G * 8 + a4;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(s + mn_off<R>(k, m)));
+      const v4s hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(s + mn_off<R>(k + 4, m)));
+      const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, both);
+    }
+  }
 };
+
+// Epilogue of one wave's TM x TN blocks of 32 x 32 outputs whose origin in
+// the block tile is row wr0, column wc0: through LDS, TNP column blocks at a
+// time.  The accumulators are 32 x 32 MFMA tiles (f32x16: D[i][j] in lane
+// j + 32*((i/4)%2), register (i%4) + 4*(i/8)) or 16 x 16 ones (f32x4, two
+// by two per block: D[i][j] in lane j + 16*(i/4), register i%4).  The wave
+// stages 32 rows x 32 TNP columns in `stage`, then every lane handles 8
+// consecutive columns of a row with 16-byte loads and stores.  Every thread
+// of the block calls it with the same trip counts (it synchronises).
+template <int MODE, int EPI, int BM, int BN, int TM, int TN, int TNP, typename Acc, int TMA,
+          int TNA>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& t, int part, int pid,
+                                              Acc (&acc)[TMA][TNA], float* stage, int wr0,
+                                              int wc0) {
+  constexpr int MF = sizeof(Acc) == sizeof(f32x16) ? 32 : 16;  // MFMA tile edge
+  static_assert(sizeof(Acc) == sizeof(f32x16) || sizeof(Acc) == sizeof(f32x4), "accumulator");
+  static_assert(TMA * MF == TM * 32 && TNA * MF == TN * 32, "accumulator tiles");
+  constexpr int PW = TNP * 32;      // staged columns per pass
+  constexpr int SP = PW + 4;        // staging row stride (floats)
+  constexpr int LPR = PW / 8;       // lanes per staged row
+  constexpr int RPP = kWave / LPR;  // rows per pass
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, r = lane & 31;
+  int64_t cbase;
+  if constexpr (MODE == MODE_ROW) cbase = t.row0 * g.ldc;
+  else cbase = (int64_t)t.e * g.c_estride;
+  float* ptile = part >= 0 ? g.part + (int64_t)pid * BM * BN : nullptr;
+  // KRAG split part: fp32 partial sums into the part's [M][N] slab
+  float* pslab = nullptr;
+  if constexpr (MODE == MODE_KRAG) {
+    if (t.slab >= 0) pslab = g.kslab + (int64_t)t.slab * g.M * g.N;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j0 = 0; j0 < TN; j0 += TNP) {
+      // GELU backward and fp32 add: every pass's auxiliary input of this row
+      // block (the bf16 pre-activation, 16 bytes; the fp32 addend, 32 bytes)
+      // is loaded before the staging, so the loads are in flight together
+      // instead of one after each pass's stores
+      constexpr bool kPre = EPI == EPI_DGELU || EPI == EPI_ADDF32;
+      constexpr int kPreV = EPI == EPI_ADDF32 ? 2 : 1;  // 16-byte vectors per pass
+      u32x4 pa[kPre ? 32 / RPP : 1][kPreV];
+      if constexpr (kPre) {
+        if (ptile == nullptr) {
+#pragma unroll
+          for (int p = 0; p < 32 / RPP; ++p) {
+            const int row = t.m0 + wr0 + i * 32 + p * RPP + lane / LPR;
+            const int col = t.n0 + wc0 + j0 * 32 + (lane % LPR) * 8;
+            const bool ok = row < t.M && col < g.N;
+            const int64_t o = cbase + (int64_t)row * g.ldc + col;
+#pragma unroll
+            for (int u = 0; u < kPreV; ++u) {
+              if constexpr (EPI == EPI_DGELU)
+                pa[p][u] = ok ? ld16(static_cast<const uint16_t*>(g.Aux) + o) : u32x4{0, 0, 0, 0};
+              else
+                pa[p][u] = ok ? ld16(static_cast<const float*>(g.Aux) + o + 4 * u)
+                              : u32x4{0, 0, 0, 0};
+            }
+          }
+        }
+      }
+      if constexpr (MF == 32) {
+#pragma unroll
+        for (int j = 0; j < TNP; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            stage[(8 * (v >> 2) + 4 * h + (v & 3)) * SP + j * 32 + r] = acc[i][j0 + j][v];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2 * TNP; ++j)
+#pragma unroll
+          for (int ri = 0; ri < 2; ++ri)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              stage[(ri * 16 + 4 * (lane >> 4) + v) * SP + j * 16 + (lane & 15)] =
+                  acc[2 * i + ri][2 * j0 + j][v];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < 32 / RPP; ++p) {
+        const int rl = p * RPP + lane / LPR, cl = (lane % LPR) * 8;
+        float v8[8];
+        *reinterpret_cast<f32x4*>(v8) = *reinterpret_cast<const f32x4*>(stage + rl * SP + cl);
+        *reinterpret_cast<f32x4*>(v8 + 4) =
+            *reinterpret_cast<const f32x4*>(stage + rl * SP + cl + 4);
+        const int tr = wr0 + i * 32 + rl, tc = wc0 + j0 * 32 + cl;  // in the tile
+        if (ptile) {  // split part: the whole fp32 tile, unmasked
+          float* q = ptile + tr * BN + tc;
+          *reinterpret_cast<f32x4*>(q) = *reinterpret_cast<const f32x4*>(v8);
+          *reinterpret_cast<f32x4*>(q + 4) = *reinterpret_cast<const f32x4*>(v8 + 4);
+        } else if (pslab) {
+          const int row = t.m0 + tr, col = t.n0 + tc;
+          if (row < g.M && col < g.N) {
+            float* q = pslab + (int64_t)row * g.N + col;
+            *reinterpret_cast<f32x4*>(q) = *reinterpret_cast<const f32x4*>(v8);
+            *reinterpret_cast<f32x4*>(q + 4) = *reinterpret_cast<const f32x4*>(v8 + 4);
+          }
+        } else {
+          const int row = t.m0 + tr, col = t.n0 + tc;
+          if (row < t.M && col < g.N)
+            epi_write8<EPI, MODE == MODE_KRAG>(g, cbase + (int64_t)row * g.ldc + col, v8,
+                                               kPre ? pa[p] : nullptr);
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
 
 // LDS of one block: the operand ring, reused as the epilogue staging area
 template <int MODE, bool B_KC, int BM, int BN>
@@ -543,86 +671,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, int 
   }
   __syncthreads();  // the staging below overwrites the ring
 
-  const int h = lane >> 5, r = lane & 31;
-  // Epilogue through LDS: each wave stages 32 rows x WN columns of its
-  // accumulators (D[i][j] sits in lane j + 32*((i/4)%2), register
-  // (i%4) + 4*(i/8)), then every lane handles 8 consecutive columns of a row
-  // with 16-byte loads and stores.
-  constexpr int SP = WN + 4;        // staging row stride (floats)
-  constexpr int LPR = WN / 8;       // lanes per staged row
-  constexpr int RPP = kWave / LPR;  // rows per pass
-  static_assert(4 * 32 * SP * 4 <= kSmemBytes, "staging does not fit");
-  float* stage = reinterpret_cast<float*>(smem) + w * 32 * SP;
-  int64_t cbase;
-  if constexpr (MODE == MODE_ROW) cbase = t.row0 * g.ldc;
-  else cbase = (int64_t)t.e * g.c_estride;
-  float* ptile = part >= 0 ? g.part + (int64_t)pid * BM * BN : nullptr;
-  // KRAG split part: fp32 partial sums into the part's [M][N] slab
-  float* pslab = nullptr;
-  if constexpr (MODE == MODE_KRAG) {
-    if (t.slab >= 0) pslab = g.kslab + (int64_t)t.slab * g.M * g.N;
-  }
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    // GELU backward and fp32 add: every pass's auxiliary input of this row
-    // block (the bf16 pre-activation, 16 bytes; the fp32 addend, 32 bytes) is
-    // loaded before the staging, so the loads are in flight together instead
-    // of one after each pass's stores
-    constexpr bool kPre = EPI == EPI_DGELU || EPI == EPI_ADDF32;
-    constexpr int kPreV = EPI == EPI_ADDF32 ? 2 : 1;  // 16-byte vectors per pass
-    u32x4 pa[kPre ? 32 / RPP : 1][kPreV];
-    if constexpr (kPre) {
-      if (ptile == nullptr) {
-#pragma unroll
-        for (int p = 0; p < 32 / RPP; ++p) {
-          const int row = t.m0 + wm * WM + i * 32 + p * RPP + lane / LPR;
-          const int col = t.n0 + wn * WN + (lane % LPR) * 8;
-          const bool ok = row < t.M && col < g.N;
-          const int64_t o = cbase + (int64_t)row * g.ldc + col;
-#pragma unroll
-          for (int u = 0; u < kPreV; ++u) {
-            if constexpr (EPI == EPI_DGELU)
-              pa[p][u] = ok ? ld16(static_cast<const uint16_t*>(g.Aux) + o) : u32x4{0, 0, 0, 0};
-            else
-              pa[p][u] = ok ? ld16(static_cast<const float*>(g.Aux) + o + 4 * u)
-                            : u32x4{0, 0, 0, 0};
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        stage[(8 * (v >> 2) + 4 * h + (v & 3)) * SP + j * 32 + r] = acc[i][j][v];
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < 32 / RPP; ++p) {
-      const int rl = p * RPP + lane / LPR, cl = (lane % LPR) * 8;
-      float v8[8];
-      *reinterpret_cast<f32x4*>(v8) = *reinterpret_cast<const f32x4*>(stage + rl * SP + cl);
-      *reinterpret_cast<f32x4*>(v8 + 4) = *reinterpret_cast<const f32x4*>(stage + rl * SP + cl + 4);
-      const int tr = wm * WM + i * 32 + rl, tc = wn * WN + cl;  // in the tile
-      if (ptile) {  // split part: the whole fp32 tile, unmasked
-        float* q = ptile + tr * BN + tc;
-        *reinterpret_cast<f32x4*>(q) = *reinterpret_cast<const f32x4*>(v8);
-        *reinterpret_cast<f32x4*>(q + 4) = *reinterpret_cast<const f32x4*>(v8 + 4);
-      } else if (pslab) {
-        const int row = t.m0 + tr, col = t.n0 + tc;
-        if (row < g.M && col < g.N) {
-          float* q = pslab + (int64_t)row * g.N + col;
-          *reinterpret_cast<f32x4*>(q) = *reinterpret_cast<const f32x4*>(v8);
-          *reinterpret_cast<f32x4*>(q + 4) = *reinterpret_cast<const f32x4*>(v8 + 4);
-        }
-      } else {
-        const int row = t.m0 + tr, col = t.n0 + tc;
-        if (row < t.M && col < g.N)
-          epi_write8<EPI, MODE == MODE_KRAG>(g, cbase + (int64_t)row * g.ldc + col, v8,
-                                             kPre ? pa[p] : nullptr);
-      }
-    }
-    __syncthreads();
-  }
+  static_assert(4 * 32 * (WN + 4) * 4 <= kSmemBytes, "staging does not fit");
+  tile_epilogue<MODE, EPI, BM, BN, TM, TN, TN>(g, t, part, pid, acc,
+                                               reinterpret_cast<float*>(smem) + w * 32 * (WN + 4),
+                                               wm * WM, wn * WN);
 }
 
 template <int MODE, bool B_KC, int EPI, int BM, int BN>
@@ -653,6 +705,144 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
     if (t.m0 >= t.M) return;
   }
   gemm_tile<MODE, B_KC, EPI, BM, BN>(g, t, part, pid, smem);
+}
+
+// ------------------------------------------------------------------ ping-pong kernel
+// 256 x 256 tiles with eight waves, two per SIMD, in two groups of four
+// (waves 0-3 and 4-7; waves w and w + 4 share a SIMD).  Wave (group g,
+// q = w % 4) owns rows 128 (q / 2) + 64 g .. +64 and columns 128 (q % 2) ..
+// +128 of the tile: 4 x 8 MFMA tiles of 16 x 16, one 16x16x32 MFMA each per
+// K tile.  (Only one wave of a SIMD issues MFMAs at a time; in that regime
+// the 16x16x32 form, accumulating in VGPRs, keeps the matrix core busier
+// than 32x32x16.)  The K tiles pass through the
+// same four-stage LDS ring as gemm_tile, filled by group 0 alone.  Both
+// groups run the same sequence of phases, one phase apart, with a block
+// barrier after every phase:
+//   group 0: read K tile 0's fragments, MFMAs of tile 0, read tile 1, ...
+//   group 1: (nothing), read tile 0, MFMAs of tile 0, read tile 1, ...
+// so on every SIMD one wave issues MFMAs while the other reads its next
+// fragments (and, in group 0, issues the copies into the ring stage the
+// previous tile freed).  Stage j is read by group 0 in phase 2j and by group
+// 1 in phase 2j + 1; tile j + 4 goes into it in phase 2j + 2.
+constexpr int kPPStages = 4;
+
+template <int MODE, bool B_KC, int EPI>
+__device__ __forceinline__ void gemm_tile_pp(const GemmArgs& g, const Tile& t, int part, int pid,
+                                             uint16_t* smem) {
+  constexpr int BM = 256, BN = 256, TM = 2, TN = 4;  // 32 x 32 blocks of the wave tile
+  constexpr int FM = 4, FN = 8;                      // 16 x 16 MFMA tiles of the wave tile
+  constexpr bool A_KC = (MODE == MODE_ROW);
+  constexpr bool BKC = (MODE == MODE_ROW) && B_KC;
+  using OpA = Operand<A_KC, BM>;
+  using OpB = Operand<BKC, BN>;
+  constexpr int kStageElems = OpA::kElems + OpB::kElems;
+  constexpr int S = kPPStages;
+  constexpr int kPer = OpA::kLoads + OpB::kLoads;  // loads per group-0 wave per tile
+
+  const uint16_t* A = static_cast<const uint16_t*>(g.A) + t.row0 * g.lda + t.kofs;
+  const uint16_t* B;
+  if constexpr (MODE == MODE_ROW)
+    B = static_cast<const uint16_t*>(g.B) + (int64_t)t.e * g.b_estride +
+        (BKC ? (int64_t)t.kofs : (int64_t)t.kofs * g.ldb);
+  else
+    B = static_cast<const uint16_t*>(g.B) + t.row0 * g.ldb;
+
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (scalar) indices: the group decides which branch a wave takes
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = w >> 2, q = w & 3;
+  const int wr0 = (q >> 1) * 128 + grp * 64, wc0 = (q & 1) * 128;
+  OpA opa;
+  OpB opb;
+  opa.init(A, g.lda, t.m0, t.M, q, lane);
+  opb.init(B, g.ldb, t.n0, g.N, q, lane);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(smem));
+  const uint32_t wslot = __builtin_amdgcn_readfirstlane((uint32_t)q);
+  auto ring = [&](int kt) { return smem + (kt % S) * kStageElems; };
+  auto issue = [&](int kt) {  // group 0 only
+    const uint32_t sa = lds0 + (uint32_t)(kt % S) * kStageElems * 2u;
+    opa.issue(kt, sa, wslot);
+    opb.issue(kt, sa + OpA::kElems * 2u, wslot);
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{};
+  bf16x8 fa[FM], fb[FN];  // fragments of one K tile
+  auto read_frags = [&](const uint16_t* st) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = opa.frag16(st, wr0 + i * 16, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = opb.frag16(st + OpA::kElems, wc0 + j * 16, lane);
+  };
+  auto mfmas = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // group 0 waits until its copies of tile j have landed; newer tiles issued
+  // so far: j + 1 .. min(j + S - 2, nfull - 1).  K is a whole number of K
+  // tiles here (the launcher's condition), so every tile is copied straight
+  // into LDS.
+  const int nfull = t.K / BK;
+  const int ntile = nfull;
+  auto wait_tile = [&](int j) {
+    int newer = min(j + S - 2, nfull - 1) - j;
+    if (newer >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * kPer) : "memory");
+    else if (newer == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kPer) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  if (grp == 0 && ntile > 0) {
+#pragma unroll
+    for (int s0 = 0; s0 < S; ++s0)
+      if (s0 < nfull) issue(s0);
+    wait_tile(0);
+  }
+  __syncthreads();
+  // Both groups run the same loop; group 1 starts one barrier later (and
+  // group 0 ends with one more), so that its fragment reads of tile j meet
+  // group 0's MFMAs of tile j.  s_barrier counts arrivals, whatever the
+  // barrier instruction a wave arrives at, and the branches are uniform per
+  // wave.
+  if (grp == 1) __syncthreads();
+  for (int j = 0; j < ntile; ++j) {
+    read_frags(ring(j));
+    if (grp == 0 && j >= 1 && j - 1 + S < nfull) issue(j - 1 + S);  // stage (j-1) % S is free
+    __syncthreads();
+    mfmas();
+    if (grp == 0 && j + 1 < nfull) wait_tile(j + 1);  // group 0 reads tile j+1 next
+    __syncthreads();
+  }
+  if (grp == 0) __syncthreads();
+  static_assert(8 * 32 * (64 + 4) * 4 <= S * kStageElems * 2, "staging does not fit");
+  tile_epilogue<MODE, EPI, BM, BN, TM, TN, 2>(g, t, part, pid, acc,
+                                              reinterpret_cast<float*>(smem) + w * 32 * (64 + 4),
+                                              wr0, wc0);
+}
+
+// Row GEMMs (MODE_ROW) whose K is a multiple of the K tile.
+template <int MODE, bool B_KC, int EPI>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
+  static_assert(MODE == MODE_ROW, "row GEMMs only");
+  constexpr int BM = 256, BN = 256;
+  __shared__ __align__(16) uint16_t smem[smem_elems<MODE, B_KC, BM, BN>()];
+  __shared__ int s_tiles[257];
+  Tile t;
+  int part, pid;
+  if (!decode_work<MODE, BM, BN>(g, s_tiles, t, part, pid)) return;
+  if (t.m0 >= t.M) return;
+  gemm_tile_pp<MODE, B_KC, EPI>(g, t, part, pid, smem);
 }
 
 // Sums the split-K parts of the tail tiles (in part order) and applies the
@@ -821,6 +1011,8 @@ __global__ __launch_bounds__(256) void gemm_schedule_kernel(const int32_t* __res
 }
 
 constexpr int kFM = 64, kFN = 64;    // fp32 block tile
+// 256 x 256 tiles on the eight-wave ping-pong kernel (gemm_pp_kernel)
+constexpr bool kPingPong = true;
 
 // bf16 block tile: 256 x 256 (4 waves of 128 x 128) when the problem has at
 // least one full round of such tiles for the chip, else 128 x 128.
@@ -931,7 +1123,10 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
       // split pays little for the launch
       const int fgrid = (int)std::min<int64_t>(ceil_div((int64_t)g.slots * BM * BN / 8, 256), 512);
       if (BM == 256) {
-        MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 256, 256><<<grid, 256, 0, s>>>(g));
+        if (kPingPong && g.K % BK_ALL == 0)
+          MOE_LAUNCH(kid, s, gemm_pp_kernel<MODE, B_KC, EPI><<<grid, 512, 0, s>>>(g));
+        else
+          MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 256, 256><<<grid, 256, 0, s>>>(g));
         MOE_LAUNCH(MOE_KERNEL_GEMM_FIXUP, s,
                    gemm_fixup_kernel<EPI, 256, 256><<<fgrid, 256, 0, s>>>(g));
       } else {
@@ -942,7 +1137,9 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
       return MOE_OK;
     }
   }
-  if (BM == 256)
+  if (MODE == MODE_ROW && BM == 256 && kPingPong && g.K % BK_ALL == 0)
+    MOE_LAUNCH(kid, s, gemm_pp_kernel<MODE_ROW, B_KC, EPI><<<grid, 512, 0, s>>>(g));
+  else if (BM == 256)
     MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 256, 256><<<grid, 256, 0, s>>>(g));
   else
     MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 128, 128><<<grid, 256, 0, s>>>(g));
