@@ -714,16 +714,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 // +128 of the tile: 4 x 8 MFMA tiles of 16 x 16, one 16x16x32 MFMA each per
 // K tile.  (Only one wave of a SIMD issues MFMAs at a time; in that regime
 // the 16x16x32 form, accumulating in VGPRs, keeps the matrix core busier
-// than 32x32x16.)  The K tiles pass through the
-// same four-stage LDS ring as gemm_tile, filled by group 0 alone.  Both
+// than 32x32x16.)  The K tiles pass through the same four-stage LDS ring as
+// gemm_tile; group 0 copies their A parts and group 1 their B parts.  Both
 // groups run the same sequence of phases, one phase apart, with a block
 // barrier after every phase:
 //   group 0: read K tile 0's fragments, MFMAs of tile 0, read tile 1, ...
 //   group 1: (nothing), read tile 0, MFMAs of tile 0, read tile 1, ...
 // so on every SIMD one wave issues MFMAs while the other reads its next
-// fragments (and, in group 0, issues the copies into the ring stage the
-// previous tile freed).  Stage j is read by group 0 in phase 2j and by group
-// 1 in phase 2j + 1; tile j + 4 goes into it in phase 2j + 2.
+// fragments and issues its copies into the ring stage the previous tile
+// freed.  Stage j is read by group 0 in phase 2j and by group 1 in phase
+// 2j + 1; tile j + 4 goes into it in phases 2j + 2 (A) and 2j + 3 (B).
 constexpr int kPPStages = 4;
 
 template <int MODE, bool B_KC, int EPI>
@@ -760,12 +760,14 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmArgs& g, const Tile& t, i
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(smem));
   const uint32_t wslot = __builtin_amdgcn_readfirstlane((uint32_t)q);
   auto ring = [&](int kt) { return smem + (kt % S) * kStageElems; };
-  auto issue = [&](int kt) {  // group 0 only
+  // group 0 copies the A part of every K tile, group 1 the B part
+  static_assert(OpA::kLoads == OpB::kLoads, "both groups wait with the same counts");
+  constexpr int kP = OpA::kLoads;  // copies per wave per K tile
+  auto issue = [&](int kt) {
     const uint32_t sa = lds0 + (uint32_t)(kt % S) * kStageElems * 2u;
-    opa.issue(kt, sa, wslot);
-    opb.issue(kt, sa + OpA::kElems * 2u, wslot);
+    if (grp == 0) opa.issue(kt, sa, wslot);
+    else opb.issue(kt, sa + OpA::kElems * 2u, wslot);
   };
-
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -787,41 +789,49 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmArgs& g, const Tile& t, i
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
   };
-  // group 0 waits until its copies of tile j have landed; newer tiles issued
-  // so far: j + 1 .. min(j + S - 2, nfull - 1).  K is a whole number of K
-  // tiles here (the launcher's condition), so every tile is copied straight
-  // into LDS.
+  // Waits until this wave's copies of K tile j have landed, given that its
+  // last copies issued are of tile min(last, nfull - 1).  K is a whole
+  // number of K tiles here (the launcher's condition), so every tile is
+  // copied straight into LDS.
   const int nfull = t.K / BK;
   const int ntile = nfull;
-  auto wait_tile = [&](int j) {
-    int newer = min(j + S - 2, nfull - 1) - j;
-    if (newer >= 2)
-      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * kPer) : "memory");
+  auto wait_tile = [&](int j, int last) {
+    const int newer = min(last, nfull - 1) - j;
+    if (newer >= 3)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(3 * kP) : "memory");
+    else if (newer == 2)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * kP) : "memory");
     else if (newer == 1)
-      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kPer) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kP) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
-  if (grp == 0 && ntile > 0) {
+  if (ntile > 0) {
 #pragma unroll
     for (int s0 = 0; s0 < S; ++s0)
       if (s0 < nfull) issue(s0);
-    wait_tile(0);
+    wait_tile(0, S - 1);
   }
   __syncthreads();
   // Both groups run the same loop; group 1 starts one barrier later (and
   // group 0 ends with one more), so that its fragment reads of tile j meet
   // group 0's MFMAs of tile j.  s_barrier counts arrivals, whatever the
   // barrier instruction a wave arrives at, and the branches are uniform per
-  // wave.
+  // wave.  Tile j's stage is free once both groups have read it, i.e. from
+  // group 0's read phase of tile j + 1 on; each group copies its part of
+  // tile j + S in its read phase of tile j + 1.  Tile j + 1 is read next by
+  // group 0, so both groups wait for their parts of it before the barrier
+  // that opens that phase: group 1 at the end of its read phase of tile j,
+  // group 0 at the end of its MFMA phase of tile j.
   if (grp == 1) __syncthreads();
   for (int j = 0; j < ntile; ++j) {
     read_frags(ring(j));
-    if (grp == 0 && j >= 1 && j - 1 + S < nfull) issue(j - 1 + S);  // stage (j-1) % S is free
+    if (j >= 1 && j - 1 + S < nfull) issue(j - 1 + S);
+    if (grp == 1 && j + 1 < nfull) wait_tile(j + 1, j + S - 1);
     __syncthreads();
     mfmas();
-    if (grp == 0 && j + 1 < nfull) wait_tile(j + 1);  // group 0 reads tile j+1 next
+    if (grp == 0 && j + 1 < nfull) wait_tile(j + 1, j + S - 1);
     __syncthreads();
   }
   if (grp == 0) __syncthreads();
