@@ -826,8 +826,9 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmArgs& g, const Tile& t, i
   // group 0 at the end of its MFMA phase of tile j.
   if (grp == 1) __syncthreads();
   for (int j = 0; j < ntile; ++j) {
-    read_frags(ring(j));
+    // the copies first: they have the longer way to go
     if (j >= 1 && j - 1 + S < nfull) issue(j - 1 + S);
+    read_frags(ring(j));
     if (grp == 1 && j + 1 < nfull) wait_tile(j + 1, j + S - 1);
     __syncthreads();
     mfmas();
