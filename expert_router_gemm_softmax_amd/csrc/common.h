@@ -29,15 +29,18 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
 __device__ __forceinline__ float bf2f(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
-// float -> bf16, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+// float -> bf16, round to nearest, ties to even: the hardware conversion
+// (v_cvt_pk_bf16_f32), which gives the same bits as rounding the float's
+// bit pattern (adding 0x7FFF plus the kept lsb, then shifting) for every
+// input that is not a NaN, subnormals and infinities included.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // two floats -> packed bf16x2 (lo in bits 0..15)
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  return static_cast<uint16_t>(pack_bf2(f, 0.0f));
 }
 
 // ------------------------------------------------------------------ storage traits
