@@ -177,12 +177,16 @@ MOE_API const char* moe_last_error(void);
  *                      ascending on equal z)
  *   gate  [T,k] float  probs[t, idx[t,j]] (renormalised over the k under
  *                      MOE_FLAG_RENORM)
- * Decisions are made on the canonical logit RN_fp32(sum in fp64 + b): the
- * fast fp32 logits are used where the top-(k+1) gaps exceed
- * cfg->route_margin, and every logit that can change the decision is
- * recomputed in fp64 otherwise.  Workspace: ws of ws_bytes >=
- * moe_workspace_bytes(cfg) (holds a transposed copy of Wr and the fast
- * logits). */
+ * Decisions follow the canonical logit RN_fp32(sum in fp64 + b): the fast
+ * fp32 logits (bf16 MFMA products, fp32 sums) are used where the top-(k+1)
+ * gaps exceed cfg->route_margin, and every logit that can change the
+ * decision is recomputed in fp64 otherwise.  This equals deciding on the
+ * canonical logits whenever each fast logit lies within margin/2 of its
+ * canonical value.  That bound is not checked at run time (the parity
+ * tests assert it on their workloads with the default margin); a larger
+ * margin widens it at the cost of more fp64 rescoring.  Workspace: ws of
+ * ws_bytes >= moe_workspace_bytes(cfg) (holds a transposed copy of Wr and
+ * the fast logits). */
 MOE_API int moe_route(const moe_cfg* cfg, const void* x, const void* Wr,
               const float* b, float* probs, int32_t* idx, float* gate,
               void* ws, size_t ws_bytes, moe_stream_t stream);
