@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
             }
             if (r >= 0) st16(dYp + (int64_t)r * d + c * V, St<T>::pack(o));
           }
-          pp = wave_sum(pp);
+          pp = wave_sum_xor(pp);
           if (lane == j + h) mine += pp;
         }
       }

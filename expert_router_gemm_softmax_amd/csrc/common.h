@@ -100,15 +100,70 @@ __device__ __forceinline__ float gelu_tanh_grad(float a) {
 }
 
 // ------------------------------------------------------------------ wave helpers
+// Wave reductions: lanes exchanged within each row of 16 by DPP (quad
+// swaps at distance 1 and 2, then the half-row and row mirrors), which
+// leaves every lane of a row holding the row's result, then the four rows'
+// results read out with readlane and combined in row order.  Every lane
+// returns the same value.  (A shuffle would go through the LDS crossbar:
+// six dependent round trips per reduction.)
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i of 8 <-> 7 - i
+constexpr int kDppMirror = 0x140;      // lane i of 16 <-> 15 - i
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 __device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return ((readlane_f(v, 0) + readlane_f(v, 16)) + readlane_f(v, 32)) + readlane_f(v, 48);
+}
+// The same sum by an xor butterfly of shuffles (every lane gets the sum).
+// In the memory-bound gathers the shuffles' latency hides behind the row
+// loads, and this form measured faster there than the DPP one above
+// (c4_large combine backward 477 vs 469 us per launch).
+__device__ __forceinline__ float wave_sum_xor(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
+               fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_d<kDppXor1>(v);
+  v += dpp_d<kDppXor2>(v);
+  v += dpp_d<kDppHalfMirror>(v);
+  v += dpp_d<kDppMirror>(v);
+  return ((readlane_d(v, 0) + readlane_d(v, 16)) + readlane_d(v, 32)) + readlane_d(v, 48);
 }
 
 // Exclusive scan of v over a block of 256 threads (4 waves); *total gets

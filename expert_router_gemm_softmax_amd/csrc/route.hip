@@ -58,16 +58,36 @@ __global__ void transpose_wr_kernel(const T* __restrict__ Wr, T* __restrict__ wr
 __device__ __forceinline__ bool route_better(float v, int e, float w, int f) {
   return v > w || (v == w && e < f);
 }
+// The wave's best (v, e) under route_better, in every lane: DPP exchanges
+// within each row of 16, then the four row winners compared in row order
+// (route_better is a strict total order, so the pairing does not matter).
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& e) {
+  const float w = dpp_f<CTRL>(v);
+  const int f = dpp_i<CTRL>(e);
+  if (route_better(w, f, v, e)) {
+    v = w;
+    e = f;
+  }
+}
 __device__ __forceinline__ void wave_argmax(float& v, int& e) {
+  argmax_step<kDppXor1>(v, e);
+  argmax_step<kDppXor2>(v, e);
+  argmax_step<kDppHalfMirror>(v, e);
+  argmax_step<kDppMirror>(v, e);
+  float bv = readlane_f(v, 0);
+  int be = __builtin_amdgcn_readlane(e, 0);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float w = __shfl_xor(v, o, kWave);
-    const int f = __shfl_xor(e, o, kWave);
-    if (route_better(w, f, v, e)) {
-      v = w;
-      e = f;
+  for (int r = 1; r < 4; ++r) {
+    const float w = readlane_f(v, 16 * r);
+    const int f = __builtin_amdgcn_readlane(e, 16 * r);
+    if (route_better(w, f, bv, be)) {
+      bv = w;
+      be = f;
     }
   }
+  v = bv;
+  e = be;
 }
 
 // Select: one wave per token, lane l holding experts l, l+64, ... (NS
@@ -99,8 +119,7 @@ __global__ __launch_bounds__(256) void route_kernel(
       z[i] = e < E ? zf[t * Epad + e] + bz[i] : -INFINITY;
       m = fmaxf(m, z[i]);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    m = wave_max(m);
     float ps[NS], sum = 0.0f;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -141,7 +160,7 @@ __global__ __launch_bounds__(256) void route_kernel(
 #pragma unroll
         for (int i = 0; i < NS; ++i)
           if (i == (e >> 6)) pe = ps[i];
-        pe = __shfl(pe, e & 63, kWave);
+        pe = readlane_f(pe, e & 63);  // e is wave-uniform
         S += pe;
         if (lane == j) psel = pe;
         if ((e & 63) == lane) idx_out[t * k + j] = e;
@@ -154,7 +173,7 @@ __global__ __launch_bounds__(256) void route_kernel(
       const float thr = E > k ? vk - tau : -INFINITY;
       int slot = 0;
       if (lane == 0) slot = atomicAdd(wl_count, 1);
-      slot = __shfl(slot, 0, kWave);
+      slot = __builtin_amdgcn_readlane(slot, 0);
       int n = 0;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
