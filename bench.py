@@ -83,12 +83,13 @@ def parse():
     return ap.parse_args()
 
 
-# name fragment of each timed kernel in a rocprofv3 trace (template arguments:
-# mode, B K-contiguous, epilogue)
-KERNEL_NAMES = {"GEMM_UP": "gemm_bf16_kernel<0, false, 1,",
-                "GEMM_DOWN": "gemm_bf16_kernel<0, false, 0,",
-                "GEMM_DH": "gemm_bf16_kernel<0, true, 2,",
-                "GEMM_DX": "gemm_bf16_kernel<0, true, 0,"}
+# name fragments of each timed kernel in a rocprofv3 trace (template
+# arguments: mode, K-contiguous B, epilogue): the eight-wave kernel that runs
+# the 256 x 256 row tiles, or the four-wave one for the other tile sizes
+KERNEL_NAMES = {"GEMM_UP": ("gemm_pp_kernel<0, false, 1>", "gemm_bf16_kernel<0, false, 1,"),
+                "GEMM_DOWN": ("gemm_pp_kernel<0, false, 0>", "gemm_bf16_kernel<0, false, 0,"),
+                "GEMM_DH": ("gemm_pp_kernel<0, true, 2>", "gemm_bf16_kernel<0, true, 2,"),
+                "GEMM_DX": ("gemm_pp_kernel<0, true, 0>", "gemm_bf16_kernel<0, true, 0,")}
 GEMM_SOURCES = ("expert_router_gemm_softmax_amd/csrc/gemm.hip",
                 "expert_router_gemm_softmax_amd/csrc/gemm.h",
                 "expert_router_gemm_softmax_amd/csrc/common.h")
@@ -121,14 +122,14 @@ def summarize_counters(a, w):
                 vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
         return vals
 
-    frag = KERNEL_NAMES[a.kernel or "GEMM_DH"]
+    frags = KERNEL_NAMES[a.kernel or "GEMM_DH"]
     out = {"kernel": a.kernel or "GEMM_DH", "workload": w.name,
            "gemm_source_sha256_16": gemm_source_hash(), "copy_probe_bytes": a.copy_probe}
     total = 0.0
     for d, counter in zip(a.summarize_counters, ("FETCH_SIZE", "WRITE_SIZE")):
         vals = per_dispatch(d, counter)
         copies = [v for (i, n), v in vals.items() if "copyBuffer" in n]
-        ks = [v for (i, n), v in vals.items() if frag in n]
+        ks = [v for (i, n), v in vals.items() if any(f in n for f in frags)]
         if not copies or not ks:
             raise SystemExit(f"{counter}: copy probe or kernel not found in {d}")
         factor = a.copy_probe / (max(copies) * 1024.0)

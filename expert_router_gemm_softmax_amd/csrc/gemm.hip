@@ -299,7 +299,11 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, int* s_tiles, Til
 // at its LDS slot; a stage is waited for with the vector-memory counter of
 // the loads issued after it.  Operands keep their HBM orientation in LDS:
 //   KC (K contiguous) tile [rows][32]: 16-byte chunk q of a row stored at
-//      chunk q ^ ((row >> 2) & 3); MFMA fragments are plain 16-byte reads.
+//      chunk q ^ ((row >> KSW) & 3); MFMA fragments are plain 16-byte reads.
+//      The shift follows the fragment shape (measured with the LDS
+//      bank-conflict counter): KSW = 2 leaves the 32x32x16 fragments (32
+//      rows x one chunk) conflict-free and gives the 16x16x32 ones (16 rows
+//      x four chunks) four conflict cycles per read; KSW = 1 is the reverse.
 //   MN (M or N contiguous) tile [32][R]: chunk c of k-row k stored at chunk
 //      c ^ mn_swz(k); fragments come from two ds_read_b64_tr_b16, which
 //      transpose 4 x 4 blocks of 16-bit elements across each 16-lane group.
@@ -319,8 +323,9 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 
+template <int KSW>
 __device__ __forceinline__ int kc_off(int row, int q) {
-  return row * BK + ((q ^ ((row >> 2) & 3)) << 3);
+  return row * BK + ((q ^ ((row >> KSW) & 3)) << 3);
 }
 __device__ __forceinline__ int mn_swz(int k) { return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1); }
 template <int R>
@@ -328,8 +333,10 @@ __device__ __forceinline__ int mn_off(int k, int m) {
   return k * R + (((m >> 3) ^ mn_swz(k)) << 3) + (m & 7);
 }
 
-// One operand tile of R rows (M or N extent) per stage.
-template <bool KC, int R>
+// One operand tile of R rows (M or N extent) per stage; KSW: the shift of
+// the K-contiguous layout's swizzle (2 for 32x32x16 fragments, 1 for
+// 16x16x32 ones).
+template <bool KC, int R, int KSW = 2>
 struct Operand {
   static_assert(KC || R >= 128, "MN swizzle needs at least 16 chunks per k-row");
   static constexpr int kChunks = R * BK / 8;      // 16-byte chunks per stage
@@ -350,7 +357,7 @@ struct Operand {
     for (int j = 0; j < kLoads; ++j) {
       const int p = (w * kLoads + j) * kWave + lane;  // physical chunk of the stage
       if constexpr (KC) {
-        const int row = p >> 2, q = (p & 3) ^ ((row >> 2) & 3);
+        const int row = p >> 2, q = (p & 3) ^ ((row >> KSW) & 3);
         src[j] = (int64_t)min(mn0 + row, lim - 1) * ld + q * 8;
       } else {
         const int k = p / (R / 8), c = (p % (R / 8)) ^ mn_swz(k);
@@ -379,7 +386,7 @@ struct Operand {
         const int gr = mn0 + row, gk = k0 + q * 8;
         const u32x4 v = (gr < lim && gk < klim) ? ld16(base + (int64_t)gr * ld + gk)
                                                 : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(s + kc_off(row, q)) = v;
+        *reinterpret_cast<u32x4*>(s + kc_off<KSW>(row, q)) = v;
       } else {
         const int k = c / (R / 8), cc = c % (R / 8);
         const int gk = k0 + k, gm = mn0 + cc * 8;
@@ -393,7 +400,7 @@ struct Operand {
   // lane l gets the 8 k values 8 (l / 32) .. +7 of row mb + l % 32
   __device__ __forceinline__ bf16x8 frag(const uint16_t* s, int mb, int kk, int lane) const {
     if constexpr (KC) {
-      return *reinterpret_cast<const bf16x8*>(s + kc_off(mb + (lane & 31), kk * 2 + (lane >> 5)));
+      return *reinterpret_cast<const bf16x8*>(s + kc_off<KSW>(mb + (lane & 31), kk * 2 + (lane >> 5)));
     } else {
       const int G = lane >> 4, a4 = (lane >> 2) & 3, b4 = lane & 3;
       const int m = mb + (G & 1) * 16 + 4 * b4;
@@ -409,7 +416,7 @@ struct Operand {
   // lane l gets the 8 k values 8 (l / 16) .. +7 of row mb + l % 16
   __device__ __forceinline__ bf16x8 frag16(const uint16_t* s, int mb, int lane) const {
     if constexpr (KC) {
-      return *reinterpret_cast<const bf16x8*>(s + kc_off(mb + (lane & 15), lane >> 4));
+      return *reinterpret_cast<const bf16x8*>(s + kc_off<KSW>(mb + (lane & 15), lane >> 4));
     } else {
       const int G = lane >> 4, a4 = (lane >> 2) & 3, b4 = lane & 3;
       const int m = mb + 4 * b4, k = G * 8 + a4;
@@ -733,8 +740,8 @@ __device__ __forceinline__ void gemm_tile_pp(const GemmArgs& g, const Tile& t, i
   constexpr int FM = 4, FN = 8;                      // 16 x 16 MFMA tiles of the wave tile
   constexpr bool A_KC = (MODE == MODE_ROW);
   constexpr bool BKC = (MODE == MODE_ROW) && B_KC;
-  using OpA = Operand<A_KC, BM>;
-  using OpB = Operand<BKC, BN>;
+  using OpA = Operand<A_KC, BM, 1>;
+  using OpB = Operand<BKC, BN, 1>;
   constexpr int kStageElems = OpA::kElems + OpB::kElems;
   constexpr int S = kPPStages;
   constexpr int kPer = OpA::kLoads + OpB::kLoads;  // loads per group-0 wave per tile
