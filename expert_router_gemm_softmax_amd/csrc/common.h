@@ -341,7 +341,6 @@ inline int64_t rows_max(const moe_cfg& c) {
   return tk < ec ? tk : ec;
 }
 
-// experts padded to 32, 64, 128 or 256 (whole 32-wide MFMA tiles) in the router
 // Block tile of the expert weight-gradient GEMMs (bf16): 256 x 256 when
 // the experts are not small (at least 512 rows each on average) and the
 // problem has a full round of such tiles for the chip, else 128 x 128
@@ -362,9 +361,31 @@ inline int64_t krag_slabs_max(const moe_cfg& c) {
   return ceil_div(768, krag_te(c)) + 2;
 }
 
+// experts padded to 32, 64, 128 or 256 (whole 32-wide MFMA tiles) in the router
 inline int route_epad(int E) {
   const int nt = (E + 31) / 32;
   return 32 * (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8);
+}
+// Block tile of the router's fast-logit GEMM (bf16): the experts in one or
+// two N tiles, 128-row M tiles when that gives a full round for the chip
+inline void route_tile(const moe_cfg& c, int& bm, int& bn) {
+  const int Epad = route_epad(c.E);
+  bn = Epad <= 64 ? 64 : 128;
+  bm = ceil_div(c.T, 128) * ceil_div(Epad, bn) >= 256 ? 128 : 64;
+}
+// K parts of that GEMM (1, 2 or 4): each writes its own fp32 partial
+// logits, summed in part order by the select kernel.  Parts are added while
+// the launch stays within two blocks per CU and each part keeps at least
+// four whole K tiles of 32.
+inline int route_ksplit(const moe_cfg& c) {
+  if (c.dtype != MOE_BF16 || c.T <= 0) return 1;
+  int bm, bn;
+  route_tile(c, bm, bn);
+  const int64_t tiles = ceil_div(c.T, bm) * ceil_div(route_epad(c.E), bn);
+  int ks = 1;
+  while (ks < 4 && tiles * ks * 2 <= 512 && c.d % (32 * ks * 2) == 0 && c.d / (ks * 2) >= 4 * 32)
+    ks *= 2;
+  return ks;
 }
 // experts padded to a multiple of 8 (16-byte bf16 rows) in the router backward
 inline int bwd_ep(int E) { return (E + 7) / 8 * 8; }
@@ -398,7 +419,7 @@ inline WsLayout ws_layout(const moe_cfg& c) {
     return o;
   };
   L.wrT = take((size_t)route_epad(c.E) * c.d * s);
-  L.zf = take((size_t)c.T * route_epad(c.E) * 4);
+  L.zf = take((size_t)route_ksplit(c) * c.T * route_epad(c.E) * 4);
   L.wl_count = take(4);
   L.wl_tok = take((size_t)c.T * 4);
   L.wl_n = take((size_t)c.T * 4);

@@ -39,6 +39,11 @@ struct GemmArgs {
   const int32_t* kplan;  // KRAG with per-expert offsets, bf16: the split plan
                          // (block_krag_plan); nullptr = no split
   float* kslab;          // its fp32 partial slabs [slab][M][N]
+  int ksplit;            // ROW one-group problems, bf16 MFMA kernel: K parts
+                         // (0 or 1: none); part p covers K elements
+                         // [p K/ksplit, (p+1) K/ksplit) and writes its own
+                         // result at C + p c_kstride (epilogue fp32 only)
+  int64_t c_kstride;
   int slots;             // filled by the launcher: concurrent blocks per round
   int ntn, ntm;          // filled by the launcher
 };

@@ -65,6 +65,7 @@ struct Tile {
   int64_t row0;  // ROW: first row of the expert; KRAG: first K row
   int kofs;      // split-K part: first K element of the part (0 otherwise)
   int slab;      // KRAG split part: its fp32 partial slab (-1 otherwise)
+  int64_t coff;  // ROW K part of a ksplit problem: offset of its output (0 otherwise)
 };
 
 // Number of output tiles (and of M tiles for ROW).  ROW problems with a
@@ -97,6 +98,7 @@ __device__ __forceinline__ void tile_of(const GemmArgs& g, const int* s_tiles, i
                                         Tile& t) {
   t.kofs = 0;
   t.slab = -1;
+  t.coff = 0;
   if constexpr (MODE == MODE_ROW) {
     int mt, nt;
     group_mn<group_m<BM>()>(lid, num_m, g.ntn, mt, nt);
@@ -200,11 +202,23 @@ __device__ __forceinline__ bool decode_work(const GemmArgs& g, int* s_tiles, Til
                                             int& pid) {
   int num_m;
   const int ntotal = tile_count<MODE, BM>(g, s_tiles, num_m);
+  part = -1;
+  pid = 0;
+  if constexpr (MODE == MODE_ROW) {
+    if (g.ksplit > 1) {  // K parts of a one-group problem, a tile's parts adjacent
+      int u;
+      if (!xcd_logical(ntotal * g.ksplit, u)) return false;
+      tile_of<MODE, BM, BN>(g, s_tiles, num_m, u / g.ksplit, t);
+      const int kp = g.K / g.ksplit, kpart = u % g.ksplit;
+      t.kofs = kpart * kp;
+      t.K = kp;
+      t.coff = kpart * g.c_kstride;
+      return true;
+    }
+  }
   const Split sp = split_of<MODE>(g, ntotal);
   const int per_full = (sp.full + 7) >> 3;
   const int bid = blockIdx.x;
-  part = -1;
-  pid = 0;
   int lid;
   if (bid < 8 * per_full) {
     lid = (bid & 7) * per_full + (bid >> 3);
@@ -452,7 +466,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& t, 
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5, r = lane & 31;
   int64_t cbase;
-  if constexpr (MODE == MODE_ROW) cbase = t.row0 * g.ldc;
+  if constexpr (MODE == MODE_ROW) cbase = t.row0 * g.ldc + t.coff;
   else cbase = (int64_t)t.e * g.c_estride;
   float* ptile = part >= 0 ? g.part + (int64_t)pid * BM * BN : nullptr;
   // KRAG split part: fp32 partial sums into the part's [M][N] slab
@@ -1098,6 +1112,14 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
   int64_t nblk;
   if constexpr (MODE == MODE_ROW) {
     nblk = g.offsets ? row_mtiles_bound(c, BM) * g.ntn : ceil_div(g.M, BM) * g.ntn;
+    if (g.ksplit > 1) {
+      // K parts: one-group bf16 problems with an fp32 epilogue and whole K
+      // tiles per part only; they replace the split-K tail
+      if (!bf || g.offsets || EPI != EPI_F32 || g.K % (BK_ALL * g.ksplit) != 0)
+        return MOE_ERR_ARG;
+      nblk *= g.ksplit;
+      g.part = nullptr;
+    }
   } else {
     g.ntm = (int)ceil_div(g.M, BM);
     nblk = (int64_t)g.E * g.ntm * g.ntn;

@@ -13,13 +13,16 @@
 // is taken among those: any expert below that band has k+1 experts
 // canonically above it.
 //
-// Two kernels.  The fast logits x Wr come from the grouped GEMM (one group
-// of T rows, the transposed router weights as a K-contiguous operand, fp32
-// epilogue into a [T, Epad] workspace matrix): the router is a skinny GEMM
-// whose cost is reading x once.  The select kernel takes one token per wave
-// (lanes across experts): softmax statistics, top-(k+1), coalesced writes of
-// probabilities, experts and gates, and the worklist of uncertain tokens;
-// the rescoring kernel then certifies those tokens in fp64, one per wave.
+// Two kernels after the logits.  The fast logits x Wr come from the grouped
+// GEMM (one group of T rows, the transposed router weights as a
+// K-contiguous operand, fp32 epilogue into [T, Epad] workspace matrices):
+// the router is a skinny GEMM whose cost is reading x once.  When its tiles
+// alone would leave CUs idle, K is cut into 2 or 4 parts, each block writing
+// one part's partial logits.  The select kernel takes four tokens per wave,
+// one per row of 16 lanes (lanes across experts): the parts' sum, softmax
+// statistics, top-(k+1), coalesced writes of probabilities, experts and
+// gates, and the worklist of uncertain tokens; the rescoring kernel then
+// certifies those tokens in fp64, one per wave.
 // Gates are the chosen probabilities, or (MOE_FLAG_RENORM) those divided by
 // their sum taken in selection order; both kernels form them the same way.
 #include "gemm.h"
@@ -90,100 +93,192 @@ __device__ __forceinline__ void wave_argmax(float& v, int& e) {
   e = be;
 }
 
-// Select: one wave per token, lane l holding experts l, l+64, ... (NS
-// slots).  Softmax statistics by wave reductions; the top-(k+1) by k+1
-// rounds of a wave argmax; tokens whose adjacent top-(k+1) gaps fall below
-// tau go to the rescoring worklist with their candidate experts (fast logit
-// >= the (k+1)-th - tau), and their experts and gates written here are
-// provisional.
-template <int NS>
+// Row reductions: the same DPP exchanges as the wave reductions, stopped
+// after the row of 16 lanes, so that each row (one token) gets its own
+// result in all of its lanes.  Every lane of a row combines the same values
+// in the same pairing (a + b and b + a are equal), so they agree bitwise.
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f<kDppMirror>(v));
+}
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
+}
+__device__ __forceinline__ void row_argmax(float& v, int& e) {
+  argmax_step<kDppXor1>(v, e);
+  argmax_step<kDppXor2>(v, e);
+  argmax_step<kDppHalfMirror>(v, e);
+  argmax_step<kDppMirror>(v, e);
+}
+
+// Select: four tokens per wave, one per row of 16 lanes; lane s of a row
+// holds the V = Epad / 16 consecutive experts s V .. s V + V - 1 (16- or
+// 8-byte loads of the logits).  Softmax statistics by row reductions; the
+// top-(k+1) by k+1 rounds of a row argmax, the round's expert and its
+// probability (from the lane that owns it) kept by lane j % 16 of the row
+// for choice j.  Tokens whose adjacent top-(k+1) gaps fall below tau go to
+// the rescoring worklist with their candidate experts (fast logit >= the
+// (k+1)-th - tau, ascending), and their experts and gates written here are
+// provisional.  The token loop is uniform over the wave (rows past T
+// compute on zeros and store nothing), so every DPP exchange runs with all
+// lanes active.
+template <int V>
 __global__ __launch_bounds__(256) void route_kernel(
-    const float* __restrict__ zf, const float* __restrict__ bias, float* __restrict__ probs,
+    const float* __restrict__ zf, int ks, const float* __restrict__ bias, float* __restrict__ probs,
     int32_t* __restrict__ idx_out, float* __restrict__ gate_out, int* __restrict__ wl_count,
     int* __restrict__ wl_tok, int* __restrict__ wl_n, int* __restrict__ wl_e, int64_t T_,
     int E, int Epad, int k, float tau, bool renorm) {
+  static_assert(V == 2 || V == 4 || V == 8 || V == 16, "experts per lane");
   const int lane = threadIdx.x & 63;
-  const int64_t nw = (int64_t)gridDim.x * 4;
-  float bz[NS];
+  const int sub = lane & 15, row0 = lane & 48;
+  const int e0 = sub * V;
+  float bz[V];
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int e = lane + kWave * i;
-    bz[i] = (e < E && bias) ? bias[e] : 0.0f;
-  }
-  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T_; t += nw) {
-    float z[NS];
+  for (int i = 0; i < V; ++i) bz[i] = (e0 + i < E && bias) ? bias[e0 + i] : 0.0f;
+  // probs rows as vectors when E fills the lanes and probs is aligned to them
+  const bool vec = E == Epad && reinterpret_cast<uintptr_t>(probs) % (V == 2 ? 8 : 16) == 0;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  for (int64_t tb = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4; tb < T_; tb += nw * 4) {
+    const int64_t t = tb + (lane >> 4);
+    const bool live = t < T_;
+    float z[V];
+    if (live) {
+      // the K parts' partial logits, summed in part order
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if (p >= ks) break;
+        const float* zr = zf + ((int64_t)p * T_ + t) * Epad + e0;
+        float a[V];
+        if constexpr (V == 2) {
+          const f32x2_t v2 = *reinterpret_cast<const f32x2_t*>(zr);
+          a[0] = v2[0];
+          a[1] = v2[1];
+        } else {
+#pragma unroll
+          for (int u = 0; u < V / 4; ++u) {
+            const f32x4 v4 = *reinterpret_cast<const f32x4*>(zr + 4 * u);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a[4 * u + q] = v4[q];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < V; ++i) z[i] = p == 0 ? a[i] : z[i] + a[i];
+      }
+    }
     float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int e = lane + kWave * i;
-      z[i] = e < E ? zf[t * Epad + e] + bz[i] : -INFINITY;
+    for (int i = 0; i < V; ++i) {
+      z[i] = e0 + i < E ? (live ? z[i] + bz[i] : 0.0f) : -INFINITY;
       m = fmaxf(m, z[i]);
     }
-    m = wave_max(m);
-    float ps[NS], sum = 0.0f;
+    m = row_max(m);
+    float ps[V], sum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      ps[i] = lane + kWave * i < E ? expf(z[i] - m) : 0.0f;
+    for (int i = 0; i < V; ++i) {
+      ps[i] = e0 + i < E ? expf(z[i] - m) : 0.0f;
       sum += ps[i];
     }
-    sum = wave_sum(sum);
+    sum = row_sum(sum);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int e = lane + kWave * i;
-      ps[i] = ps[i] / sum;
-      if (e < E) probs[t * E + e] = ps[i];
+    for (int i = 0; i < V; ++i) ps[i] = ps[i] / sum;
+    if (live) {
+      float* pr = probs + t * E + e0;
+      if (vec) {  // whole rows of V: vector stores (t E + e0 is a multiple of V)
+        if constexpr (V == 2) {
+          *reinterpret_cast<f32x2_t*>(pr) = f32x2_t{ps[0], ps[1]};
+        } else {
+#pragma unroll
+          for (int u = 0; u < V / 4; ++u)
+            *reinterpret_cast<f32x4*>(pr + 4 * u) =
+                f32x4{ps[4 * u], ps[4 * u + 1], ps[4 * u + 2], ps[4 * u + 3]};
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+          if (e0 + i < E) pr[i] = ps[i];
+      }
     }
-    // top-(k+1): taken experts are marked per slot
+    // top-(k+1): taken experts are marked per slot by their owner lane
     const int nsel = E > k ? k + 1 : k;
     uint32_t taken = 0;
     float vsel_prev = 0.0f, vk = -INFINITY;
     bool flag = false;
-    float psel = 0.0f, S = 0.0f;  // lane j: probability of the j-th choice
+    float S = 0.0f;
+    float psel0 = 0.0f, psel1 = 0.0f;  // lane s: choices s and s + 16
+    int esel0 = 0, esel1 = 0;
     for (int j = 0; j < nsel; ++j) {
       float v = -INFINITY;
       int e = 0x7fffffff;
 #pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        const int ei = lane + kWave * i;
-        if (ei < E && !((taken >> i) & 1u) && route_better(z[i], ei, v, e)) {
+      for (int i = 0; i < V; ++i)
+        if (e0 + i < E && !((taken >> i) & 1u) && route_better(z[i], e0 + i, v, e)) {
           v = z[i];
-          e = ei;
+          e = e0 + i;
         }
-      }
-      wave_argmax(v, e);
-      if ((e & 63) == lane) taken |= 1u << (e >> 6);
+      row_argmax(v, e);
+      const int o = e - e0;  // the winner's slot in its owner lane
+      if ((unsigned)o < (unsigned)V) taken |= 1u << o;
       if (j > 0 && vsel_prev - v < tau) flag = true;
       vsel_prev = v;
       if (j < k) {
-        // the owner lane writes the expert; its probability goes to lane j
-        float pe = 0.0f;
+        float pown = 0.0f;
 #pragma unroll
-        for (int i = 0; i < NS; ++i)
-          if (i == (e >> 6)) pe = ps[i];
-        pe = readlane_f(pe, e & 63);  // e is wave-uniform
+        for (int i = 0; i < V; ++i)
+          if (i == o) pown = ps[i];
+        const float pe = __shfl(pown, row0 | (e / V), kWave);
         S += pe;
-        if (lane == j) psel = pe;
-        if ((e & 63) == lane) idx_out[t * k + j] = e;
+        if (j < 16) {
+          if (sub == j) {
+            psel0 = pe;
+            esel0 = e;
+          }
+        } else if (sub == j - 16) {
+          psel1 = pe;
+          esel1 = e;
+        }
       } else {
         vk = v;
       }
     }
-    if (lane < k) gate_out[t * k + lane] = renorm ? psel / S : psel;
-    if (flag) {  // uniform over the wave
-      const float thr = E > k ? vk - tau : -INFINITY;
-      int slot = 0;
-      if (lane == 0) slot = atomicAdd(wl_count, 1);
-      slot = __builtin_amdgcn_readlane(slot, 0);
-      int n = 0;
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        const int e = lane + kWave * i;
-        const bool in = e < E && z[i] >= thr;
-        const uint64_t um = __ballot(in);
-        if (in) wl_e[(int64_t)slot * Epad + n + __popcll(um & ((1ull << lane) - 1ull))] = e;
-        n += __popcll(um);
+    if (live) {
+      if (sub < k) {
+        idx_out[t * k + sub] = esel0;
+        gate_out[t * k + sub] = renorm ? psel0 / S : psel0;
       }
-      if (lane == 0) {
+      if (sub + 16 < k) {
+        idx_out[t * k + sub + 16] = esel1;
+        gate_out[t * k + sub + 16] = renorm ? psel1 / S : psel1;
+      }
+    }
+    if (flag && live) {  // uniform over the row
+      const float thr = E > k ? vk - tau : -INFINITY;
+      uint32_t in = 0;
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+        if (e0 + i < E && z[i] >= thr) in |= 1u << i;
+      // this lane's first position among the row's candidates (ascending
+      // experts): inclusive scan of the counts over the row, minus its own
+      const int cnt = __popc(in);
+      int incl = cnt;
+#pragma unroll
+      for (int dlt = 1; dlt < 16; dlt <<= 1) {
+        const int up = __shfl_up(incl, dlt, 16);
+        if (sub >= dlt) incl += up;
+      }
+      const int n = __shfl(incl, row0 | 15, kWave);
+      int slot = 0;
+      if (sub == 0) slot = atomicAdd(wl_count, 1);
+      slot = __shfl(slot, row0, kWave);
+      int pos = incl - cnt;
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+        if ((in >> i) & 1u) wl_e[(int64_t)slot * Epad + pos++] = e0 + i;
+      if (sub == 0) {
         wl_tok[slot] = (int)t;
         wl_n[slot] = n;
       }
@@ -318,27 +413,29 @@ int launch_route_t(const moe_cfg& c, const T* x, const T* Wr, const float* b, fl
   g.ldb = c.d;
   g.C = zf;
   g.ldc = Epad;
-  g.bn = Epad <= 64 ? 64 : 128;
-  g.bm = ceil_div(c.T, 128) * ceil_div(Epad, g.bn) >= 256 ? 128 : 64;
+  route_tile(c, g.bm, g.bn);
+  const int ks = route_ksplit(c);
+  g.ksplit = ks;
+  g.c_kstride = c.T * (int64_t)Epad;
   rc = launch_gemm(MOE_KERNEL_ROUTE_LOGITS, MODE_ROW, true, EPI_F32, c, g, s);
   if (rc != MOE_OK) return rc;
   const float tau = c.route_margin > 0.0f ? c.route_margin : 1e-3f;
-  const int grid = (int)std::min<int64_t>(ceil_div(c.T, 4), 16384);
-  if (Epad <= 64)
-    MOE_LAUNCH(MOE_KERNEL_ROUTE, s,
-               route_kernel<1><<<grid, 256, 0, s>>>(zf, b, probs, idx, gate, wl.count, wl.tok,
-                                                    wl.n, wl.e, c.T, c.E, Epad, c.k, tau,
-                                                    renorm));
-  else if (Epad <= 128)
-    MOE_LAUNCH(MOE_KERNEL_ROUTE, s,
-               route_kernel<2><<<grid, 256, 0, s>>>(zf, b, probs, idx, gate, wl.count, wl.tok,
-                                                    wl.n, wl.e, c.T, c.E, Epad, c.k, tau,
-                                                    renorm));
+  // four tokens per wave, sixteen per block
+  const int grid = (int)std::min<int64_t>(ceil_div(c.T, 16), 16384);
+#define MOE_ROUTE_SELECT(V)                                                                 \
+  MOE_LAUNCH(MOE_KERNEL_ROUTE, s,                                                           \
+             route_kernel<V><<<grid, 256, 0, s>>>(zf, ks, b, probs, idx, gate, wl.count,     \
+                                                  wl.tok, wl.n, wl.e, c.T, c.E, Epad, c.k, tau, \
+                                                  renorm))
+  if (Epad == 32)
+    MOE_ROUTE_SELECT(2);
+  else if (Epad == 64)
+    MOE_ROUTE_SELECT(4);
+  else if (Epad == 128)
+    MOE_ROUTE_SELECT(8);
   else
-    MOE_LAUNCH(MOE_KERNEL_ROUTE, s,
-               route_kernel<4><<<grid, 256, 0, s>>>(zf, b, probs, idx, gate, wl.count, wl.tok,
-                                                    wl.n, wl.e, c.T, c.E, Epad, c.k, tau,
-                                                    renorm));
+    MOE_ROUTE_SELECT(16);
+#undef MOE_ROUTE_SELECT
   const int rgrid = (int)std::min<int64_t>(ceil_div(c.T, 4), 2048);
   MOE_LAUNCH(MOE_KERNEL_ROUTE, s,
              route_rescore_kernel<T><<<rgrid, 256, 0, s>>>(
