@@ -6,12 +6,18 @@
 //
 // Decision rule.  The decision is defined on the canonical logit
 // z = RN_fp32(sum_i x_i Wr_ie + b_e) with the sum in fp64.  The fast path
-// computes zf with fp32 accumulation.  If every gap between neighbours in
-// the top-(k+1) of zf is at least tau, the order of zf is the canonical
-// order (|zf - z| < tau/2).  Otherwise every expert whose zf lies within
-// tau of the (k+1)-th value or above it is rescored in fp64 and the top-k
-// is taken among those: any expert below that band has k+1 experts
-// canonically above it.
+// computes zf with fp32 accumulation; with |zf - z| < tau/2 for every
+// expert, two experts whose fast logits differ by at least tau are in the
+// same order canonically.  Cutting the fast top-(k+1) wherever neighbours
+// differ by at least tau splits it into clusters that keep their order
+// canonically; only inside a cluster of two or more can the order change.
+// An expert below rank k can enter the top-k only through the cluster of
+// rank k, and only if no cut separates rank k from rank k - 1 and its zf
+// lies within tau of the (k+1)-th value (any expert further below has k+1
+// experts canonically above it).  If there is no cluster of two, the fast
+// order is the canonical one; otherwise the members of those clusters that
+// reach an output rank are rescored in fp64 and each cluster's output ranks
+// go to its canonically best members.
 //
 // Two kernels after the logits.  The fast logits x Wr come from the grouped
 // GEMM (one group of T rows, the transposed router weights as a
@@ -207,7 +213,9 @@ __global__ __launch_bounds__(256) void route_kernel(
     const int nsel = E > k ? k + 1 : k;
     uint32_t taken = 0;
     float vsel_prev = 0.0f, vk = -INFINITY;
+    int ek = 0;
     bool flag = false;
+    uint64_t cuts = 0;  // bit r: v_{r-1} - v_r >= tau (ranks 1 .. k)
     float S = 0.0f;
     float psel0 = 0.0f, psel1 = 0.0f;  // lane s: choices s and s + 16
     int esel0 = 0, esel1 = 0;
@@ -223,7 +231,10 @@ __global__ __launch_bounds__(256) void route_kernel(
       row_argmax(v, e);
       const int o = e - e0;  // the winner's slot in its owner lane
       if ((unsigned)o < (unsigned)V) taken |= 1u << o;
-      if (j > 0 && vsel_prev - v < tau) flag = true;
+      if (j > 0) {
+        if (vsel_prev - v < tau) flag = true;
+        else cuts |= 1ull << j;
+      }
       vsel_prev = v;
       if (j < k) {
         float pown = 0.0f;
@@ -243,8 +254,10 @@ __global__ __launch_bounds__(256) void route_kernel(
         }
       } else {
         vk = v;
+        ek = e;
       }
     }
+    if (nsel == k) cuts |= 1ull << k;  // no (k+1)-th expert: nothing below rank k - 1 competes
     if (live) {
       if (sub < k) {
         idx_out[t * k + sub] = esel0;
@@ -256,11 +269,45 @@ __global__ __launch_bounds__(256) void route_kernel(
       }
     }
     if (flag && live) {  // uniform over the row
-      const float thr = E > k ? vk - tau : -INFINITY;
-      uint32_t in = 0;
+      // Cuts split ranks 0 .. k into clusters; members of different
+      // clusters keep their fast order canonically.  The candidates are the
+      // members of clusters of two or more that reach an output rank (< k),
+      // each with that cluster's output ranks [lo, hi]; the unranked
+      // experts within tau of v_k join the last cluster when no cut
+      // separates rank k from rank k - 1.
+      int rk[V];
 #pragma unroll
-      for (int i = 0; i < V; ++i)
-        if (e0 + i < E && z[i] >= thr) in |= 1u << i;
+      for (int i = 0; i < V; ++i) rk[i] = -1;
+      for (int r = 0; r < nsel; ++r) {
+        const int er = r < k ? __shfl(r < 16 ? esel0 : esel1, row0 | (r & 15), kWave) : ek;
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+          if (e0 + i == er) rk[i] = r;
+      }
+      const float thr = E > k ? vk - tau : -INFINITY;
+      const bool open_end = !((cuts >> k) & 1ull);
+      uint32_t in = 0;
+      int ent[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        ent[i] = 0;
+        int r = rk[i];
+        bool cand = true;
+        if (r < 0) {  // unranked: a candidate only within tau of v_k and with no cut at k
+          cand = open_end && e0 + i < E && z[i] >= thr;
+          r = k;
+        }
+        // cluster of rank r: from the last cut at or below r to the rank
+        // before the first cut above it
+        const uint64_t upto = (2ull << r) - 1ull;
+        const uint64_t below = cuts & upto, above = cuts & ~upto;
+        const int lo = below ? 63 - __clzll((long long)below) : 0;
+        const int hf = above ? __ffsll((long long)above) - 2 : nsel - 1;
+        if (cand && hf > lo && lo < k) {
+          in |= 1u << i;
+          ent[i] = (e0 + i) | (lo << 16) | (min(hf, k - 1) << 24);
+        }
+      }
       // this lane's first position among the row's candidates (ascending
       // experts): inclusive scan of the counts over the row, minus its own
       const int cnt = __popc(in);
@@ -277,7 +324,7 @@ __global__ __launch_bounds__(256) void route_kernel(
       int pos = incl - cnt;
 #pragma unroll
       for (int i = 0; i < V; ++i)
-        if ((in >> i) & 1u) wl_e[(int64_t)slot * Epad + pos++] = e0 + i;
+        if ((in >> i) & 1u) wl_e[(int64_t)slot * Epad + pos++] = ent[i];
       if (sub == 0) {
         wl_tok[slot] = (int)t;
         wl_n[slot] = n;
@@ -291,9 +338,12 @@ constexpr int kRescoreGroup = 4;  // candidates rescored together
 // Canonical rescoring of the worklist: one wave per uncertain token.  Each
 // candidate's logit is RN_fp32(fp64 sum of x_i Wr_ie + b_e), four
 // candidates at a time with all their 16-byte loads in flight; lane u % 64
-// keeps candidate u.  Then the top-k among the candidates (z descending,
-// expert ascending, by wave argmax) replaces the token's provisional
-// experts and gates.
+// keeps candidate u.  Each candidate carries its cluster's output ranks
+// [lo, hi]; rank r inside some cluster goes to the best (z descending,
+// expert ascending) of that cluster's candidates not yet placed, by wave
+// argmax, and every other rank keeps the select kernel's expert.  The
+// token's experts and gates are then written again in full (the gate
+// renormalisation sums the final choices in rank order).
 template <typename T>
 __global__ __launch_bounds__(256) void route_rescore_kernel(
     const int* __restrict__ wl_count, const int* __restrict__ wl_tok,
@@ -316,7 +366,7 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
       int ec[kRescoreGroup];
 #pragma unroll
       for (int q = 0; q < kRescoreGroup; ++q) {
-        ec[q] = cand[c0 + q < n ? c0 + q : c0];
+        ec[q] = cand[c0 + q < n ? c0 + q : c0] & 0xffff;
         wr[q] = wrT + (int64_t)ec[q] * d;
       }
       double acc[kRescoreGroup];
@@ -359,37 +409,54 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
         }
       }
     }
-    // top-k among the candidates by k rounds of a wave argmax
-    int ce[4];
+    // candidates' experts and cluster ranks; the ranks some cluster covers
+    int ce[4], lo[4], hi[4];
+    uint32_t cov = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = lane + kWave * i;
-      ce[i] = u < n ? cand[u] : 0x7fffffff;
+      const int en = u < n ? cand[u] : 0;
+      ce[i] = u < n ? (en & 0xffff) : 0x7fffffff;
+      lo[i] = u < n ? (en >> 16) & 0xff : 1;
+      hi[i] = u < n ? (en >> 24) & 0xff : 0;
+      if (u < n) cov |= (2u << hi[i]) - (1u << lo[i]);  // ranks lo .. hi (hi <= 31)
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cov |= (uint32_t)__shfl_xor((int)cov, o, kWave);
+    const int eprov = lane < k ? idx_out[t * k + lane] : 0;  // the select kernel's experts
     uint32_t taken = 0;
     float psel = 0.0f, S = 0.0f;  // lane j: probability of the j-th choice
+    int esel = 0;
     for (int j = 0; j < k; ++j) {
-      float v = -INFINITY;
-      int e = 0x7fffffff;
+      int e;
+      if ((cov >> j) & 1u) {
+        float v = -INFINITY;
+        e = 0x7fffffff;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + kWave * i < n && !((taken >> i) & 1u) && route_better(cz[i], ce[i], v, e)) {
-          v = cz[i];
-          e = ce[i];
-        }
-      wave_argmax(v, e);
-      // the lane holding the winner marks it and writes the expert
+        for (int i = 0; i < 4; ++i)
+          if (lo[i] <= j && j <= hi[i] && !((taken >> i) & 1u) &&
+              route_better(cz[i], ce[i], v, e)) {
+            v = cz[i];
+            e = ce[i];
+          }
+        wave_argmax(v, e);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + kWave * i < n && ce[i] == e && !((taken >> i) & 1u)) {
-          taken |= 1u << i;
-          idx_out[t * k + j] = e;
-        }
-      const float pe = e < E ? probs[t * E + e] : 0.0f;  // e < E: n >= k candidates
+        for (int i = 0; i < 4; ++i)
+          if (ce[i] == e && !((taken >> i) & 1u)) taken |= 1u << i;
+      } else {
+        e = __builtin_amdgcn_readlane(eprov, j);
+      }
+      const float pe = probs[t * E + e];
       S += pe;
-      if (lane == j) psel = pe;
+      if (lane == j) {
+        psel = pe;
+        esel = e;
+      }
     }
-    if (lane < k) gate_out[t * k + lane] = renorm ? psel / S : psel;
+    if (lane < k) {
+      idx_out[t * k + lane] = esel;
+      gate_out[t * k + lane] = renorm ? psel / S : psel;
+    }
   }
 }
 
