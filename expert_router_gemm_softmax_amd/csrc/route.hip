@@ -424,6 +424,9 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) cov |= (uint32_t)__shfl_xor((int)cov, o, kWave);
     const int eprov = lane < k ? idx_out[t * k + lane] : 0;  // the select kernel's experts
+    float pv[4];  // the token's probabilities, expert lane + 64 i in slot i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = lane + kWave * i < E ? probs[t * E + lane + kWave * i] : 0.0f;
     uint32_t taken = 0;
     float psel = 0.0f, S = 0.0f;  // lane j: probability of the j-th choice
     int esel = 0;
@@ -446,7 +449,9 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
       } else {
         e = __builtin_amdgcn_readlane(eprov, j);
       }
-      const float pe = probs[t * E + e];
+      // e is wave-uniform: its probability from the lane that holds it
+      const float pq = (e >> 6) == 0 ? pv[0] : (e >> 6) == 1 ? pv[1] : (e >> 6) == 2 ? pv[2] : pv[3];
+      const float pe = readlane_f(pq, e & 63);
       S += pe;
       if (lane == j) {
         psel = pe;

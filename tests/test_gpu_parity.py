@@ -155,6 +155,44 @@ def test_exact_ties_go_to_the_lower_expert(M):
     assert ties.sum() > 50
 
 
+WIDE_MARGIN_CASES = [  # T, d, E, k, renorm
+    (512, 64, 64, 6, False),
+    (256, 128, 128, 8, True),
+    (256, 64, 256, 32, False),   # four 16-lane rows of 16 experts each; ranks past 16
+]
+
+
+@pytest.mark.parametrize("case", WIDE_MARGIN_CASES,
+                         ids=lambda c: "T{}E{}k{}{}".format(c[0], c[2], c[3],
+                                                            "-renorm" if c[4] else ""))
+def test_wide_margin_rescoring_is_canonical(M, case):
+    """A certification margin at the median gap of the top-(k+1) logits sends
+    most tokens to the fp64 rescoring, with clusters of near-equal logits of
+    every shape: several per token, the cluster of rank k reaching into the
+    output ranks, and experts below rank k within the margin of it.  Routing
+    stays bit-exact with the oracle's canonical top-k and the gates bitwise
+    their formula (renormalised over the final order where asked)."""
+    T, d, E, k, renorm = case
+    w, inp = make_case(T, d, E, k, 64, "bf16", None, "normal", seed=11, renorm=renorm)
+    fw = O.layer_fwd(inp, w)
+    zs = -np.sort(-fw["z"], axis=1)
+    gaps = zs[:, :k] - zs[:, 1:k + 1]
+    tau = float(np.median(gaps))
+    # the shapes this margin produces (on the canonical logits; the fast
+    # ones differ by far less than tau)
+    near = gaps < tau
+    several = sum(int(np.sum(np.diff(np.concatenate(([0], near[t].astype(int), [0]))) == 1)) >= 2
+                  for t in range(T))
+    open_end = near[:, k - 1]
+    below = np.sum((fw["z"] >= zs[:, k:k + 1] - tau) & (fw["z"] < zs[:, k:k + 1]), axis=1) > 0
+    say("tau", tau, "tokens with two clusters", several, "open at rank k", int(open_end.sum()),
+        "with experts below rank k in the band", int((open_end & below).sum()))
+    assert several > T // 4 and (open_end & below).sum() > T // 4
+    res = run_layer(M, w, inp, route_margin=tau)
+    bw = O.layer_bwd(inp, w, fw)
+    check_layer_full(res, fw, bw, w)
+
+
 def test_zero_tokens(M):
     import torch
     w = W.custom(0, 64, 4, 2, 64, dtype="bf16", cf=None, aux_coeff=0.01)
