@@ -917,14 +917,27 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
 // GEMM in part order and stores the bf16 result (non-temporally, like the
 // unsplit tiles); experts that were not split are skipped.
 __global__ __launch_bounds__(256) void gemm_krag_fixup_kernel(GemmArgs g) {
+  // the plan's unit prefix and first slabs, read once into LDS (one
+  // dependent global load per expert would serialise E round trips)
+  __shared__ int s_units[257], s_slab[256];
+  __shared__ int s_any;
   const int32_t* plan = g.kplan;
   const int E = g.E;
   const int te = g.ntm * g.ntn;
+  if (threadIdx.x == 0) s_any = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) s_units[i] = plan[i];
+  for (int i = threadIdx.x; i < E; i += blockDim.x) s_slab[i] = plan[E + 1 + i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += blockDim.x)
+    if (s_units[i + 1] - s_units[i] > te) s_any = 1;
+  __syncthreads();
+  if (s_any == 0) return;  // no expert was split
   const int64_t chunks = (int64_t)g.M * (g.N / 8);
   for (int e = 0; e < E; ++e) {
-    const int parts = (plan[e + 1] - plan[e]) / te;
+    const int parts = (s_units[e + 1] - s_units[e]) / te;
     if (parts <= 1) continue;
-    const float* s0 = g.kslab + (int64_t)plan[E + 1 + e] * g.M * g.N;
+    const float* s0 = g.kslab + (int64_t)s_slab[e] * g.M * g.N;
     for (int64_t it = blockIdx.x * 256 + threadIdx.x; it < chunks;
          it += (int64_t)gridDim.x * 256) {
       const int64_t row = it / (g.N / 8);
