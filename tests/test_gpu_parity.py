@@ -43,6 +43,8 @@ SMALL_CASES = [
     (300, 64, 256, 16, 64, "bf16", None, "normal"), # E = 256 (largest), k = 16
     (100, 64, 40, 32, 64, "bf16", 1.0, "normal"),   # k = 32 (largest), drops
     (200, 64, 100, 4, 64, "f32", 1.0, "zipf"),      # fp32 router over 100 experts
+    (1000, 512, 40, 3, 256, "bf16", 1.25, "normal"),  # router logits in 4 K parts, E < Epad
+    (2000, 256, 128, 8, 64, "bf16", 1.0, "normal"),   # router logits in 2 K parts, 8 per lane
 ]
 
 
