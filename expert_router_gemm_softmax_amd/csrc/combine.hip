@@ -129,7 +129,11 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(
         const int c = g0 + s * kWave + lane;
         if (c >= nch) continue;
         if constexpr (sizeof(OutT) == sizeof(T)) {
-          st16(out + t * d + c * V, St<T>::pack(acc[s]));
+          // the layer's output (combine) or the router's dX: read by no
+          // later kernel of the step, so stored non-temporally, leaving the
+          // memory-side cache to the backward's inputs
+          __builtin_nontemporal_store(St<T>::pack(acc[s]),
+                                      reinterpret_cast<u32x4*>(out + t * d + c * V));
         } else {
           float* o = reinterpret_cast<float*>(out) + t * d + c * V;
 #pragma unroll
