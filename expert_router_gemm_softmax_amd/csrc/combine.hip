@@ -14,8 +14,11 @@ constexpr int kBwdCPL = 4;  // the same for combine backward (fewer registers)
 
 // Loads the chunks of one pass (chunk c = g0 + s*64 + lane) of row r of src
 // into v; chunks past the row end, and every chunk of a dropped row
-// (r < 0), are not loaded.
-template <typename T, int CPL>
+// (r < 0), are not loaded.  NT: the step's last read of these rows (Y in the
+// combine backward, dXp in the unpermute-sum), marked non-temporal so that
+// they do not push the kernel's output (read by the next kernel) out of
+// the memory-side cache.
+template <typename T, int CPL, bool NT = false>
 __device__ __forceinline__ void load_pass(const T* __restrict__ src, int64_t r, int d, int g0,
                                           int nch, int lane, u32x4 (&v)[CPL]) {
   constexpr int V = St<T>::kVec;
@@ -23,7 +26,12 @@ __device__ __forceinline__ void load_pass(const T* __restrict__ src, int64_t r, 
 #pragma unroll
   for (int s = 0; s < CPL; ++s) {
     const int c = g0 + s * kWave + lane;
-    if (c < nch) v[s] = ld16(src + r * d + c * V);
+    if (c < nch) {
+      if constexpr (NT)
+        v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + r * d + c * V));
+      else
+        v[s] = ld16(src + r * d + c * V);
+    }
   }
 }
 
@@ -95,10 +103,10 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(
         const bool u0 = r0 >= 0 || (fb && r0 == -1);
         const bool u1 = r1 >= 0 || (fb && r1 == -1);
         u32x4 y0[kCPL], y1[kCPL];
-        load_pass(r0 >= 0 ? src : fb, u0 ? (r0 >= 0 ? (int64_t)r0 : t) : -1, d, g0, nch, lane,
-                  y0);
-        load_pass(r1 >= 0 ? src : fb, u1 ? (r1 >= 0 ? (int64_t)r1 : t) : -1, d, g0, nch, lane,
-                  y1);
+        load_pass<T, kCPL, !GATED>(r0 >= 0 ? src : fb, u0 ? (r0 >= 0 ? (int64_t)r0 : t) : -1, d,
+                                   g0, nch, lane, y0);
+        load_pass<T, kCPL, !GATED>(r1 >= 0 ? src : fb, u1 ? (r1 >= 0 ? (int64_t)r1 : t) : -1, d,
+                                   g0, nch, lane, y1);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int32_t r = h ? r1 : r0;
@@ -218,8 +226,10 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
         const bool u0 = r0 >= 0 || (x && r0 == -1);
         const bool u1 = r1 >= 0 || (x && r1 == -1);
         u32x4 y0[kBwdCPL], y1[kBwdCPL];
-        load_pass(r0 >= 0 ? Y : x, u0 ? (r0 >= 0 ? (int64_t)r0 : t) : -1, d, g0, nch, lane, y0);
-        load_pass(r1 >= 0 ? Y : x, u1 ? (r1 >= 0 ? (int64_t)r1 : t) : -1, d, g0, nch, lane, y1);
+        load_pass<T, kBwdCPL, true>(r0 >= 0 ? Y : x, u0 ? (r0 >= 0 ? (int64_t)r0 : t) : -1, d, g0,
+                                    nch, lane, y0);
+        load_pass<T, kBwdCPL, true>(r1 >= 0 ? Y : x, u1 ? (r1 >= 0 ? (int64_t)r1 : t) : -1, d, g0,
+                                    nch, lane, y1);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int32_t r = h ? r1 : r0;
