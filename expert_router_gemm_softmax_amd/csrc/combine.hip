@@ -14,10 +14,10 @@ constexpr int kBwdCPL = 4;  // the same for combine backward (fewer registers)
 
 // Loads the chunks of one pass (chunk c = g0 + s*64 + lane) of row r of src
 // into v; chunks past the row end, and every chunk of a dropped row
-// (r < 0), are not loaded.  NT: the step's last read of these rows (Y in the
-// combine backward, dXp in the unpermute-sum), marked non-temporal so that
-// they do not push the kernel's output (read by the next kernel) out of
-// the memory-side cache.
+// (r < 0), are not loaded.  NT: the step's last read of these rows (dOut and
+// Y in the combine backward, dXp in the unpermute-sum), marked non-temporal
+// so that they do not push the kernel's output (read by the next kernel) out
+// of the memory-side cache.
 template <typename T, int CPL, bool NT = false>
 __device__ __forceinline__ void load_pass(const T* __restrict__ src, int64_t r, int d, int g0,
                                           int nch, int lane, u32x4 (&v)[CPL]) {
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     float mine = 0.0f;  // lane j < k: dgate[t, j]
     for (int g0 = 0; g0 < nch; g0 += kWave * kBwdCPL) {
       u32x4 gv[kBwdCPL];
-      load_pass(dOut, t, d, g0, nch, lane, gv);
+      load_pass<T, kBwdCPL, true>(dOut, t, d, g0, nch, lane, gv);
       for (int j = 0; j < k; j += 2) {
         const int32_t r0 = rows[j];
         const int32_t r1 = j + 1 < k ? rows[j + 1] : -2;  // -2: no assignment

@@ -165,6 +165,8 @@ __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
 
 // x_perm[row_of[t,j]] = x[t]: one wave per token reads the row once (up to
 // kCopyVec 16-byte vectors per lane in flight) and writes every kept copy.
+// x is read non-temporally, so that it does not push the copies, which the
+// up-projection reads next, out of the memory-side cache.
 constexpr int kCopyVec = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void permute_copy_kernel(
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(
 #pragma unroll
       for (int q = 0; q < kCopyVec; ++q) {
         const int c = c0 + q * kWave + lane;
-        if (c < nch) v[q] = ld16(src + c * V);
+        if (c < nch) v[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * V));
       }
       for (int j = 0; j < k; ++j) {
         const int32_t row = row_of[t * k + j];
