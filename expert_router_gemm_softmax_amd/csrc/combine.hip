@@ -77,7 +77,10 @@ __device__ __forceinline__ float router_term(const float (&dzf)[8 * RV],
 // lo of the bf16 pair in dzb [T][2E]; Wr [d][E]) -- the E products per
 // output run on the VALU, and no fp32 sum goes through HBM.  The result is
 // bitwise router_dx_kernel's on the fp32 unpermute-sum.
-template <typename T, typename OutT, bool GATED, int RV = 0>
+// NTL: the rows are read non-temporally -- the unpermute-sum's dXp (its last
+// read in the step), and the combine's Y when it cannot stay in the
+// memory-side cache until the combine backward reads it again.
+template <typename T, typename OutT, bool GATED, int RV = 0, bool NTL = !GATED>
 __global__ __launch_bounds__(256) void gather_sum_kernel(
     const T* __restrict__ src, const int32_t* __restrict__ row_of,
     const float* __restrict__ gate, const T* __restrict__ fb, OutT* __restrict__ out,
@@ -103,9 +106,9 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(
         const bool u0 = r0 >= 0 || (fb && r0 == -1);
         const bool u1 = r1 >= 0 || (fb && r1 == -1);
         u32x4 y0[kCPL], y1[kCPL];
-        load_pass<T, kCPL, !GATED>(r0 >= 0 ? src : fb, u0 ? (r0 >= 0 ? (int64_t)r0 : t) : -1, d,
+        load_pass<T, kCPL, NTL>(r0 >= 0 ? src : fb, u0 ? (r0 >= 0 ? (int64_t)r0 : t) : -1, d,
                                    g0, nch, lane, y0);
-        load_pass<T, kCPL, !GATED>(r1 >= 0 ? src : fb, u1 ? (r1 >= 0 ? (int64_t)r1 : t) : -1, d,
+        load_pass<T, kCPL, NTL>(r1 >= 0 ? src : fb, u1 ? (r1 >= 0 ? (int64_t)r1 : t) : -1, d,
                                    g0, nch, lane, y1);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -266,12 +269,25 @@ inline int token_grid(int64_t T_) {
 
 }  // namespace
 
+// The memory-side cache (MALL) of MI355X, 256 MB: Y larger than it is read
+// non-temporally by the combine (c4_large: combine 242 -> 222 us, the
+// combine backward unchanged; with Y inside it, as at c2_zipf, the combine
+// backward would lose its cache hits: 31 -> 37 us).
+constexpr size_t kMallBytes = (size_t)256 << 20;
+
 int launch_combine(const moe_cfg& c, const void* Y, const int32_t* row_of,
                    const float* gate, const void* x, void* out, hipStream_t s) {
   if (c.T == 0) return MOE_OK;
   const int grid = token_grid(c.T);
   const void* fb = (c.flags & MOE_FLAG_DROP_IDENTITY) ? x : nullptr;
-  if (c.dtype == MOE_BF16)
+  const bool nt = (size_t)rows_max(c) * (size_t)c.d * elem_bytes(c) > kMallBytes;
+  if (c.dtype == MOE_BF16 && nt)
+    MOE_LAUNCH(MOE_KERNEL_COMBINE, s,
+               gather_sum_kernel<uint16_t, uint16_t, true, 0, true><<<grid, 256, 0, s>>>(
+                   static_cast<const uint16_t*>(Y), row_of, gate,
+                   static_cast<const uint16_t*>(fb), static_cast<uint16_t*>(out), c.T, c.d,
+                   c.k));
+  else if (c.dtype == MOE_BF16)
     MOE_LAUNCH(MOE_KERNEL_COMBINE, s,
                gather_sum_kernel<uint16_t, uint16_t, true><<<grid, 256, 0, s>>>(
                    static_cast<const uint16_t*>(Y), row_of, gate,
