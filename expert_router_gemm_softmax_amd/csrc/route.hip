@@ -46,7 +46,8 @@ struct RouteWorklist {
   int* count;  // number of uncertain tokens
   int* tok;    // [T] their token indices
   int* n;      // [T] their candidate counts
-  int* e;      // [T, Epad] their candidate experts, ascending
+  int* e;      // [T, Epad] their candidates, ascending: expert | lo << 16 |
+               // hi << 24, [lo, hi] the output ranks of the candidate's cluster
 };
 
 // wrT[e][i] = Wr[i][e] for e < E, zero rows for E <= e < Epad.
@@ -128,9 +129,10 @@ __device__ __forceinline__ void row_argmax(float& v, int& e) {
 // top-(k+1) by k+1 rounds of a row argmax, the round's expert and its
 // probability (from the lane that owns it) kept by lane j % 16 of the row
 // for choice j.  Tokens whose adjacent top-(k+1) gaps fall below tau go to
-// the rescoring worklist with their candidate experts (fast logit >= the
-// (k+1)-th - tau, ascending), and their experts and gates written here are
-// provisional.  The token loop is uniform over the wave (rows past T
+// the rescoring worklist with the members of their uncertain clusters
+// (ascending experts, each with its cluster's output ranks), and their
+// experts and gates written here are provisional for those ranks.  The
+// token loop is uniform over the wave (rows past T
 // compute on zeros and store nothing), so every DPP exchange runs with all
 // lanes active.
 template <int V>
