@@ -390,24 +390,47 @@ struct Operand {
                    :: "v"(gp), "s"(dst) : "memory", "m0");
     }
   }
-  // partial K tile [k0, klim) through registers, zero outside
-  __device__ __forceinline__ void tail(uint16_t* s, int k0, int klim) const {
+  // Partial K tile [k0, klim) through registers, zero outside, in two
+  // halves, so that all of a thread's loads (both operands') are in flight
+  // together before the first store: every chunk is loaded from an address
+  // clamped into the operand (its own when it is inside; k0 < klim holds
+  // for a partial tile), so that no load is predicated away, and bit i of
+  // `in` says whether chunk i is inside; the store half writes zeros for
+  // the chunks outside.  (Loaded and stored one chunk at a time, each load
+  // waited for alone, the partial tile of the weight gradients, whose K is
+  // an expert's ragged row count, cost about 2.5% of their time.)
+  static constexpr int kTail = kChunks / 256;  // chunks per thread
+  __device__ __forceinline__ void tail_load(int k0, int klim, u32x4 (&v)[kTail],
+                                            uint32_t& in) const {
+    in = 0;
 #pragma unroll
-    for (int i = 0; i < kChunks / 256; ++i) {
+    for (int i = 0; i < kTail; ++i) {
       const int c = threadIdx.x + i * 256;
+      int64_t at;
       if constexpr (KC) {
         const int row = c >> 2, q = c & 3;
         const int gr = mn0 + row, gk = k0 + q * 8;
-        const u32x4 v = (gr < lim && gk < klim) ? ld16(base + (int64_t)gr * ld + gk)
-                                                : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(s + kc_off<KSW>(row, q)) = v;
+        in |= (uint32_t)(gr < lim && gk < klim) << i;
+        at = (int64_t)min(gr, lim - 1) * ld + (gk < klim ? gk : k0);
       } else {
         const int k = c / (R / 8), cc = c % (R / 8);
         const int gk = k0 + k, gm = mn0 + cc * 8;
-        const u32x4 v = (gk < klim && gm < lim) ? ld16(base + (int64_t)gk * ld + gm)
-                                                : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(s + mn_off<R>(k, cc * 8)) = v;
+        in |= (uint32_t)(gk < klim && gm < lim) << i;
+        at = (int64_t)min(gk, klim - 1) * ld + min(gm, lim - 8);
       }
+      v[i] = ld16(base + at);
+    }
+  }
+  __device__ __forceinline__ void tail_store(uint16_t* s, const u32x4 (&v)[kTail],
+                                             uint32_t in) const {
+#pragma unroll
+    for (int i = 0; i < kTail; ++i) {
+      const int c = threadIdx.x + i * 256;
+      const u32x4 x = ((in >> i) & 1u) ? v[i] : u32x4{0, 0, 0, 0};
+      if constexpr (KC)
+        *reinterpret_cast<u32x4*>(s + kc_off<KSW>(c >> 2, c & 3)) = x;
+      else
+        *reinterpret_cast<u32x4*>(s + mn_off<R>(c / (R / 8), (c % (R / 8)) * 8)) = x;
     }
   }
   // MFMA 32x32x16 fragment of the 32 rows starting at mb, k sub-step kk:
@@ -644,9 +667,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, int 
   constexpr int KS = BK / 16;                      // k steps per tile
   const int nfull = t.K / BK;
   const int ntile = nfull + (t.K % BK != 0 ? 1 : 0);
-  auto write_tail = [&](int kt) {
-    opa.tail(ring(kt), kt * BK, t.K);
-    opb.tail(ring(kt) + OpA::kElems, kt * BK, t.K);
+  auto write_tail = [&](int kt) {  // both operands' loads first, then the stores
+    u32x4 va[OpA::kTail], vb[OpB::kTail];
+    uint32_t ia, ib;
+    opa.tail_load(kt * BK, t.K, va, ia);
+    opb.tail_load(kt * BK, t.K, vb, ib);
+    opa.tail_store(ring(kt), va, ia);
+    opb.tail_store(ring(kt) + OpA::kElems, vb, ib);
   };
   if (ntile > 0) {
 #pragma unroll

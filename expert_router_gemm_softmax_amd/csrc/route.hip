@@ -64,9 +64,11 @@ __global__ void transpose_wr_kernel(const T* __restrict__ Wr, T* __restrict__ wr
 }
 
 // Wave argmax over (value, expert) pairs: larger value first, lower
-// expert on equal values (-0 == +0).
+// expert on equal values (-0 == +0).  Conditions here and at the callers
+// are combined with bitwise operators, which evaluate every operand, so the
+// compiler emits compares and selects rather than branches.
 __device__ __forceinline__ bool route_better(float v, int e, float w, int f) {
-  return v > w || (v == w && e < f);
+  return (v > w) | ((v == w) & (e < f));
 }
 // The wave's best (v, e) under route_better, in every lane: DPP exchanges
 // within each row of 16, then the four row winners compared in row order
@@ -224,12 +226,13 @@ __global__ __launch_bounds__(256) void route_kernel(
     for (int j = 0; j < nsel; ++j) {
       float v = -INFINITY;
       int e = 0x7fffffff;
+      // this lane's best untaken expert
 #pragma unroll
-      for (int i = 0; i < V; ++i)
-        if (e0 + i < E && !((taken >> i) & 1u) && route_better(z[i], e0 + i, v, e)) {
-          v = z[i];
-          e = e0 + i;
-        }
+      for (int i = 0; i < V; ++i) {
+        const bool ok = (e0 + i < E) & !((taken >> i) & 1u) & route_better(z[i], e0 + i, v, e);
+        v = ok ? z[i] : v;
+        e = ok ? e0 + i : e;
+      }
       row_argmax(v, e);
       const int o = e - e0;  // the winner's slot in its owner lane
       if ((unsigned)o < (unsigned)V) taken |= 1u << o;
@@ -438,12 +441,12 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
         float v = -INFINITY;
         e = 0x7fffffff;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (lo[i] <= j && j <= hi[i] && !((taken >> i) & 1u) &&
-              route_better(cz[i], ce[i], v, e)) {
-            v = cz[i];
-            e = ce[i];
-          }
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = (lo[i] <= j) & (j <= hi[i]) & !((taken >> i) & 1u) &
+                          route_better(cz[i], ce[i], v, e);
+          v = ok ? cz[i] : v;
+          e = ok ? ce[i] : e;
+        }
         wave_argmax(v, e);
 #pragma unroll
         for (int i = 0; i < 4; ++i)

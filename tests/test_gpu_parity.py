@@ -195,6 +195,30 @@ def test_wide_margin_rescoring_is_canonical(M, case):
     check_layer_full(res, fw, bw, w)
 
 
+LARGE_T_ROUTER_CASES = [  # T, d, E, k
+    (32700, 512, 128, 2),  # 256 row tiles of 128 (60 rows in the last), K in two parts
+    (33000, 256, 160, 3),  # 258 row tiles x 2 expert tiles (Epad 256, 96 padded), one K part
+]
+
+
+@pytest.mark.parametrize("case", LARGE_T_ROUTER_CASES, ids=lambda c: "T{}d{}E{}".format(*c[:3]))
+def test_router_at_large_token_counts(M, case):
+    """The router's logit GEMM at token counts like the largest workload's,
+    with a ragged last row tile: K cut into parts whose partial logits the
+    select kernel sums, and padded expert columns across two expert tiles.
+    Routing stays bit-exact with the oracle, the fast logits within tau/2 of
+    the canonical ones, and every other output within tolerance."""
+    T, d, E, k = case
+    w, inp = make_case(T, d, E, k, 32, "bf16", 1.0, "normal", seed=13)
+    res = run_layer(M, w, inp)
+    fw = O.layer_fwd(inp, w)
+    bw = O.layer_bwd(inp, w, fw)
+    check_layer_full(res, fw, bw, w)
+    err = logit_error(res, fw)
+    say("logit error", err)
+    assert err <= 1e-3 / 2
+
+
 def test_zero_tokens(M):
     import torch
     w = W.custom(0, 64, 4, 2, 64, dtype="bf16", cf=None, aux_coeff=0.01)
