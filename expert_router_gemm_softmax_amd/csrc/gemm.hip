@@ -725,8 +725,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, int 
                                                wm * WM, wn * WN);
 }
 
+// Weight gradients on 128 x 128 tiles (short, skewed reductions: most of a
+// tile's time is its prologue and epilogue) are held to three waves per
+// SIMD, three blocks per CU, so that a block's fixed costs overlap the
+// others' MFMAs; unconstrained they took 172 registers, two blocks per CU.
+template <int MODE, int BM, int BN>
+constexpr int gemm_waves_per_simd() {
+  return MODE == MODE_KRAG && BM * BN <= 128 * 128 ? 3 : 1;
+}
+
 template <int MODE, bool B_KC, int EPI, int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256) __attribute__((
+    amdgpu_waves_per_eu(gemm_waves_per_simd<MODE, BM, BN>()))) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __align__(16) uint16_t smem[smem_elems<MODE, B_KC, BM, BN>()];
   __shared__ int s_tiles[257];
   if constexpr (MODE == MODE_KRAG) {
