@@ -497,35 +497,47 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& t, 
   if constexpr (MODE == MODE_KRAG) {
     if (t.slab >= 0) pslab = g.kslab + (int64_t)t.slab * g.M * g.N;
   }
+  // GELU backward and fp32 add: the auxiliary input of a pass (the bf16
+  // pre-activation, 16 bytes per row and lane; the fp32 addend, 32 bytes)
+  // is loaded before the pass's staging, so that a lane's loads are in
+  // flight together; where the registers allow (the GELU backward, and the
+  // fp32 add on 128 x 128 tiles) every pass's is loaded before the first.
+  constexpr bool kPre = EPI == EPI_DGELU || EPI == EPI_ADDF32;
+  constexpr int kPreV = EPI == EPI_ADDF32 ? 2 : 1;  // 16-byte vectors per row
+  constexpr int kNP = TN / TNP;                      // passes per row block
+  constexpr bool kHoist = kPre && (EPI == EPI_DGELU || BM * BN <= 128 * 128);
+  u32x4 pa[kHoist ? TM * kNP : 1][kPre ? 32 / RPP : 1][kPreV];
+  auto load_aux = [&](int slot, int i, int jp) {
+#pragma unroll
+    for (int p = 0; p < 32 / RPP; ++p) {
+      const int row = t.m0 + wr0 + i * 32 + p * RPP + lane / LPR;
+      const int col = t.n0 + wc0 + jp * TNP * 32 + (lane % LPR) * 8;
+      const bool ok = row < t.M && col < g.N;
+      const int64_t o = cbase + (int64_t)row * g.ldc + col;
+#pragma unroll
+      for (int u = 0; u < kPreV; ++u) {
+        if constexpr (EPI == EPI_DGELU)
+          pa[slot][p][u] = ok ? ld16(static_cast<const uint16_t*>(g.Aux) + o) : u32x4{0, 0, 0, 0};
+        else
+          pa[slot][p][u] =
+              ok ? ld16(static_cast<const float*>(g.Aux) + o + 4 * u) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  if constexpr (kHoist) {
+    if (ptile == nullptr) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jp = 0; jp < kNP; ++jp) load_aux(i * kNP + jp, i, jp);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j0 = 0; j0 < TN; j0 += TNP) {
-      // GELU backward and fp32 add: every pass's auxiliary input of this row
-      // block (the bf16 pre-activation, 16 bytes; the fp32 addend, 32 bytes)
-      // is loaded before the staging, so the loads are in flight together
-      // instead of one after each pass's stores
-      constexpr bool kPre = EPI == EPI_DGELU || EPI == EPI_ADDF32;
-      constexpr int kPreV = EPI == EPI_ADDF32 ? 2 : 1;  // 16-byte vectors per pass
-      u32x4 pa[kPre ? 32 / RPP : 1][kPreV];
-      if constexpr (kPre) {
-        if (ptile == nullptr) {
-#pragma unroll
-          for (int p = 0; p < 32 / RPP; ++p) {
-            const int row = t.m0 + wr0 + i * 32 + p * RPP + lane / LPR;
-            const int col = t.n0 + wc0 + j0 * 32 + (lane % LPR) * 8;
-            const bool ok = row < t.M && col < g.N;
-            const int64_t o = cbase + (int64_t)row * g.ldc + col;
-#pragma unroll
-            for (int u = 0; u < kPreV; ++u) {
-              if constexpr (EPI == EPI_DGELU)
-                pa[p][u] = ok ? ld16(static_cast<const uint16_t*>(g.Aux) + o) : u32x4{0, 0, 0, 0};
-              else
-                pa[p][u] = ok ? ld16(static_cast<const float*>(g.Aux) + o + 4 * u)
-                              : u32x4{0, 0, 0, 0};
-            }
-          }
-        }
+      if constexpr (kPre && !kHoist) {
+        if (ptile == nullptr) load_aux(0, i, j0 / TNP);
       }
       if constexpr (MF == 32) {
 #pragma unroll
@@ -567,7 +579,8 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& g, const Tile& t, 
           const int row = t.m0 + tr, col = t.n0 + tc;
           if (row < t.M && col < g.N)
             epi_write8<EPI, MODE == MODE_KRAG>(g, cbase + (int64_t)row * g.ldc + col, v8,
-                                               kPre ? pa[p] : nullptr);
+                                               kPre ? pa[kHoist ? i * kNP + j0 / TNP : 0][p]
+                                                    : nullptr);
         }
       }
       __syncthreads();
