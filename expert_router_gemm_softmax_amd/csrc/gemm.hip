@@ -1108,6 +1108,9 @@ __global__ __launch_bounds__(256) void gemm_schedule_kernel(const int32_t* __res
 constexpr int kFM = 64, kFN = 64;    // fp32 block tile
 // 256 x 256 tiles on the eight-wave ping-pong kernel (gemm_pp_kernel)
 constexpr bool kPingPong = true;
+// epilogues of the expert GEMMs, the only ones that take 128 x 256 tiles
+template <int EPI>
+constexpr bool kWideRow() { return EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_DGELU; }
 
 // bf16 block tile: 256 x 256 (4 waves of 128 x 128) when the problem has at
 // least one full round of such tiles for the chip, else 128 x 128.
@@ -1162,6 +1165,9 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
     // one-group problems choose freely; grouped ones follow the schedule
     BM = g.offsets ? row_bm(c) : (use_big_tile(c, MODE_KRAG, g.M, g.N, 1) ? 256 : 128);
     BN = BM;
+    // wide expert GEMMs on 128-row tiles take 128 x 256 tiles: two blocks
+    // per CU instead of three, a third less LDS traffic per flop
+    if (kWideRow<EPI>() && g.offsets && BM == 128 && g.N >= 2048) BN = 256;
     if constexpr (B_KC && (EPI == EPI_F32 || EPI == EPI_ADDF32)) {
       if (!g.offsets && g.bm) BM = g.bm;
       if (!g.offsets && g.bn) BN = g.bn;
@@ -1194,7 +1200,7 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
   if constexpr (MODE == MODE_ROW) {
     // split-K tail for the bf16 kernels: whole tiles, then up to one block
     // per CU for the parts
-    if (bf && g.part != nullptr && (BM == 256 || BM == 128) && BN == BM &&
+    if (bf && g.part != nullptr && (BM == 256 || BM == 128) && (BN == BM || BN == 2 * BM) &&
         (g.offsets || one_group_splits(g.M, BM, g.ntn, g.K))) {
       g.slots = 256;  // CUs
       nblk = grid8(nblk) + g.slots;
@@ -1234,10 +1240,25 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
         MOE_LAUNCH(MOE_KERNEL_GEMM_FIXUP, s,
                    gemm_fixup_kernel<EPI, 256, 256><<<fgrid, 256, 0, s>>>(g));
       } else {
+        if constexpr (kWideRow<EPI>()) {
+          if (BN == 256) {
+            MOE_LAUNCH(kid, s,
+                       gemm_bf16_kernel<MODE, B_KC, EPI, 128, 256><<<grid, 256, 0, s>>>(g));
+            MOE_LAUNCH(MOE_KERNEL_GEMM_FIXUP, s,
+                       gemm_fixup_kernel<EPI, 128, 256><<<fgrid, 256, 0, s>>>(g));
+            return MOE_OK;
+          }
+        }
         MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE, B_KC, EPI, 128, 128><<<grid, 256, 0, s>>>(g));
         MOE_LAUNCH(MOE_KERNEL_GEMM_FIXUP, s,
                    gemm_fixup_kernel<EPI, 128, 128><<<fgrid, 256, 0, s>>>(g));
       }
+      return MOE_OK;
+    }
+  }
+  if constexpr (MODE == MODE_ROW && kWideRow<EPI>()) {
+    if (BM == 128 && BN == 256) {
+      MOE_LAUNCH(kid, s, gemm_bf16_kernel<MODE_ROW, B_KC, EPI, 128, 256><<<grid, 256, 0, s>>>(g));
       return MOE_OK;
     }
   }
