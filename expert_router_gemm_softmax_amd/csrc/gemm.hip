@@ -1165,9 +1165,9 @@ int run_gemm(int kid, const moe_cfg& c, GemmArgs g, hipStream_t s) {
     // one-group problems choose freely; grouped ones follow the schedule
     BM = g.offsets ? row_bm(c) : (use_big_tile(c, MODE_KRAG, g.M, g.N, 1) ? 256 : 128);
     BN = BM;
-    // wide expert GEMMs on 128-row tiles take 128 x 256 tiles: two blocks
+    // expert GEMMs on 128-row tiles, N >= 1024, take 128 x 256 tiles: two blocks
     // per CU instead of three, a third less LDS traffic per flop
-    if (kWideRow<EPI>() && g.offsets && BM == 128 && g.N >= 2048) BN = 256;
+    if (kWideRow<EPI>() && g.offsets && BM == 128 && g.N >= 1024) BN = 256;
     if constexpr (B_KC && (EPI == EPI_F32 || EPI == EPI_ADDF32)) {
       if (!g.offsets && g.bm) BM = g.bm;
       if (!g.offsets && g.bn) BN = g.bn;
