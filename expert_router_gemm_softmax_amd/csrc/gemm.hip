@@ -15,10 +15,15 @@
 //        reduction runs over a ragged K = m_e (H^T dYp, x_perm^T dA).
 //        Experts with m_e = 0 get a zero matrix.
 //
-// bf16 kernel (gfx950): v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
-// block tile 256 x 256 or 128 x 128 (4 waves in 2 x 2), K tiles of 32 held
-// in a ring of 4 (256 x 256) or 3 LDS stages filled straight from HBM by
-// global_load_lds_dwordx4.  Operands keep their HBM orientation in LDS:
+// bf16 kernels (gfx950), fp32 accumulation, K tiles of 32 held in a ring of
+// LDS stages filled straight from HBM by global_load_lds_dwordx4:
+//   gemm_pp_kernel: row GEMMs on 256 x 256 tiles, eight waves in two groups
+//     that alternate between reading a K tile's fragments and issuing its
+//     v_mfma_f32_16x16x32_bf16 (four stages);
+//   gemm_bf16_kernel: four waves in 2 x 2 with v_mfma_f32_32x32x16_bf16 on
+//     128 x 128, 128 x 256 (wide expert row GEMMs) or 256 x 256 tiles (the
+//     weight gradients, the router's GEMMs, row GEMMs not on 256-row
+//     tiles); four stages for 256 x 256, else three.  Operands keep their HBM orientation in LDS:
 // K-contiguous tiles with an XOR swizzle, read as 16-byte fragments;
 // M/N-contiguous tiles read with the transposing ds_read_b64_tr_b16.  Tiles
 // are ordered so that the blocks resident on one XCD (block id mod 8) work
@@ -329,7 +334,8 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, int* s_tiles, Til
 // final partial K tile goes through registers with zero fill.
 constexpr int BK = BK_ALL;
 // stages of the ring: 4 for the 256 x 256 tile (1 block per CU); 3 for
-// smaller tiles, so that three blocks fit a CU's LDS
+// smaller tiles, so that three blocks of 128 x 128 (or two of 128 x 256)
+// fit a CU's LDS
 template <int BM, int BN>
 constexpr int ring_stages() { return BM * BN >= 256 * 256 ? 4 : 3; }
 
